@@ -67,10 +67,10 @@ __all__ = [
 #     sums of a tile are added left to right; tile sums are added left to
 #     right.
 #   row sum of row i: columns are cut into tiles of TILE_COLS = 256 columns;
-#     inside a tile "lane" l (0..63) sums columns 4l..4l+3 left to right, the
-#     64 lane values are combined by the halving tree v[l] += v[l + s] for
-#     s = 32, 16, 8, 4, 2, 1 (result v[0]); tile values are added left to
-#     right starting from +0.0.
+#     inside a tile "lane" l (0..63) sums the columns l, l+64, l+128, l+192
+#     of the tile left to right, the 64 lane values are combined by the
+#     halving tree v[l] += v[l + s] for s = 32, 16, 8, 4, 2, 1 (result v[0]);
+#     tile values are added left to right starting from +0.0.
 #   Ragged edges are padded with +0.0, which changes no float64 sum of
 #   non-negative terms.
 # ---------------------------------------------------------------------------
@@ -91,10 +91,10 @@ def canonical_row_sums(a: np.ndarray) -> np.ndarray:
     cp = max(_ceil_to(cols, TILE_COLS), TILE_COLS)
     p = np.zeros((rows, cp), dtype=np.float64)
     p[:, :cols] = a
-    t = p.reshape(rows, cp // TILE_COLS, TILE_COLS // LANE_COLS, LANE_COLS)
-    v = t[..., 0].copy()
+    t = p.reshape(rows, cp // TILE_COLS, LANE_COLS, TILE_COLS // LANE_COLS)
+    v = t[:, :, 0, :].copy()                 # lane l of a tile: columns l + 64c
     for c in range(1, LANE_COLS):
-        v = v + t[..., c]
+        v = v + t[:, :, c, :]
     s = TILE_COLS // LANE_COLS // 2
     while s >= 1:
         v = v[..., :s] + v[..., s:2 * s]

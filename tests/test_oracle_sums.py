@@ -48,20 +48,20 @@ def _row(cols, entries):
 
 
 def test_row_sum_lane_order_is_sequential():
-    # within a lane (4 consecutive columns) the sum is left to right:
+    # within a lane (columns l, l+64, l+128, l+192) the sum is left to right:
     # ((1 + t) + t) = 1 under ties-to-even, whereas 1 + (t + t) = 1 + 2^-52
-    a = _row(256, {0: 1.0, 1: TINY, 2: TINY})
+    a = _row(256, {0: 1.0, 64: TINY, 128: TINY})
     assert canonical_row_sums(a)[0] == 1.0
 
 
 def test_row_sum_tree_shape():
     # lanes 1 and 33 meet at the first tree level (s = 32): t + t = 2^-52,
     # then 1 + 2^-52 is exact
-    a = _row(256, {0: 1.0, 4 * 1: TINY, 4 * 33: TINY})
+    a = _row(256, {0: 1.0, 1: TINY, 33: TINY})
     assert canonical_row_sums(a)[0] == 1.0 + 2.0 ** -52
     # lanes 1 and 2 never meet before lane 0 absorbs them one at a time
     # (s = 2: v0 = 1 + t -> 1; s = 1: v0 = 1 + (t) -> 1)
-    a = _row(256, {0: 1.0, 4 * 1: TINY, 4 * 2: TINY})
+    a = _row(256, {0: 1.0, 1: TINY, 2: TINY})
     assert canonical_row_sums(a)[0] == 1.0
 
 
