@@ -1,0 +1,209 @@
+// Prefill GEMM on packed planes: Y = Σ_p (X ⊙ h_p) B_pᵀ ⊙ g_p.
+//
+// The pages' kernel (RaBiT paper App. E.1) covers only the decode GEMV; this
+// prefill path is a dense contraction and runs on the fp16 matrix cores:
+//   * B tile = ±h_p[k] in fp16, exact: the sign bit of h_p is flipped where
+//     the plane bit is 1 (two columns k, k+16 of a 32-column word per dword).
+//   * A tile = X in fp16; each row of X is first scaled by a power of two so
+//     that its largest |x| lies in [2^14, 2^15) (exact for bf16 inputs above
+//     the fp16 subnormal range), the scale is undone in the epilogue.
+//   * fp32 accumulation, one accumulator set per path; g_p applied in the
+//     epilogue (paper §4.1 eq.: W_hat = g ⊙ B ⊙ h).
+// Inside a 32-column block the contraction index κ is permuted so that
+// dword m of a fragment holds columns (m, m + 16): κ = 2m + hh <-> column
+// m + 16 hh. A and B use the same κ order, so the MFMA sums the same pairs.
+#include <algorithm>
+
+#include "rabit_internal.h"
+
+namespace rabit {
+
+namespace {
+
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int kBM = 128, kBN = 128, kBK = 32;
+constexpr int kLdsStride = 20;  // dwords per 32-column row in LDS (16 + 4 padding)
+
+struct GemmWs {
+  uint16_t* xh;      // fp16 [m][Kp], κ-permuted inside 32-column blocks
+  int* rowexp;       // [m] power-of-two exponent applied to row m
+  uint32_t* hpairs;  // [2][Kp/32][16] fp16 pairs (h[32b+m], h[32b+m+16])
+};
+
+__host__ inline size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+__host__ inline GemmWs carve(void* ws, int in, int m) {
+  const size_t Kp = (size_t)col_groups(in) * 128;
+  char* p = (char*)ws;
+  GemmWs w;
+  w.xh = (uint16_t*)p;
+  p += a256((size_t)m * Kp * 2);
+  w.rowexp = (int*)p;
+  p += a256((size_t)m * 4);
+  w.hpairs = (uint32_t*)p;
+  return w;
+}
+
+__host__ inline size_t ws_bytes(int in, int m) {
+  const size_t Kp = (size_t)col_groups(in) * 128;
+  return a256((size_t)m * Kp * 2) + a256((size_t)m * 4) + a256(2 * (Kp / 32) * 16 * 4);
+}
+
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+// One workgroup per row of X: row maximum, exponent, scaled fp16 copy.
+__global__ __launch_bounds__(256) void k_gemm_prep_x(const uint16_t* __restrict__ X, int in, int Kp,
+                                                     GemmWs ws) {
+  const int m = blockIdx.x;
+  const uint16_t* xr = X + (size_t)m * in;
+  float mx = 0.0f;
+  for (int j = threadIdx.x; j < in; j += 256) mx = fmaxf(mx, fabsf(bf16_bits_to_f32(xr[j])));
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) mx = fmaxf(mx, __shfl_xor(mx, s, 64));
+  __shared__ float smx[4];
+  __shared__ int s_e;
+  if ((threadIdx.x & 63) == 0) smx[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float t = fmaxf(fmaxf(smx[0], smx[1]), fmaxf(smx[2], smx[3]));
+    s_e = (t > 0.0f) ? 14 - ilogbf(t) : 0;
+  }
+  __syncthreads();
+  const int e = s_e;
+  uint16_t* xo = ws.xh + (size_t)m * Kp;
+  for (int kk = threadIdx.x; kk < Kp; kk += 256) {
+    const int blk = kk >> 5, kap = kk & 31;
+    const int col = blk * 32 + (kap >> 1) + 16 * (kap & 1);
+    const float v = col < in ? bf16_bits_to_f32(xr[col]) : 0.0f;
+    xo[kk] = f32_to_f16_bits(ldexpf(v, e));
+  }
+  if (threadIdx.x == 0) ws.rowexp[m] = e;
+}
+
+__global__ void k_gemm_prep_h(const uint16_t* __restrict__ h, int in, int Kp, GemmWs ws) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;  // (p, blk, pair)
+  const int nb = Kp / 32;
+  if (idx >= 2 * nb * 16) return;
+  const int pr = idx & 15, blk = (idx >> 4) % nb, p = idx / (16 * nb);
+  const int c0 = blk * 32 + pr, c1 = c0 + 16;
+  const uint32_t lo = c0 < in ? h[(size_t)p * in + c0] : 0;
+  const uint32_t hi = c1 < in ? h[(size_t)p * in + c1] : 0;
+  ws.hpairs[idx] = lo | (hi << 16);
+}
+
+// 128 x 128 output tile per workgroup, 4 waves in 2 x 2, 64 x 64 per wave.
+__global__ __launch_bounds__(256) void k_gemm(const uint4* __restrict__ planes,
+                                              const uint16_t* __restrict__ g, int out, int M,
+                                              int Kp, GemmWs ws, void* Y, int y_dtype) {
+  const int n0 = blockIdx.x * kBN, m0 = blockIdx.y * kBM;
+  const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63;
+  const int wm = (wv >> 1) * 64, wn = (wv & 1) * 64;
+  const int KG = Kp / 128;
+  const int out_pad = row_groups(out) * 64;
+
+  __shared__ uint32_t sA[kBM * kLdsStride];
+  __shared__ uint32_t sB[2][kBN * kLdsStride];
+
+  v4f acc[2][4][4];
+#pragma unroll
+  for (int p = 0; p < 2; ++p)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[p][i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+  // B loader: thread -> (row n0 + (tid & 127), path tid >> 7)
+  const int bn = n0 + (tid & 127), bp = tid >> 7;
+  const bool bvalid = bn < out_pad;
+  const uint32_t* wsrc = (const uint32_t*)(planes + unit_index(bn >> 6, 0, bp, bn & 63, KG));
+  // A loader: thread -> row m0 + (tid >> 1), half (tid & 1) of the 32 columns
+  const int am = m0 + (tid >> 1), ah = tid & 1;
+  const bool avalid = am < M;
+  const uint4* asrc = (const uint4*)(ws.xh + (size_t)(avalid ? am : 0) * Kp) + ah * 2;
+
+  for (int k0 = 0; k0 < Kp; k0 += kBK) {
+    const int kb = k0 >> 5;
+    // stage A (two 16-byte chunks per thread)
+    uint4 a0 = make_uint4(0, 0, 0, 0), a1 = a0;
+    if (avalid) {
+      a0 = asrc[(size_t)kb * 4 + 0];
+      a1 = asrc[(size_t)kb * 4 + 1];
+    }
+    // stage B: one canonical word, 16 sign-flipped fp16 pairs
+    uint32_t w = 0;
+    if (bvalid) w = wsrc[(size_t)(kb >> 2) * 128 * 4 + (kb & 3)];
+    const uint32_t* hp = ws.hpairs + ((size_t)bp * (Kp / 32) + kb) * 16;
+    uint32_t e[16];
+#pragma unroll
+    for (int mm = 0; mm < 16; ++mm) e[mm] = hp[mm] ^ ((w << (15 - mm)) & 0x80008000u);
+    __syncthreads();
+    uint32_t* da = sA + (tid >> 1) * kLdsStride + ah * 8;
+    *(uint4*)(da) = a0;
+    *(uint4*)(da + 4) = a1;
+    uint32_t* db = sB[bp] + (tid & 127) * kLdsStride;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) *(uint4*)(db + 4 * q) = make_uint4(e[4 * q], e[4 * q + 1], e[4 * q + 2], e[4 * q + 3]);
+    __syncthreads();
+
+    const int fr = l & 15, fg = l >> 4;
+    v8h fa[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[i] = *(const v8h*)(sA + (wm + 16 * i + fr) * kLdsStride + 4 * fg);
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const v8h fb = *(const v8h*)(sB[p] + (wn + 16 * j + fr) * kLdsStride + 4 * fg);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          acc[p][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[i], fb, acc[p][i][j], 0, 0, 0);
+      }
+    }
+  }
+
+  // epilogue: C[i][j] of a 16x16 tile: lane l, reg r -> row 4(l/16)+r, col l%16
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int n = n0 + wn + 16 * j + (l & 15);
+    if (n >= out) continue;
+    const float g0 = f16_bits_to_f32(g[n]), g1 = f16_bits_to_f32(g[out + n]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + wm + 16 * i + 4 * (l >> 4) + r;
+        if (m >= M) continue;
+        const float v = ldexpf(g0 * acc[0][i][j][r] + g1 * acc[1][i][j][r], -ws.rowexp[m]);
+        if (y_dtype == RABIT_OUT_F32)
+          ((float*)Y)[(size_t)m * out + n] = v;
+        else
+          ((uint16_t*)Y)[(size_t)m * out + n] = f32_to_bf16_rne(v);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+size_t gemm_workspace_bytes(int out, int in, int m) {
+  (void)out;
+  return ws_bytes(in, m);
+}
+
+hipError_t launch_gemm(const uint4* planes, const uint16_t* g, const uint16_t* h, int out, int in,
+                       const uint16_t* X, int m, void* Y, int y_dtype, void* ws, hipStream_t st) {
+  const int Kp = col_groups(in) * 128;
+  GemmWs w = carve(ws, in, m);
+  hipLaunchKernelGGL(k_gemm_prep_x, dim3(m), dim3(256), 0, st, X, in, Kp, w);
+  const int nh = 2 * (Kp / 32) * 16;
+  hipLaunchKernelGGL(k_gemm_prep_h, dim3((nh + 255) / 256), dim3(256), 0, st, h, in, Kp, w);
+  const dim3 grid((out + kBN - 1) / kBN, (m + kBM - 1) / kBM);
+  hipLaunchKernelGGL(k_gemm, grid, dim3(256), 0, st, planes, g, out, m, Kp, w, Y, y_dtype);
+  return hipGetLastError();
+}
+
+}  // namespace rabit

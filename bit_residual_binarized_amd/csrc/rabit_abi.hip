@@ -1,0 +1,335 @@
+// extern "C" entry points of librabit: argument validation, workspace
+// carving and dispatch to the HIP launchers. Nothing here allocates device
+// memory; every call enqueues on the caller's stream.
+#include <algorithm>
+
+#include "rabit_internal.h"
+
+using namespace rabit;
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return na && nb && x < y + nb && y < x + na;
+}
+
+int dev_status(hipError_t e) { return e == hipSuccess ? RABIT_OK : RABIT_EDEVICE; }
+
+int check_dims(int64_t out, int64_t in) {
+  if (out < 1 || in < 1 || out > RABIT_MAX_FEATURES || in > RABIT_MAX_FEATURES) return RABIT_ESHAPE;
+  return RABIT_OK;
+}
+
+// layer header checks shared by every op that reads a packed layer
+int check_layer(const rabit_layer* L) {
+  if (!L) return RABIT_EINVAL;
+  if (L->layout_version != RABIT_LAYOUT_V1) return RABIT_EINVAL;
+  if (L->n_paths != 2) return RABIT_EUNSUPPORTED;
+  int s = check_dims(L->out_features, L->in_features);
+  if (s) return s;
+  if (!L->planes || !L->g || !L->h) return RABIT_EINVAL;
+  if (!aligned16(L->planes) || !aligned16(L->g) || !aligned16(L->h)) return RABIT_EALIGN;
+  const size_t pb = rabit_planes_bytes(L->out_features, L->in_features, 2);
+  const size_t gb = (size_t)2 * L->out_features * 2, hb = (size_t)2 * L->in_features * 2;
+  if (overlap(L->planes, pb, L->g, gb) || overlap(L->planes, pb, L->h, hb) ||
+      overlap(L->g, gb, L->h, hb))
+    return RABIT_EINVAL;
+  return RABIT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t rabit_layout_version(void) { return RABIT_LAYOUT_V1; }
+
+const char* rabit_status_string(int status) {
+  switch (status) {
+    case RABIT_OK: return "ok";
+    case RABIT_EINVAL: return "invalid argument";
+    case RABIT_ESHAPE: return "unsupported shape";
+    case RABIT_EALIGN: return "device pointer not 16-byte aligned";
+    case RABIT_EUNSUPPORTED: return "unsupported option";
+    case RABIT_EDEVICE: return "HIP launch or runtime error";
+    case RABIT_EWORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+  }
+}
+
+size_t rabit_planes_bytes(int32_t out, int32_t in, int32_t n_paths) {
+  if (check_dims(out, in) || n_paths != 2) return 0;
+  return (size_t)n_paths * row_groups(out) * 64 * col_groups(in) * 16;
+}
+
+size_t rabit_pack_workspace_bytes(int32_t out, int32_t in) {
+  if (check_dims(out, in)) return 0;
+  return pack_workspace_bytes(out, in);
+}
+
+size_t rabit_gemv_workspace_bytes(int32_t out, int32_t in, int32_t batch) {
+  if (check_dims(out, in) || batch < 1 || batch > RABIT_MAX_GEMV_BATCH) return 0;
+  return gemv_workspace_bytes(out, in, batch);
+}
+
+size_t rabit_gemm_workspace_bytes(int32_t out, int32_t in, int32_t m) {
+  if (check_dims(out, in) || m < 1 || m > RABIT_MAX_GEMM_M) return 0;
+  return gemm_workspace_bytes(out, in, m);
+}
+
+int rabit_pack(const float* W, uint32_t scale_mode, const rabit_layer* L, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  if (!L || !W) return RABIT_EINVAL;
+  if (scale_mode != RABIT_SCALES_GIVEN && scale_mode != RABIT_SCALES_MEANABS) return RABIT_EINVAL;
+  int s = check_layer(L);
+  if (s) return s;
+  if (!aligned16(W)) return RABIT_EALIGN;
+  const int out = L->out_features, in = L->in_features;
+  const size_t wb = (size_t)out * in * 4;
+  if (overlap(W, wb, L->planes, rabit_planes_bytes(out, in, 2)) ||
+      overlap(W, wb, L->g, (size_t)4 * out) || overlap(W, wb, L->h, (size_t)4 * in))
+    return RABIT_EINVAL;
+  const bool meanabs = scale_mode == RABIT_SCALES_MEANABS;
+  if (meanabs) {
+    if (!workspace) return RABIT_EWORKSPACE;
+    if (workspace_bytes < pack_workspace_bytes(out, in)) return RABIT_EWORKSPACE;
+    if (!aligned16(workspace)) return RABIT_EALIGN;
+  }
+  return dev_status(launch_pack(W, out, in, meanabs, L->g, L->h, (uint4*)L->planes, workspace,
+                                (hipStream_t)stream));
+}
+
+int rabit_unpack(const rabit_layer* L, uint32_t* words, void* stream) {
+  int s = check_layer(L);
+  if (s) return s;
+  if (!words) return RABIT_EINVAL;
+  if (!aligned16(words)) return RABIT_EALIGN;
+  return dev_status(launch_unpack((const uint4*)L->planes, L->out_features, L->in_features, words,
+                                  (hipStream_t)stream));
+}
+
+namespace {
+int check_gemv_common(const rabit_layer* L, int32_t batch, void* workspace, size_t workspace_bytes) {
+  int s = check_layer(L);
+  if (s) return s;
+  if (batch < 1 || batch > RABIT_MAX_GEMV_BATCH) return RABIT_ESHAPE;
+  if (!workspace || workspace_bytes < gemv_workspace_bytes(L->out_features, L->in_features, batch))
+    return RABIT_EWORKSPACE;
+  if (!aligned16(workspace)) return RABIT_EALIGN;
+  return RABIT_OK;
+}
+int check_gemv_x(const rabit_layer* L, const uint16_t* x) {
+  if (!x) return RABIT_EINVAL;
+  if (!aligned16(x)) return RABIT_EALIGN;
+  (void)L;
+  return RABIT_OK;
+}
+int check_gemv_y(const rabit_layer* L, int32_t batch, void* y, int32_t y_dtype, const void* x) {
+  if (!y) return RABIT_EINVAL;
+  if (y_dtype != RABIT_OUT_F32 && y_dtype != RABIT_OUT_BF16) return RABIT_EINVAL;
+  if (!aligned16(y)) return RABIT_EALIGN;
+  const int out = L->out_features, in = L->in_features;
+  const size_t yb = (size_t)batch * out * (y_dtype == RABIT_OUT_F32 ? 4 : 2);
+  if ((x && overlap(y, yb, x, (size_t)batch * in * 2)) ||
+      overlap(y, yb, L->planes, rabit_planes_bytes(out, in, 2)))
+    return RABIT_EINVAL;
+  return RABIT_OK;
+}
+}  // namespace
+
+int rabit_gemv(const rabit_layer* L, const uint16_t* x, int32_t batch, void* y, int32_t y_dtype,
+               void* workspace, size_t workspace_bytes, void* stream) {
+  int s = check_layer(L);
+  if (s) return s;
+  if (!x || !y) return RABIT_EINVAL;
+  if (y_dtype != RABIT_OUT_F32 && y_dtype != RABIT_OUT_BF16) return RABIT_EINVAL;
+  if (batch < 1 || batch > RABIT_MAX_GEMV_BATCH) return RABIT_ESHAPE;
+  if ((s = check_gemv_x(L, x)) || (s = check_gemv_y(L, batch, y, y_dtype, x))) return s;
+  if ((s = check_gemv_common(L, batch, workspace, workspace_bytes))) return s;
+  return dev_status(launch_gemv((const uint4*)L->planes, L->g, L->h, L->out_features,
+                                L->in_features, x, batch, y, y_dtype, workspace,
+                                (hipStream_t)stream));
+}
+
+int rabit_gemv_prepare(const rabit_layer* L, const uint16_t* x, int32_t batch, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  int s = check_gemv_common(L, batch, workspace, workspace_bytes);
+  if (s) return s;
+  if ((s = check_gemv_x(L, x))) return s;
+  return dev_status(launch_gemv_prepare(L->h, L->out_features, L->in_features, x, batch, workspace,
+                                        (hipStream_t)stream));
+}
+
+int rabit_gemv_run(const rabit_layer* L, int32_t batch, void* y, int32_t y_dtype, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  int s = check_gemv_common(L, batch, workspace, workspace_bytes);
+  if (s) return s;
+  if ((s = check_gemv_y(L, batch, y, y_dtype, nullptr))) return s;
+  return dev_status(launch_gemv_run((const uint4*)L->planes, L->g, L->out_features, L->in_features,
+                                    batch, y, y_dtype, workspace, (hipStream_t)stream));
+}
+
+int rabit_gemm(const rabit_layer* L, const uint16_t* X, int32_t m, void* Y, int32_t y_dtype,
+               void* workspace, size_t workspace_bytes, void* stream) {
+  int s = check_layer(L);
+  if (s) return s;
+  if (!X || !Y) return RABIT_EINVAL;
+  if (y_dtype != RABIT_OUT_F32 && y_dtype != RABIT_OUT_BF16) return RABIT_EINVAL;
+  if (m < 1 || m > RABIT_MAX_GEMM_M) return RABIT_ESHAPE;
+  if (!aligned16(X) || !aligned16(Y)) return RABIT_EALIGN;
+  const int out = L->out_features, in = L->in_features;
+  const size_t yb = (size_t)m * out * (y_dtype == RABIT_OUT_F32 ? 4 : 2);
+  if (overlap(Y, yb, X, (size_t)m * in * 2) ||
+      overlap(Y, yb, L->planes, rabit_planes_bytes(out, in, 2)))
+    return RABIT_EINVAL;
+  if (!workspace || workspace_bytes < gemm_workspace_bytes(out, in, m)) return RABIT_EWORKSPACE;
+  if (!aligned16(workspace)) return RABIT_EALIGN;
+  return dev_status(launch_gemm((const uint4*)L->planes, L->g, L->h, out, in, X, m, Y, y_dtype,
+                                workspace, (hipStream_t)stream));
+}
+
+// --------------------------------------------------------------------------
+// decode step
+// --------------------------------------------------------------------------
+namespace {
+
+struct DecodeWs {
+  uint16_t *xa, *xb, *n, *attn, *z;
+  float *q, *k, *v, *o, *gate, *up, *down;
+  void* lin;
+  size_t lin_bytes;
+};
+
+size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int check_cfg(const rabit_decoder_cfg* c) {
+  if (!c) return RABIT_EINVAL;
+  if (c->hidden < 1 || c->ffn < 1 || c->n_layers < 1 || c->hidden > RABIT_MAX_FEATURES ||
+      c->ffn > RABIT_MAX_FEATURES)
+    return RABIT_ESHAPE;
+  if (!c->mlp_only) {
+    if (c->n_heads < 1 || c->n_kv_heads < 1 || c->head_dim < 1 || c->n_heads % c->n_kv_heads)
+      return RABIT_ESHAPE;
+    if ((int64_t)c->n_heads * c->head_dim != c->hidden) return RABIT_ESHAPE;
+  }
+  if (!(c->rms_eps > 0.0f)) return RABIT_EINVAL;
+  return RABIT_OK;
+}
+
+size_t lin_ws(const rabit_decoder_cfg* c, int batch) {
+  const int kv = c->mlp_only ? 0 : c->n_kv_heads * c->head_dim;
+  size_t mx = 0;
+  const int shapes[5][2] = {{c->hidden, c->hidden}, {kv, c->hidden}, {c->ffn, c->hidden},
+                            {c->hidden, c->ffn}, {c->hidden, c->hidden}};
+  for (auto& sh : shapes) {
+    if (sh[0] < 1) continue;
+    const size_t b = batch <= RABIT_MAX_GEMV_BATCH ? gemv_workspace_bytes(sh[0], sh[1], batch)
+                                                   : gemm_workspace_bytes(sh[0], sh[1], batch);
+    mx = std::max(mx, b);
+  }
+  return mx;
+}
+
+size_t decode_ws(const rabit_decoder_cfg* c, int batch, DecodeWs* w, void* base) {
+  const int H = c->hidden, F = c->ffn;
+  const int kv = c->mlp_only ? 0 : c->n_kv_heads * c->head_dim;
+  const size_t sz[12] = {a256((size_t)batch * H * 2), a256((size_t)batch * H * 2),
+                         a256((size_t)batch * H * 2), a256((size_t)batch * H * 2),
+                         a256((size_t)batch * F * 2), a256((size_t)batch * H * 4),
+                         a256((size_t)batch * std::max(kv, 1) * 4),
+                         a256((size_t)batch * std::max(kv, 1) * 4), a256((size_t)batch * H * 4),
+                         a256((size_t)batch * F * 4), a256((size_t)batch * F * 4),
+                         a256((size_t)batch * H * 4)};
+  size_t off = 0;
+  char* p = (char*)base;
+  void** slots[12] = {(void**)&w->xa,   (void**)&w->xb, (void**)&w->n,    (void**)&w->attn,
+                      (void**)&w->z,    (void**)&w->q,  (void**)&w->k,    (void**)&w->v,
+                      (void**)&w->o,    (void**)&w->gate, (void**)&w->up, (void**)&w->down};
+  for (int i = 0; i < 12; ++i) {
+    if (base) *slots[i] = p + off;
+    off += sz[i];
+  }
+  w->lin = base ? p + off : nullptr;
+  w->lin_bytes = lin_ws(c, batch);
+  return off + w->lin_bytes;
+}
+
+hipError_t linear(const rabit_layer& L, const uint16_t* x, int batch, float* y, const DecodeWs& w,
+                  hipStream_t st) {
+  if (batch <= RABIT_MAX_GEMV_BATCH)
+    return launch_gemv((const uint4*)L.planes, L.g, L.h, L.out_features, L.in_features, x, batch,
+                       y, RABIT_OUT_F32, w.lin, st);
+  return launch_gemm((const uint4*)L.planes, L.g, L.h, L.out_features, L.in_features, x, batch, y,
+                     RABIT_OUT_F32, w.lin, st);
+}
+
+}  // namespace
+
+size_t rabit_decode_workspace_bytes(const rabit_decoder_cfg* cfg, int32_t batch) {
+  if (check_cfg(cfg) || batch < 1 || batch > RABIT_MAX_GEMM_M) return 0;
+  DecodeWs w;
+  return decode_ws(cfg, batch, &w, nullptr);
+}
+
+int rabit_decode_step(const rabit_decoder_cfg* cfg, const rabit_layer* layers, const uint16_t* x,
+                      int32_t batch, uint16_t* out, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  int s = check_cfg(cfg);
+  if (s) return s;
+  if (!layers || !x || !out) return RABIT_EINVAL;
+  if (batch < 1 || batch > RABIT_MAX_GEMM_M) return RABIT_ESHAPE;
+  if (!aligned16(x) || !aligned16(out)) return RABIT_EALIGN;
+  const int H = cfg->hidden, F = cfg->ffn;
+  const int kv = cfg->mlp_only ? 0 : cfg->n_kv_heads * cfg->head_dim;
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    for (int m = cfg->mlp_only ? 4 : 0; m < 7; ++m) {
+      const rabit_layer& L = layers[l * 7 + m];
+      if ((s = check_layer(&L))) return s;
+      static const int kOut[7] = {0, 1, 1, 0, 2, 2, 0}, kIn[7] = {0, 0, 0, 0, 0, 0, 2};
+      const int want_out = kOut[m] == 0 ? H : (kOut[m] == 1 ? kv : F);
+      const int want_in = kIn[m] == 0 ? H : F;
+      if (L.out_features != want_out || L.in_features != want_in) return RABIT_ESHAPE;
+    }
+  }
+  DecodeWs w;
+  const size_t need = decode_ws(cfg, batch, &w, nullptr);
+  if (!workspace || workspace_bytes < need) return RABIT_EWORKSPACE;
+  if (!aligned16(workspace)) return RABIT_EALIGN;
+  decode_ws(cfg, batch, &w, workspace);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  const uint16_t* cur = x;
+  for (int l = 0; l < cfg->n_layers && e == hipSuccess; ++l) {
+    const rabit_layer* Ls = layers + l * 7;
+    uint16_t* nxt = (l == cfg->n_layers - 1) ? out : (cur == w.xa ? w.xb : w.xa);
+    if (!cfg->mlp_only) {
+      if (!e) e = launch_rmsnorm(cur, w.n, batch, H, cfg->rms_eps, st);
+      if (!e) e = linear(Ls[0], w.n, batch, w.q, w, st);
+      if (!e) e = linear(Ls[1], w.n, batch, w.k, w, st);
+      if (!e) e = linear(Ls[2], w.n, batch, w.v, w, st);
+      if (!e) e = launch_attn_1tok(w.v, kv, w.attn, batch, cfg->n_heads, cfg->n_kv_heads,
+                                   cfg->head_dim, st);
+      if (!e) e = linear(Ls[3], w.attn, batch, w.o, w, st);
+      if (!e) e = launch_residual_add(cur, w.o, nxt, batch, H, st);
+      cur = nxt;
+    }
+    if (!e) e = launch_rmsnorm(cur, w.n, batch, H, cfg->rms_eps, st);
+    if (!e) e = linear(Ls[4], w.n, batch, w.gate, w, st);
+    if (!e) e = linear(Ls[5], w.n, batch, w.up, w, st);
+    if (!e) e = launch_silu_mul(w.gate, w.up, w.z, batch, F, st);
+    if (!e) e = linear(Ls[6], w.z, batch, w.down, w, st);
+    // the residual may write in place (cur == nxt when attention ran)
+    if (!e) e = launch_residual_add(cur, w.down, nxt, batch, H, st);
+    cur = nxt;
+  }
+  return dev_status(e);
+}
+
+int rabit_test_f64_to_16(const double* in, uint16_t* out, int32_t n, int32_t bf16, void* stream) {
+  if (!in || !out || n < 1) return RABIT_EINVAL;
+  return dev_status(launch_test_f64_to_16(in, out, n, bf16, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,312 @@
+"""Thin ctypes binding of librabit (include/rabit.h).
+
+Argument marshalling only: every step of the hot path runs in the HIP
+kernels of librabit.so. torch supplies device memory and the current stream.
+There is no fallback: if the library is missing, load() raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "librabit.so")
+
+RABIT_OK = 0
+RABIT_EINVAL = -1
+RABIT_ESHAPE = -2
+RABIT_EALIGN = -3
+RABIT_EUNSUPPORTED = -4
+RABIT_EDEVICE = -5
+RABIT_EWORKSPACE = -6
+RABIT_SCALES_GIVEN = 0
+RABIT_SCALES_MEANABS = 1
+RABIT_OUT_F32 = 0
+RABIT_OUT_BF16 = 1
+RABIT_LAYOUT_V1 = 1
+MAX_GEMV_BATCH = 16
+
+# every symbol include/rabit.h declares
+EXPORTS = [
+    "rabit_planes_bytes", "rabit_pack_workspace_bytes", "rabit_gemv_workspace_bytes",
+    "rabit_gemm_workspace_bytes", "rabit_pack", "rabit_unpack", "rabit_gemv", "rabit_gemm",
+    "rabit_decode_workspace_bytes", "rabit_decode_step", "rabit_status_string",
+    "rabit_layout_version", "rabit_test_f64_to_16", "rabit_gemv_prepare", "rabit_gemv_run",
+]
+
+
+class RabitLayerC(ctypes.Structure):
+    _fields_ = [
+        ("layout_version", ctypes.c_int32),
+        ("out_features", ctypes.c_int32),
+        ("in_features", ctypes.c_int32),
+        ("n_paths", ctypes.c_int32),
+        ("planes", ctypes.c_void_p),
+        ("g", ctypes.c_void_p),
+        ("h", ctypes.c_void_p),
+    ]
+
+
+class DecoderCfgC(ctypes.Structure):
+    _fields_ = [
+        ("hidden", ctypes.c_int32),
+        ("ffn", ctypes.c_int32),
+        ("n_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("n_layers", ctypes.c_int32),
+        ("rms_eps", ctypes.c_float),
+        ("mlp_only", ctypes.c_int32),
+    ]
+
+
+class RabitError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        self.code = code
+        super().__init__(f"{what}: {status_string(code)} ({code})")
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load librabit.so (built by bit_residual_binarized_amd.build); raise if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"librabit.so not found at {path}; run "
+                           "`python -m bit_residual_binarized_amd.build` first")
+    lib = ctypes.CDLL(path)
+    vp, sz, i32, u32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_uint32
+    lp = ctypes.POINTER(RabitLayerC)
+    sig = {
+        "rabit_planes_bytes": (sz, [i32, i32, i32]),
+        "rabit_pack_workspace_bytes": (sz, [i32, i32]),
+        "rabit_gemv_workspace_bytes": (sz, [i32, i32, i32]),
+        "rabit_gemm_workspace_bytes": (sz, [i32, i32, i32]),
+        "rabit_pack": (ctypes.c_int, [vp, u32, lp, vp, sz, vp]),
+        "rabit_unpack": (ctypes.c_int, [lp, vp, vp]),
+        "rabit_gemv": (ctypes.c_int, [lp, vp, i32, vp, i32, vp, sz, vp]),
+        "rabit_gemm": (ctypes.c_int, [lp, vp, i32, vp, i32, vp, sz, vp]),
+        "rabit_gemv_prepare": (ctypes.c_int, [lp, vp, i32, vp, sz, vp]),
+        "rabit_gemv_run": (ctypes.c_int, [lp, i32, vp, i32, vp, sz, vp]),
+        "rabit_decode_workspace_bytes": (sz, [ctypes.POINTER(DecoderCfgC), i32]),
+        "rabit_decode_step": (ctypes.c_int, [ctypes.POINTER(DecoderCfgC), lp, vp, i32, vp, vp, sz, vp]),
+        "rabit_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "rabit_layout_version": (i32, []),
+        "rabit_test_f64_to_16": (ctypes.c_int, [vp, vp, i32, i32, vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def status_string(code: int) -> str:
+    return load().rabit_status_string(code).decode()
+
+
+def _check(code: int, what: str) -> None:
+    if code != RABIT_OK:
+        raise RabitError(code, what)
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t: torch.Tensor | None):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def planes_bytes(out: int, inp: int) -> int:
+    return int(load().rabit_planes_bytes(out, inp, 2))
+
+
+@dataclass
+class PackedLayer:
+    """Device buffers of one frozen 2-path layer (see rabit_layer in rabit.h)."""
+    out_features: int
+    in_features: int
+    planes: torch.Tensor  # uint8 [planes_bytes]
+    g: torch.Tensor       # int16 fp16 bits [2, out]
+    h: torch.Tensor       # int16 fp16 bits [2, in]
+
+    @staticmethod
+    def empty(out: int, inp: int, device="cuda") -> "PackedLayer":
+        pb = planes_bytes(out, inp)
+        if pb == 0:
+            raise RabitError(RABIT_ESHAPE, "planes_bytes")
+        return PackedLayer(out, inp,
+                           torch.empty(pb, dtype=torch.uint8, device=device),
+                           torch.empty(2, out, dtype=torch.int16, device=device),
+                           torch.empty(2, inp, dtype=torch.int16, device=device))
+
+    def c(self) -> RabitLayerC:
+        return RabitLayerC(RABIT_LAYOUT_V1, self.out_features, self.in_features, 2,
+                           self.planes.data_ptr(), self.g.data_ptr(), self.h.data_ptr())
+
+    def scales_f16(self):
+        return self.g.view(torch.float16), self.h.view(torch.float16)
+
+
+def _ws(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+
+
+def pack(w: torch.Tensor, layer: PackedLayer, mode: int = RABIT_SCALES_MEANABS,
+         workspace: torch.Tensor | None = None, stream=None) -> PackedLayer:
+    """Derive and pack both paths of `w` (float32 [out, in], cuda) into `layer`."""
+    lib = load()
+    assert w.dtype == torch.float32 and w.is_contiguous()
+    nb = lib.rabit_pack_workspace_bytes(layer.out_features, layer.in_features)
+    if workspace is None and mode == RABIT_SCALES_MEANABS:
+        workspace = _ws(nb, w.device)
+    lc = layer.c()
+    _check(lib.rabit_pack(_ptr(w), mode, ctypes.byref(lc), _ptr(workspace),
+                          0 if workspace is None else workspace.numel(), _stream(stream)),
+           "rabit_pack")
+    return layer
+
+
+def unpack(layer: PackedLayer, stream=None) -> torch.Tensor:
+    lib = load()
+    nw = (layer.in_features + 31) // 32
+    words = torch.empty(2, layer.out_features, nw, dtype=torch.int32, device=layer.planes.device)
+    lc = layer.c()
+    _check(lib.rabit_unpack(ctypes.byref(lc), _ptr(words), _stream(stream)), "rabit_unpack")
+    return words
+
+
+def gemv_workspace(layer: PackedLayer, batch: int) -> torch.Tensor:
+    nb = load().rabit_gemv_workspace_bytes(layer.out_features, layer.in_features, batch)
+    return _ws(nb, layer.planes.device)
+
+
+def gemv(layer: PackedLayer, x: torch.Tensor, y_dtype: int = RABIT_OUT_F32,
+         y: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+         stream=None) -> torch.Tensor:
+    """y[b] = Σ_p g_p ⊙ (B_p (h_p ⊙ x[b])); x bfloat16 [batch, in] on cuda."""
+    lib = load()
+    assert x.dtype == torch.bfloat16 and x.is_contiguous()
+    batch = x.shape[0]
+    if y is None:
+        dt = torch.float32 if y_dtype == RABIT_OUT_F32 else torch.bfloat16
+        y = torch.empty(batch, layer.out_features, dtype=dt, device=x.device)
+    if workspace is None:
+        workspace = gemv_workspace(layer, batch)
+    lc = layer.c()
+    _check(lib.rabit_gemv(ctypes.byref(lc), _ptr(x), batch, _ptr(y), y_dtype, _ptr(workspace),
+                          workspace.numel(), _stream(stream)), "rabit_gemv")
+    return y
+
+
+def gemv_prepare(layer: PackedLayer, x: torch.Tensor, workspace: torch.Tensor, stream=None) -> None:
+    assert x.dtype == torch.bfloat16 and x.is_contiguous()
+    lc = layer.c()
+    _check(load().rabit_gemv_prepare(ctypes.byref(lc), _ptr(x), x.shape[0], _ptr(workspace),
+                                     workspace.numel(), _stream(stream)), "rabit_gemv_prepare")
+
+
+def gemv_run(layer: PackedLayer, batch: int, y: torch.Tensor, workspace: torch.Tensor,
+             y_dtype: int = RABIT_OUT_F32, stream=None) -> torch.Tensor:
+    lc = layer.c()
+    _check(load().rabit_gemv_run(ctypes.byref(lc), batch, _ptr(y), y_dtype, _ptr(workspace),
+                                 workspace.numel(), _stream(stream)), "rabit_gemv_run")
+    return y
+
+
+def gemm_workspace(layer: PackedLayer, m: int) -> torch.Tensor:
+    nb = load().rabit_gemm_workspace_bytes(layer.out_features, layer.in_features, m)
+    return _ws(nb, layer.planes.device)
+
+
+def gemm(layer: PackedLayer, xm: torch.Tensor, y_dtype: int = RABIT_OUT_F32,
+         y: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+         stream=None) -> torch.Tensor:
+    lib = load()
+    assert xm.dtype == torch.bfloat16 and xm.is_contiguous()
+    m = xm.shape[0]
+    if y is None:
+        dt = torch.float32 if y_dtype == RABIT_OUT_F32 else torch.bfloat16
+        y = torch.empty(m, layer.out_features, dtype=dt, device=xm.device)
+    if workspace is None:
+        workspace = gemm_workspace(layer, m)
+    lc = layer.c()
+    _check(lib.rabit_gemm(ctypes.byref(lc), _ptr(xm), m, _ptr(y), y_dtype, _ptr(workspace),
+                          workspace.numel(), _stream(stream)), "rabit_gemm")
+    return y
+
+
+MATRICES = ("q", "k", "v", "o", "gate", "up", "down")
+
+
+@dataclass
+class DecoderCfg:
+    hidden: int
+    ffn: int
+    n_heads: int = 1
+    n_kv_heads: int = 1
+    head_dim: int = 1
+    n_layers: int = 1
+    rms_eps: float = 1e-5
+    mlp_only: bool = False
+
+    def c(self) -> DecoderCfgC:
+        return DecoderCfgC(self.hidden, self.ffn, self.n_heads, self.n_kv_heads, self.head_dim,
+                           self.n_layers, self.rms_eps, int(self.mlp_only))
+
+
+def decode_workspace(cfg: DecoderCfg, batch: int, device="cuda") -> torch.Tensor:
+    cc = cfg.c()
+    nb = load().rabit_decode_workspace_bytes(ctypes.byref(cc), batch)
+    if nb == 0:
+        raise RabitError(RABIT_ESHAPE, "rabit_decode_workspace_bytes")
+    return _ws(nb, device)
+
+
+def layer_array(cfg: DecoderCfg, layers: list[dict]):
+    """ctypes array [n_layers * 7] in q,k,v,o,gate,up,down order."""
+    arr = (RabitLayerC * (7 * cfg.n_layers))()
+    for li, mats in enumerate(layers):
+        for mi, name in enumerate(MATRICES):
+            pl = mats.get(name)
+            if pl is not None:
+                arr[li * 7 + mi] = pl.c()
+    return arr
+
+
+def decode_step(cfg: DecoderCfg, layers, x: torch.Tensor, out: torch.Tensor | None = None,
+                workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """One decode step through cfg.n_layers blocks; layers is a list of dicts
+    name -> PackedLayer, or a prebuilt layer_array."""
+    lib = load()
+    assert x.dtype == torch.bfloat16 and x.is_contiguous()
+    batch = x.shape[0]
+    if out is None:
+        out = torch.empty_like(x)
+    if workspace is None:
+        workspace = decode_workspace(cfg, batch, x.device)
+    arr = layers if isinstance(layers, ctypes.Array) else layer_array(cfg, layers)
+    cc = cfg.c()
+    _check(lib.rabit_decode_step(ctypes.byref(cc), arr, _ptr(x), batch, _ptr(out),
+                                 _ptr(workspace), workspace.numel(), _stream(stream)),
+           "rabit_decode_step")
+    return out
+
+
+def test_f64_to_16(v: torch.Tensor, bf16: bool, stream=None) -> torch.Tensor:
+    lib = load()
+    assert v.dtype == torch.float64 and v.is_cuda
+    out = torch.empty(v.numel(), dtype=torch.int16, device=v.device)
+    _check(lib.rabit_test_f64_to_16(_ptr(v), _ptr(out), v.numel(), int(bf16), _stream(stream)),
+           "rabit_test_f64_to_16")
+    return out

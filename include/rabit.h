@@ -1,0 +1,238 @@
+/*
+ * rabit.h - C ABI of the MI355X (gfx950) hot path for RaBiT-style 2-path
+ * residual binarization.
+ *
+ * Method (the pages about "RaBiT: Residual-Aware Binarization Training for
+ * Accurate and Efficient LLMs", arXiv 2602.05367):
+ *   - paper §4.1, "Binary Building Blocks": W_hat = g ⊙ B ⊙ h, B in {±1}
+ *   - paper §4.1, "Multi-bit Approximation via Stacking": W_hat^(2) =
+ *     Σ_{p=1,2} g_p ⊙ B_p ⊙ h_p; g_p is per output row, h_p per input column
+ *     (paper §4.3 maps g to the output side and h to the input side)
+ *   - paper §4.2, "The Coupled Forward Pass": B_1 = sign(W), R_1 = W − W_hat_1,
+ *     B_2 = sign(R_1); after training the cores are derived once from W and
+ *     frozen and W is discarded
+ *   - paper App. E.1, "Weight Packing": 32 columns per uint32, +1 -> 0, -1 -> 1
+ *   - paper §5.4: the layer is additions plus element-wise scaling
+ *
+ * Conventions for every entry point
+ *   - Every pointer named "device" is a device pointer owned by the caller;
+ *     the library keeps no pointer after a call returns and allocates nothing.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream). Argument errors are returned before anything is enqueued.
+ *   - Device pointers must be 16-byte aligned (RABIT_EALIGN otherwise).
+ *   - Calls that take a workspace need at least rabit_*_workspace_bytes()
+ *     bytes of it (RABIT_EWORKSPACE otherwise). The workspace is scratch: its
+ *     contents need not be initialised and are undefined afterwards. Two calls
+ *     that overlap in time must not share a workspace.
+ *   - Inputs containing NaN or Inf are not supported (results unspecified).
+ *   - Launch failures are reported as RABIT_EDEVICE.
+ *
+ * Readings where the pages are silent (the oracle implements the same):
+ *   - sign(v) = +1 unless v < 0, so +0, -0 give +1 (bit 0).
+ *   - Canonical word k of a row holds columns 32k .. 32k+31, column 32k+t in
+ *     bit t (LSB first); bits past the last column are 0.
+ *   - Mean-|.| scales: g[i] = fp16_rne(S_row(i) / in), h[j] =
+ *     fp16_rne(S_col(j) / out) where S are float64 sums of |M| in this order:
+ *       S_col: rows in tiles of 64, tiles in 4 segments of 16 rows; a segment
+ *         is summed in ascending row order from +0.0, the 4 segment sums of a
+ *         tile left to right, tile sums left to right.
+ *       S_row: columns in tiles of 256; lane l (0..63) of a tile sums tile
+ *         columns l, l+64, l+128, l+192 left to right; the lane values are
+ *         combined by v[l] += v[l+s] for s = 32,16,8,4,2,1 (result v[0]);
+ *         tile results are added left to right from +0.0.
+ *     The divide is one IEEE float64 division and the conversion a single
+ *     direct round-to-nearest-even to fp16 (overflow gives +inf).
+ *   - R_1 = fl32(W − B_1 * (g_1 * h_1)): the fp16 product is exact in fp32,
+ *     the subtraction rounds once.
+ */
+#ifndef RABIT_H_
+#define RABIT_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RABIT_LAYOUT_V1 1
+
+typedef enum {
+  RABIT_OK = 0,
+  RABIT_EINVAL = -1,        /* null pointer, bad enum, aliasing, bad layout version */
+  RABIT_ESHAPE = -2,        /* dimension < 1 or above the supported maximum */
+  RABIT_EALIGN = -3,        /* device pointer not 16-byte aligned */
+  RABIT_EUNSUPPORTED = -4,  /* n_paths != 2, or an unsupported option */
+  RABIT_EDEVICE = -5,       /* a HIP launch or runtime call failed */
+  RABIT_EWORKSPACE = -6     /* workspace missing or too small */
+} rabit_status;
+
+enum {
+  RABIT_SCALES_GIVEN = 0,   /* g_1, h_1 are inputs; g_2, h_2 are not touched */
+  RABIT_SCALES_MEANABS = 1  /* all four scales written as mean |.| (see above) */
+};
+
+enum {
+  RABIT_OUT_F32 = 0,        /* y as float32 */
+  RABIT_OUT_BF16 = 1        /* y rounded once (RNE) to bfloat16 */
+};
+
+/* Largest supported dimensions (out_features, in_features, batch, M). */
+#define RABIT_MAX_FEATURES (1 << 19)
+#define RABIT_MAX_GEMV_BATCH 16
+#define RABIT_MAX_GEMM_M (1 << 20)
+
+/*
+ * One frozen 2-path layer (paper §4.2: cores derived once, W discarded).
+ *
+ * planes  device, rabit_planes_bytes(out, in, 2) bytes. Device layout V1: a
+ *         sequence of 16-byte units indexed (rg, kg, p, r) in row-major order,
+ *         rg in [0, ceil(out/64)) = group of 64 output rows,
+ *         kg in [0, ceil(in/128)) = group of 128 input columns,
+ *         p in {0, 1} = path, r in [0, 64) = row inside the group.
+ *         Unit (rg, kg, p, r) holds, as 4 little-endian uint32, the canonical
+ *         words 4*kg + 0, +1, +2, +3 of row 64*rg + r of path p. Rows >= out
+ *         and words past ceil(in/32) are zero. (A wave of 64 lanes loads one
+ *         (rg, kg, p) slab of 1 KiB with one 16-byte load per lane.)
+ * g       device, fp16 bit patterns [2][out]: g_1 then g_2 (per output row)
+ * h       device, fp16 bit patterns [2][in]:  h_1 then h_2 (per input column)
+ */
+typedef struct {
+  int32_t layout_version;   /* RABIT_LAYOUT_V1 */
+  int32_t out_features;     /* rows of W (outputs) */
+  int32_t in_features;      /* columns of W (inputs) */
+  int32_t n_paths;          /* 2 */
+  void *planes;
+  uint16_t *g;
+  uint16_t *h;
+} rabit_layer;
+
+/* Bytes of the plane buffer: n_paths * ceil(out/64)*64 * ceil(in/128) * 16. */
+size_t rabit_planes_bytes(int32_t out_features, int32_t in_features, int32_t n_paths);
+
+/* Workspace needed by rabit_pack / rabit_gemv / rabit_gemm for these sizes. */
+size_t rabit_pack_workspace_bytes(int32_t out_features, int32_t in_features);
+size_t rabit_gemv_workspace_bytes(int32_t out_features, int32_t in_features, int32_t batch);
+size_t rabit_gemm_workspace_bytes(int32_t out_features, int32_t in_features, int32_t m);
+
+/*
+ * Derive and pack both paths of one layer (paper §4.2 steps 1-3, App. E.1).
+ *
+ * W           device float32 [out][in], row-major, contiguous (read only).
+ * scale_mode  RABIT_SCALES_MEANABS: writes g_1, h_1 = mean |W| per row/column,
+ *             then g_2, h_2 = mean |R_1|, and the planes.
+ *             RABIT_SCALES_GIVEN: reads g_1 = layer->g[0..out), h_1 =
+ *             layer->h[0..in); writes only the planes.
+ * layer       host pointer; its device buffers are written as described.
+ * Errors: RABIT_EINVAL (null, bad mode, W aliasing an output),
+ * RABIT_ESHAPE, RABIT_EALIGN, RABIT_EUNSUPPORTED, RABIT_EWORKSPACE,
+ * RABIT_EDEVICE.
+ */
+int rabit_pack(const float *W, uint32_t scale_mode, const rabit_layer *layer,
+               void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Test hook: write the canonical words of both planes.
+ * words  device uint32 [2][out][ceil(in/32)] (path 1 first).
+ */
+int rabit_unpack(const rabit_layer *layer, uint32_t *words, void *stream);
+
+/*
+ * Decode GEMV (paper App. E.1, "binary GEMV operations"):
+ *   y[b][i] = Σ_p g_p[i] * Σ_j B_p[i][j] * h_p[j] * x[b][j]
+ *
+ * x       device bfloat16 bit patterns [batch][in], row-major.
+ * batch   1 .. RABIT_MAX_GEMV_BATCH.
+ * y       device [batch][out], float32 (RABIT_OUT_F32) or bfloat16
+ *         (RABIT_OUT_BF16), written entirely.
+ * Arithmetic: h_p*x is formed exactly and held as a fixed-point integer per
+ * (batch row, path), scaled by a power of two so that the largest |h_p*x|
+ * maps into [2^29, 2^30) (per-element error <= 2^-30 of that largest value);
+ * the signed sums are exact integers; the final combination is done in
+ * float64 and rounded once.
+ * Result is bitwise repeatable (no order-dependent arithmetic).
+ */
+int rabit_gemv(const rabit_layer *layer, const uint16_t *x, int32_t batch,
+               void *y, int32_t y_dtype, void *workspace, size_t workspace_bytes,
+               void *stream);
+
+/*
+ * The two halves of rabit_gemv, for callers that time or schedule them apart.
+ * rabit_gemv_prepare forms the activation operand of every path (u_p = h_p ⊙
+ * x in fixed point, its per-row shift and Σ u) in the workspace and clears
+ * the split-K state; rabit_gemv_run streams the planes and writes y. A run
+ * consumes the workspace of the last prepare for the same layer and batch;
+ * rabit_gemv is prepare followed by run. Errors as rabit_gemv.
+ */
+int rabit_gemv_prepare(const rabit_layer *layer, const uint16_t *x, int32_t batch,
+                       void *workspace, size_t workspace_bytes, void *stream);
+int rabit_gemv_run(const rabit_layer *layer, int32_t batch, void *y, int32_t y_dtype,
+                   void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Prefill GEMM: Y[m][i] = Σ_p g_p[i] * Σ_j B_p[i][j] * h_p[j] * X[m][j].
+ *
+ * X       device bfloat16 bit patterns [M][in], row-major.
+ * M       1 .. RABIT_MAX_GEMM_M.
+ * Y       device [M][out] float32 or bfloat16.
+ * Arithmetic: MFMA fp16 x fp16 -> fp32. The B tile holds ±h_p (exact in
+ * fp16); each X row is scaled by a power of two so that its largest |x| is
+ * in [2^14, 2^15), rounded to fp16, and unscaled in the epilogue, where g_p
+ * is applied in fp32.
+ */
+int rabit_gemm(const rabit_layer *layer, const uint16_t *X, int32_t m,
+               void *Y, int32_t y_dtype, void *workspace, size_t workspace_bytes,
+               void *stream);
+
+/*
+ * Decoder configuration for rabit_decode_step (a Llama-style block; the pages
+ * time Llama2 decoding, Table 7, without defining the block).
+ */
+typedef struct {
+  int32_t hidden;       /* model width */
+  int32_t ffn;          /* MLP width */
+  int32_t n_heads;      /* query heads */
+  int32_t n_kv_heads;   /* key/value heads (GQA) */
+  int32_t head_dim;
+  int32_t n_layers;
+  float rms_eps;        /* RMSNorm epsilon (unit weight) */
+  int32_t mlp_only;     /* 1: blocks have no attention (q/k/v/o unused) */
+} rabit_decoder_cfg;
+
+size_t rabit_decode_workspace_bytes(const rabit_decoder_cfg *cfg, int32_t batch);
+
+/*
+ * One decode step through cfg->n_layers blocks, one token per batch row.
+ *
+ * layers   host array [n_layers * 7] of layers in the order
+ *          q, k, v, o, gate, up, down (q/k/v/o ignored when mlp_only).
+ * x        device bf16 [batch][hidden] input hidden state.
+ * out      device bf16 [batch][hidden] output hidden state (may equal x).
+ * Per block (bf16 at each arrow that stores an activation):
+ *   n = rmsnorm(x) -> [q,k,v = W n] -> a = attention over a one-token
+ *   context (each head returns its KV group's v) -> x = x + W_o a ->
+ *   n = rmsnorm(x) -> z = silu(W_gate n) * (W_up n) -> x = x + W_down z.
+ * batch    1 .. RABIT_MAX_GEMV_BATCH uses the GEMV; larger batches the GEMM.
+ * Errors: as the ops above; RABIT_ESHAPE if a layer's shape does not match
+ * cfg (q, o: hidden x hidden; k, v: n_kv_heads*head_dim x hidden; gate, up:
+ * ffn x hidden; down: hidden x ffn).
+ */
+int rabit_decode_step(const rabit_decoder_cfg *cfg, const rabit_layer *layers,
+                      const uint16_t *x, int32_t batch, uint16_t *out,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+const char *rabit_status_string(int status);
+int32_t rabit_layout_version(void);
+
+/*
+ * Test hook: the library's float64 -> fp16 (bf16 = 0) or -> bfloat16
+ * (bf16 = 1) round-to-nearest-even, as used for the scales and outputs.
+ * in: device float64 [n]; out: device uint16 [n].
+ */
+int rabit_test_f64_to_16(const double *in, uint16_t *out, int32_t n, int32_t bf16, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RABIT_H_ */

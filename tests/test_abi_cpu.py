@@ -1,0 +1,128 @@
+"""Boundary tests that need no GPU: the library loads, exports every symbol
+include/rabit.h declares, sizes follow the documented closed forms, and every
+argument error is returned before anything is enqueued (the pointers used
+below are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from bit_residual_binarized_amd import rabit
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(rabit.LIB_PATH):
+        from bit_residual_binarized_amd.build import build
+        build()
+    return rabit.load()
+
+
+def header_symbols():
+    text = open(os.path.join(ROOT, "include", "rabit.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rabit_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_header_symbol(lib):
+    syms = header_symbols()
+    assert len(syms) >= 12
+    for s in syms:
+        assert hasattr(lib, s), s
+    assert sorted(rabit.EXPORTS) == syms
+
+
+def test_sizes(lib):
+    assert lib.rabit_planes_bytes(4096, 4096, 2) == 2 * 4096 * 4096 // 8
+    assert lib.rabit_planes_bytes(11008, 4096, 2) == 2 * 11008 * 4096 // 8
+    assert lib.rabit_planes_bytes(1, 1, 2) == 2048
+    assert lib.rabit_planes_bytes(65, 129, 2) == 2 * 2 * 64 * 2 * 16
+    assert lib.rabit_planes_bytes(0, 4, 2) == 0
+    assert lib.rabit_planes_bytes(4, 4, 3) == 0
+    assert lib.rabit_planes_bytes(1 << 20, 4, 2) == 0
+    assert lib.rabit_pack_workspace_bytes(4096, 4096) > 0
+    assert lib.rabit_gemv_workspace_bytes(4096, 4096, 1) > 0
+    assert lib.rabit_gemv_workspace_bytes(4096, 4096, 17) == 0
+    assert lib.rabit_gemm_workspace_bytes(4096, 4096, 512) > 0
+    assert lib.rabit_layout_version() == 1
+    for code in range(-6, 1):
+        assert rabit.status_string(code) != "unknown status"
+
+
+FAKE = 1 << 40  # aligned, never dereferenced
+
+
+def fake_layer(out=256, inp=512, version=1, paths=2, planes=FAKE, g=FAKE + (1 << 30), h=FAKE + (2 << 30)):
+    return rabit.RabitLayerC(version, out, inp, paths, planes, g, h)
+
+
+def gemv(lib, layer, x=FAKE + (3 << 30), batch=1, y=FAKE + (4 << 30), dtype=0, ws=FAKE + (5 << 30),
+         wsb=1 << 30):
+    return lib.rabit_gemv(ctypes.byref(layer) if layer is not None else None, x, batch, y, dtype, ws,
+                          wsb, None)
+
+
+def test_gemv_argument_errors(lib):
+    L = fake_layer()
+    assert gemv(lib, None) == rabit.RABIT_EINVAL
+    assert gemv(lib, fake_layer(version=2)) == rabit.RABIT_EINVAL
+    assert gemv(lib, fake_layer(paths=3)) == rabit.RABIT_EUNSUPPORTED
+    assert gemv(lib, fake_layer(out=0)) == rabit.RABIT_ESHAPE
+    assert gemv(lib, fake_layer(inp=1 << 20)) == rabit.RABIT_ESHAPE
+    assert gemv(lib, fake_layer(planes=0)) == rabit.RABIT_EINVAL
+    assert gemv(lib, fake_layer(g=FAKE + 8 + (1 << 30))) == rabit.RABIT_EALIGN
+    assert gemv(lib, fake_layer(h=FAKE)) == rabit.RABIT_EINVAL        # h aliases planes
+    assert gemv(lib, L, x=0) == rabit.RABIT_EINVAL
+    assert gemv(lib, L, x=FAKE + 2 + (3 << 30)) == rabit.RABIT_EALIGN
+    assert gemv(lib, L, batch=0) == rabit.RABIT_ESHAPE
+    assert gemv(lib, L, batch=17) == rabit.RABIT_ESHAPE
+    assert gemv(lib, L, dtype=7) == rabit.RABIT_EINVAL
+    assert gemv(lib, L, y=FAKE + (3 << 30)) == rabit.RABIT_EINVAL     # y aliases x
+    assert gemv(lib, L, ws=0) == rabit.RABIT_EWORKSPACE
+    assert gemv(lib, L, wsb=16) == rabit.RABIT_EWORKSPACE
+    assert gemv(lib, L, ws=FAKE + 4 + (5 << 30)) == rabit.RABIT_EALIGN
+
+
+def test_pack_argument_errors(lib):
+    L = fake_layer()
+    w = FAKE + (6 << 30)
+    pk = lambda w=w, mode=1, layer=L, ws=FAKE + (5 << 30), wsb=1 << 30: lib.rabit_pack(
+        w, mode, ctypes.byref(layer), ws, wsb, None)
+    assert pk(w=0) == rabit.RABIT_EINVAL
+    assert pk(mode=5) == rabit.RABIT_EINVAL
+    assert pk(w=w + 4) == rabit.RABIT_EALIGN
+    assert pk(w=FAKE) == rabit.RABIT_EINVAL          # W aliases the planes it would write
+    assert pk(ws=0) == rabit.RABIT_EWORKSPACE
+    assert pk(wsb=8) == rabit.RABIT_EWORKSPACE
+    assert pk(layer=fake_layer(paths=1)) == rabit.RABIT_EUNSUPPORTED
+
+
+def test_gemm_and_unpack_errors(lib):
+    L = fake_layer()
+    X, Y, ws = FAKE + (3 << 30), FAKE + (4 << 30), FAKE + (5 << 30)
+    assert lib.rabit_gemm(ctypes.byref(L), X, 0, Y, 0, ws, 1 << 30, None) == rabit.RABIT_ESHAPE
+    assert lib.rabit_gemm(ctypes.byref(L), X, 8, X, 0, ws, 1 << 30, None) == rabit.RABIT_EINVAL
+    assert lib.rabit_gemm(ctypes.byref(L), X, 8, Y, 0, ws, 16, None) == rabit.RABIT_EWORKSPACE
+    assert lib.rabit_unpack(ctypes.byref(L), 0, None) == rabit.RABIT_EINVAL
+    assert lib.rabit_unpack(ctypes.byref(fake_layer(version=0)), Y, None) == rabit.RABIT_EINVAL
+
+
+def test_decode_cfg_errors(lib):
+    cfg = rabit.DecoderCfg(hidden=64, ffn=96, n_heads=4, n_kv_heads=3, head_dim=16)
+    cc = cfg.c()
+    assert lib.rabit_decode_workspace_bytes(ctypes.byref(cc), 1) == 0   # 4 % 3 != 0
+    cfg = rabit.DecoderCfg(hidden=64, ffn=96, n_heads=4, n_kv_heads=2, head_dim=16)
+    cc = cfg.c()
+    assert lib.rabit_decode_workspace_bytes(ctypes.byref(cc), 1) > 0
+    arr = (rabit.RabitLayerC * 7)()
+    for i in range(7):
+        arr[i] = fake_layer(out=64, inp=64, planes=FAKE + i * (1 << 32), g=FAKE + i * (1 << 32) + (1 << 30),
+                            h=FAKE + i * (1 << 32) + (2 << 30))
+    x, out, ws = FAKE + (100 << 32), FAKE + (101 << 32), FAKE + (102 << 32)
+    # k has 64 rows but n_kv_heads * head_dim = 32 -> shape error before any launch
+    assert lib.rabit_decode_step(ctypes.byref(cc), arr, x, 1, out, ws, 1 << 40, None) == rabit.RABIT_ESHAPE
+    mlp = rabit.DecoderCfg(hidden=64, ffn=96, mlp_only=True).c()
+    assert lib.rabit_decode_step(ctypes.byref(mlp), arr, x, 1, out, ws, 1 << 40, None) == rabit.RABIT_ESHAPE

@@ -1,0 +1,291 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bars: packed words and fp16 scales bit-exact;
+GEMV/GEMM/decode outputs within a normwise relative error of 2e-3 per batch
+row (max_i |y - ŷ| / max_i |ŷ|); unit-vector probes bit-exact.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth.inputs import (weight_f32, act_bf16, bf16_values, random_f16_scales, seed_w, seed_x)
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def pack_gpu(rabit, w_cpu, mode=None, g=None, h=None):
+    mode = rabit.RABIT_SCALES_MEANABS if mode is None else mode
+    out, inp = w_cpu.shape
+    layer = rabit.PackedLayer.empty(out, inp)
+    if g is not None:
+        gg = torch.zeros(2, out, dtype=torch.float16)
+        hh = torch.zeros(2, inp, dtype=torch.float16)
+        gg[0] = torch.from_numpy(g)
+        hh[0] = torch.from_numpy(h)
+        layer.g.copy_(gg.view(torch.int16))
+        layer.h.copy_(hh.view(torch.int16))
+    rabit.pack(w_cpu.cuda(), layer, mode)
+    torch.cuda.synchronize()
+    return layer
+
+
+def check_pack(rabit, layer, d, out, inp, check_scales=True):
+    words = rabit.unpack(layer).cpu().numpy().view(np.uint32)
+    w1, w2 = oracle.pack_words(d.s1), oracle.pack_words(d.s2)
+    assert np.array_equal(words[0], w1), "path-1 words differ"
+    assert np.array_equal(words[1], w2), "path-2 words differ"
+    raw = layer.planes.cpu().numpy().view(np.uint32)
+    assert np.array_equal(raw, oracle.device_planes(w1, w2, out, inp)), "device layout differs"
+    if check_scales:
+        g = layer.g.cpu().numpy().view(np.float16)
+        h = layer.h.cpu().numpy().view(np.float16)
+        for name, got, ref in (("g1", g[0], d.g1), ("h1", h[0], d.h1), ("g2", g[1], d.g2), ("h2", h[1], d.h2)):
+            bad = np.flatnonzero(got.view(np.uint16) != ref.view(np.uint16))
+            assert bad.size == 0, f"{name}: {bad.size} fp16 scales differ, first at {bad[:5]}"
+
+
+PACK_SHAPES = [(4, 8), (64, 256), (100, 300), (130, 1000), (1, 1), (65, 129), (256, 4096),
+               (1024, 4096), (4096, 4096)]
+
+
+@pytest.mark.parametrize("shape", PACK_SHAPES)
+def test_pack_meanabs_bit_exact(gpu_lib, shape):
+    out, inp = shape
+    say("pack meanabs", shape)
+    w = weight_f32(out, inp, 1000 + out + inp)
+    layer = pack_gpu(gpu_lib, w)
+    d = oracle.derive(w.numpy())
+    check_pack(gpu_lib, layer, d, out, inp)
+
+
+def test_pack_given_scales_bit_exact(gpu_lib):
+    out, inp = 300, 700
+    say("pack given", out, inp)
+    w = weight_f32(out, inp, 77)
+    g, h = random_f16_scales(out, 1), random_f16_scales(inp, 2)
+    layer = pack_gpu(gpu_lib, w, gpu_lib.RABIT_SCALES_GIVEN, g, h)
+    d = oracle.derive(w.numpy(), mode="given", g1=g, h1=h)
+    check_pack(gpu_lib, layer, d, out, inp, check_scales=False)
+
+
+def test_pack_edge_values(gpu_lib):
+    # zeros, negative zeros, engineered |W| == g1 h1 ties, a zero row/column,
+    # float32 subnormals
+    out, inp = 64, 256
+    say("pack edge values")
+    w = weight_f32(out, inp, 88).numpy().copy()
+    w[3] = 0.0
+    w[:, 5] = -0.0
+    w[7, :20] = np.float32(1e-40)
+    w[8, :20] = -np.float32(3e-42)
+    wt = torch.from_numpy(w)
+    layer = pack_gpu(gpu_lib, wt)
+    d = oracle.derive(w)
+    check_pack(gpu_lib, layer, d, out, inp)
+    # ties: W = ±g1 h1 exactly, with given scales
+    g = np.full(out, 0.5, np.float16)
+    h = np.full(inp, 0.25, np.float16)
+    w2 = np.where(np.arange(inp)[None, :] % 2 == 0, 0.125, -0.125).astype(np.float32) * np.ones((out, 1), np.float32)
+    layer = pack_gpu(gpu_lib, torch.from_numpy(w2), gpu_lib.RABIT_SCALES_GIVEN, g, h)
+    d = oracle.derive(w2, mode="given", g1=g, h1=h)
+    check_pack(gpu_lib, layer, d, out, inp, check_scales=False)
+
+
+def test_pack_repeatable(gpu_lib):
+    say("pack repeatable")
+    w = weight_f32(512, 1024, 99)
+    a = pack_gpu(gpu_lib, w)
+    b = pack_gpu(gpu_lib, w)
+    assert torch.equal(a.planes, b.planes) and torch.equal(a.g, b.g) and torch.equal(a.h, b.h)
+
+
+def test_f64_to_f16_and_bf16_rounding(gpu_lib):
+    say("f64 -> fp16/bf16 rounding")
+    allh = np.arange(0, 0x7C00, dtype=np.uint16).view(np.float16).astype(np.float64)
+    mids = (allh[:-1] + allh[1:]) / 2.0
+    rng = np.random.default_rng(5)
+    extra = np.concatenate([rng.standard_normal(100000) * np.exp2(rng.integers(-30, 18, 100000)),
+                            [0.0, -0.0, 65504.0, 65519.99, 65520.0, 1e6, 2.0 ** -25, 2.0 ** -24]])
+    v = np.concatenate([mids, np.nextafter(mids, np.inf), np.nextafter(mids, -np.inf), extra])
+    v = np.concatenate([v, -v])
+    got = gpu_lib.test_f64_to_16(torch.from_numpy(v).cuda(), bf16=False).cpu().numpy().view(np.uint16)
+    ref = oracle.f16_rne(v).view(np.uint16)
+    assert np.array_equal(got, ref)
+    vb = np.concatenate([rng.standard_normal(200000) * np.exp2(rng.integers(-140, 120, 200000)),
+                         [0.0, 1.0 + 2.0 ** -8, 1.0 + 2.0 ** -8 + 2.0 ** -30, 3.4e38, 3.4e39]])
+    gotb = gpu_lib.test_f64_to_16(torch.from_numpy(vb).cuda(), bf16=True).cpu().numpy().view(np.uint16)
+    refb = oracle.bf16_rne(vb).astype(np.float32).view(np.uint32) >> 16
+    assert np.array_equal(gotb, refb.astype(np.uint16))
+
+
+GEMV_SHAPES = [(4, 8), (64, 256), (100, 300), (130, 1000), (65, 129), (1, 4096), (4096, 4096),
+               (11008, 4096), (4096, 11008), (1024, 4096), (512, 14336)]
+
+
+@pytest.mark.parametrize("shape", GEMV_SHAPES)
+def test_gemv_batch1(gpu_lib, shape):
+    out, inp = shape
+    say("gemv b=1", shape)
+    w = weight_f32(out, inp, 2000 + out + inp)
+    layer = pack_gpu(gpu_lib, w)
+    d = oracle.derive(w.numpy())
+    x = act_bf16(1, inp, 3000 + inp)
+    y = gpu_lib.gemv(layer, x.cuda()).cpu().numpy().astype(np.float64)
+    ref = oracle.gemv(d, bf16_values(x))
+    err = oracle.normwise_rel_err(y, ref)
+    say("  normwise err", err)
+    assert err < TOL
+    y2 = gpu_lib.gemv(layer, x.cuda()).cpu().numpy()
+    assert np.array_equal(y.astype(np.float32), y2), "not repeatable"
+
+
+@pytest.mark.parametrize("batch", [2, 3, 4, 8, 16])
+def test_gemv_batches(gpu_lib, batch):
+    out, inp = 1024, 4096
+    say("gemv batch", batch)
+    w = weight_f32(out, inp, 4000 + batch)
+    layer = pack_gpu(gpu_lib, w)
+    d = oracle.derive(w.numpy())
+    x = act_bf16(batch, inp, seed_x(3, batch))
+    y = gpu_lib.gemv(layer, x.cuda()).cpu().numpy().astype(np.float64)
+    ref = oracle.gemv(d, bf16_values(x))
+    err = oracle.normwise_rel_err(y, ref)
+    say("  normwise err", err)
+    assert err < TOL
+
+
+def test_gemv_unit_vector_probe_bit_exact(gpu_lib):
+    out, inp = 256, 640
+    say("gemv unit probes")
+    w = weight_f32(out, inp, 5)
+    layer = pack_gpu(gpu_lib, w)
+    d = oracle.derive(w.numpy())
+    we = oracle.weff(d)
+    for j in (0, 1, 127, 128, 333, 639):
+        x = torch.zeros(1, inp, dtype=torch.bfloat16)
+        x[0, j] = 1.0
+        y = gpu_lib.gemv(layer, x.cuda()).cpu().numpy()
+        assert np.array_equal(y[0], we[:, j].astype(np.float32)), j
+
+
+def test_gemv_bf16_output_and_outlier_input(gpu_lib):
+    out, inp = 512, 2048
+    say("gemv bf16 out + outliers")
+    w = weight_f32(out, inp, 6)
+    layer = pack_gpu(gpu_lib, w)
+    d = oracle.derive(w.numpy())
+    x = act_bf16(2, inp, 7)
+    x[0, 17] = 3000.0   # a massive activation
+    x[1, 100:110] = 1e-30
+    ref = oracle.gemv(d, bf16_values(x))
+    yf = gpu_lib.gemv(layer, x.cuda()).cpu().numpy().astype(np.float64)
+    assert oracle.normwise_rel_err(yf, ref) < 1e-6
+    yb = gpu_lib.gemv(layer, x.cuda(), y_dtype=gpu_lib.RABIT_OUT_BF16).cpu().to(torch.float32).numpy()
+    assert oracle.normwise_rel_err(yb.astype(np.float64), ref) < 2 ** -8
+
+
+def test_gemv_prepare_run_equals_gemv(gpu_lib):
+    out, inp = 1000, 3000
+    say("gemv prepare/run")
+    layer = pack_gpu(gpu_lib, weight_f32(out, inp, 8))
+    x = act_bf16(1, inp, 9).cuda()
+    ws = gpu_lib.gemv_workspace(layer, 1)
+    y = torch.empty(1, out, device="cuda")
+    gpu_lib.gemv_prepare(layer, x, ws)
+    gpu_lib.gemv_run(layer, 1, y, ws)
+    assert torch.equal(y, gpu_lib.gemv(layer, x))
+
+
+GEMM_CASES = [(64, 256, 1), (130, 1000, 37), (256, 4096, 512), (1024, 4096, 130), (300, 1100, 257)]
+
+
+@pytest.mark.parametrize("case", GEMM_CASES)
+def test_gemm(gpu_lib, case):
+    out, inp, m = case
+    say("gemm", case)
+    w = weight_f32(out, inp, 6000 + m)
+    layer = pack_gpu(gpu_lib, w)
+    d = oracle.derive(w.numpy())
+    xm = act_bf16(m, inp, 7000 + m)
+    y = gpu_lib.gemm(layer, xm.cuda()).cpu().numpy().astype(np.float64)
+    ref = oracle.gemm(d, bf16_values(xm))
+    err = oracle.normwise_rel_err(y, ref)
+    say("  normwise err", err)
+    assert err < TOL
+
+
+def test_gemm_rows_match_gemv(gpu_lib):
+    out, inp, m = 512, 2048, 40
+    say("gemm vs gemv rows")
+    layer = pack_gpu(gpu_lib, weight_f32(out, inp, 10))
+    xm = act_bf16(m, inp, 11).cuda()
+    ym = gpu_lib.gemm(layer, xm).cpu().numpy().astype(np.float64)
+    for r in (0, 17, 39):
+        yv = gpu_lib.gemv(layer, xm[r:r + 1].contiguous()).cpu().numpy().astype(np.float64)
+        assert oracle.normwise_rel_err(ym[r:r + 1], yv) < 1e-5
+
+
+def _decode_case(gpu_lib, cfg, mlp_only, batch, seed):
+    H, F = cfg.hidden, cfg.ffn
+    kv = cfg.n_kv_heads * cfg.head_dim
+    shapes = {"q": (H, H), "k": (kv, H), "v": (kv, H), "o": (H, H), "gate": (F, H), "up": (F, H), "down": (H, F)}
+    names = ["gate", "up", "down"] if mlp_only else list(shapes)
+    layers, dmats = [], []
+    for li in range(cfg.n_layers):
+        ld, dd = {}, {}
+        for n in names:
+            w = weight_f32(*shapes[n], seed + 10 * li + len(n))
+            ld[n] = pack_gpu(gpu_lib, w)
+            dd[n] = oracle.derive(w.numpy())
+        layers.append(ld)
+        dmats.append(dd)
+    x = act_bf16(batch, H, seed + 99)
+    y = gpu_lib.decode_step(cfg, layers, x.cuda()).cpu().to(torch.float32).numpy().astype(np.float64)
+    ref = bf16_values(x)
+    ocfg = {"n_heads": cfg.n_heads, "n_kv_heads": cfg.n_kv_heads, "head_dim": cfg.head_dim, "rms_eps": cfg.rms_eps}
+    for dd in dmats:
+        ref = oracle.decode_layer(ref, dd, ocfg)
+    return y, ref
+
+
+def bf16_close(y, ref, tol=TOL):
+    """|y - ŷ| <= tol * max|ŷ| (per batch row) + one bf16 ulp of ŷ, elementwise:
+    both sides round nearly equal values to bf16, so a rounding boundary can
+    fall between them (one ulp, up to 2^-8 relative)."""
+    y = np.atleast_2d(y)
+    ref = np.atleast_2d(ref)
+    a = np.abs(ref)
+    ulp = np.exp2(np.floor(np.log2(np.where(a > 0, a, 1.0))) - 7)
+    allow = tol * a.max(axis=1, keepdims=True) + ulp
+    bad = np.abs(y - ref) > allow
+    return not bad.any(), int(bad.sum())
+
+
+def test_decode_mlp_block(gpu_lib):
+    say("decode mlp block")
+    cfg = gpu_lib.DecoderCfg(hidden=1024, ffn=2752, n_layers=2, mlp_only=True)
+    y, ref = _decode_case(gpu_lib, cfg, True, 1, 500)
+    err = oracle.normwise_rel_err(y, ref)
+    ok, nbad = bf16_close(y, ref)
+    say("  normwise err", err, "elements outside bound", nbad)
+    assert ok
+
+
+@pytest.mark.parametrize("batch", [1, 4, 20])
+def test_decode_attention_block(gpu_lib, batch):
+    say("decode attention block batch", batch)
+    cfg = gpu_lib.DecoderCfg(hidden=512, ffn=1376, n_heads=8, n_kv_heads=2, head_dim=64, n_layers=2)
+    y, ref = _decode_case(gpu_lib, cfg, False, batch, 600 + batch)
+    err = oracle.normwise_rel_err(y, ref)
+    ok, nbad = bf16_close(y, ref)
+    say("  normwise err", err, "elements outside bound", nbad)
+    assert ok
