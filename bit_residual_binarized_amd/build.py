@@ -26,6 +26,9 @@ FLAGS = [
     "-fno-fast-math",
     # packed fp32 ALU ops are not used on this target
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs: with AGPRs the allocator rotated the GEMV's
+    # 64 loop-carried accumulators through copies on every iteration
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function", "-Wno-unused-result",
 ]
 
