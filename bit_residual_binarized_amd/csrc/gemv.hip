@@ -2,26 +2,35 @@
 //
 // RaBiT paper App. E.1 describes a CUDA GEMV that expands sign bits with
 // shifts/XOR into fp16 FMAs and notes that the limit moves toward register
-// throughput. On gfx950 the sign expansion is done by the int8 matrix cores:
+// throughput. On gfx950 the ±1 contraction runs on the matrix cores, with the
+// plane bits used directly as fp4 operands:
 //
 //  * Σ_j s_j u_j = Σ_j u_j − 2 Σ_{bit_j = 1} u_j with s_j = 1 − 2 bit_j and
 //    u = h_p ⊙ x (paper §5.4: additions and element-wise scaling).
-//  * u is formed exactly (float64) and held as a fixed-point integer
-//    u_fx = rint(u * 2^sh), with one exponent per (batch row, path, K range)
-//    chosen so that the range's max |u_fx| lies in [2^29, 2^30); u_fx is
-//    split into four signed bytes d_0..d_3, u_fx = Σ_i 256^i d_i.
-//  * For a stored word w (32 columns of one row) and a slice t in 0..7,
-//    (w & (0x01010101 << t)) is a dword of four int8 values bit * 2^t
-//    (t = 7: bit * -128) for the columns 8r + t, r = 0..3. One v_and per four
-//    weights feeds V_MFMA_I32_4X4X4_16B_I8 with the A operand broadcast from
-//    one of its 16 blocks: lane = output row, A block = the 4 digit rows of
-//    the 4 columns of one (word, slice) pair. Per lane and slice the result
-//    is the 4 digit sums of that lane's row: 8 int32 accumulators x 4 digits.
-//  * Per K range the sums are exact integers; the range result
-//    g_1 S_1 + g_2 S_2 is formed in float64. Ranges are reduced in a fixed
-//    order (4 waves of a workgroup through LDS, then workgroups by a small
-//    kernel), so the output is bitwise repeatable. No atomics, no fences.
+//  * The input columns are cut into K ranges of 512 (one "chunk"). Per
+//    (batch row, path, range), u is formed exactly (float64) and held as a
+//    fixed-point integer v = rint(u · 2^sh), sh chosen so that the range's
+//    largest |u| maps into [2^18, 2^19); v + 2^20 is written in 7 base-8
+//    digits 0..7.
+//  * A stored word w (32 columns of one row, bit t of nibble e = column
+//    4e + t) gives four fp4 slices: w & 0x1..1 (value 0.5 per set bit),
+//    w & 0x2..2 (1.0), (w >> 1) & 0x2..2 (1.0), (w >> 3) & 0x1..1 (0.5).
+//  * V_MFMA_SCALE_F32_16X16X128_F8F6F4 (unit scales) multiplies one slice
+//    (16 rows x 128 columns, fp4) by an fp6 e2m3 operand whose rows are the
+//    digits, coded so that every product is digit/8 (fp6 codes d or 2d are
+//    exact and linear below 16). One extra row of ones yields the set-bit
+//    count. Every product and fp32 partial sum is an exact multiple of 1/8
+//    below 2^11, so Σ bit·v is recovered exactly as an integer.
+//  * Each workgroup builds the digit operand of its own range in LDS from x
+//    and h (no separate activation pass), then its 4 waves stream 64-row
+//    groups of planes through the matrix cores (one 8 KiB slab per wave and
+//    row group, prefetched one row group ahead).
+//  * Per range, g_1 S_1 + g_2 S_2 is formed in float64 from exact integers.
+//    With one range it is the output; otherwise the ranges' partials are
+//    summed in a fixed order by a small kernel, so the output is bitwise
+//    repeatable. No atomics, no fences.
 #include <algorithm>
+#include <type_traits>
 
 #include "rabit_internal.h"
 
@@ -29,80 +38,63 @@ namespace rabit {
 
 namespace {
 
-constexpr int kWaves = 4;    // waves per workgroup; they share a row group and split K
-constexpr int kMaxRing = 3;  // column groups (both paths) in flight per wave
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 
-// K split of one GEMV: S = kWaves * SG ranges of kg_per column groups (a
-// multiple of the ring depth, so only the last range is ragged).
-struct Plan {
-  int RG, KG, SG, S, kg_per, ring;
+constexpr int kChunk = 512;                    // columns per K range
+constexpr int kImgDw = 6;                      // dwords per lane of one fp6 image (32 x 6 bits)
+constexpr int kImgDwords = 64 * kImgDw;        // one (path, slice) image
+constexpr int kPairDwords = 8 * kImgDwords;    // 2 paths x 4 slices, one batch pair (12 KiB)
+constexpr int kFxTop = 18;                     // max |v| of a range in [2^18, 2^19]
+constexpr int kOff = 1 << 20;                  // v + kOff in [0, 2^21): 7 digits of base 8
+
+// One matrix of a launch. All segments of a launch share the input x (and so
+// in_features); their row blocks are numbered consecutively.
+struct Seg {
+  const uint4* planes;
+  const uint16_t* g;
+  const uint16_t* h;
+  void* y;       // output [batch][out] (direct mode)
+  double* part;  // partials [batch][S][RG*64] (split mode)
+  int out, RG, rb0;
 };
 
-__host__ inline Plan make_plan(int out, int in) {
-  Plan p;
-  p.RG = row_groups(out);
-  p.KG = col_groups(in);
-  const int target_waves = 2048;
-  const int max_sg = std::max(1, (p.KG + kWaves - 1) / kWaves);
-  p.SG = std::max(1, std::min(max_sg, (target_waves + kWaves * p.RG - 1) / (kWaves * p.RG)));
-  p.S = kWaves * p.SG;
-  const int kg_per = (p.KG + p.S - 1) / p.S;
-  p.ring = std::min(kMaxRing, kg_per);
-  p.kg_per = ((kg_per + p.ring - 1) / p.ring) * p.ring;
-  return p;
-}
+constexpr int kMaxSeg = 3;
 
-// Workspace (all offsets 256-byte aligned):
-//   abuf   uint32 [batch][KG+1][64 lanes][2 paths][2 vgprs] A operand images;
-//                 slot KG is all zero (read by surplus ring slots)
-//   rshift int32  [batch][2][S]                             per-range exponent
-//   rusum  int64  [batch][2][S]                             per-range Σ u_fx
-//   part   double [batch][SG][RG*64]                        per-workgroup partials
-struct GemvWs {
-  uint32_t* abuf;
-  int* rshift;
-  long long* rusum;
-  double* part;
+struct Args {
+  Seg seg[kMaxSeg];
+  const uint16_t* x;  // bf16 [batch][in]
+  int nseg, in, KG, S, m, batch, y_dtype, direct;
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-__host__ inline size_t ws_layout(const Plan& P, int batch, void* base, GemvWs* w) {
-  const size_t sz[4] = {align256((size_t)batch * (P.KG + 1) * 64 * 4 * 4),
-                        align256((size_t)batch * 2 * P.S * sizeof(int)),
-                        align256((size_t)batch * 2 * P.S * sizeof(long long)),
-                        align256((size_t)batch * P.SG * P.RG * 64 * sizeof(double))};
-  char* p = (char*)base;
-  if (w) {
-    w->abuf = (uint32_t*)p;
-    w->rshift = (int*)(p + sz[0]);
-    w->rusum = (long long*)(p + sz[0] + sz[1]);
-    w->part = (double*)(p + sz[0] + sz[1] + sz[2]);
-  }
-  return sz[0] + sz[1] + sz[2] + sz[3];
+struct Plan {
+  int KG, S, m, NBP;  // NBP: batch pairs per workgroup
+  int RB[kMaxSeg];    // row blocks per segment (4 m row groups each)
+};
+
+__host__ inline int nbp_for(int batch) {
+  const int pairs = (batch + 1) / 2;
+  return pairs <= 1 ? 1 : pairs <= 2 ? 2 : 4;
 }
 
-__device__ __forceinline__ double u_exact(const uint16_t* __restrict__ h,
-                                          const uint16_t* __restrict__ x, int j) {
-  return (double)f16_bits_to_f32(h[j]) * (double)bf16_bits_to_f32(x[j]);
+__host__ inline Plan make_plan(const int* outs, int nseg, int in, int batch) {
+  Plan P;
+  P.KG = col_groups(in);
+  P.S = (in + kChunk - 1) / kChunk;
+  P.NBP = nbp_for(batch);
+  int quads = 0;
+  for (int s = 0; s < nseg; ++s) quads += (row_groups(outs[s]) + 3) / 4;
+  // rows per workgroup: enough workgroups to fill the chip a few times over,
+  // more row groups per workgroup (amortising its digit build) beyond that
+  P.m = std::max(1, std::min(8, quads * P.S / 512));
+  for (int s = 0; s < nseg; ++s) P.RB[s] = (row_groups(outs[s]) + 4 * P.m - 1) / (4 * P.m);
+  return P;
 }
 
-__device__ __forceinline__ int ufx_at(const uint16_t* __restrict__ h,
-                                      const uint16_t* __restrict__ x, int in, int j, int sh) {
-  if (j >= in) return 0;
-  return (int)rint(ldexp(u_exact(h, x, j), sh));
-}
-
-// digit i (signed byte) of the balanced base-256 expansion of v
-__device__ __forceinline__ uint32_t digit_byte(int v, int i) {
-  int d = 0;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    d = (int)(int8_t)(v & 0xFF);
-    if (k == i) break;
-    v = (v - d) >> 8;
-  }
-  return (uint32_t)(uint8_t)(int8_t)d;
+__host__ inline size_t part_bytes(int out, int S, int batch) {
+  return align256((size_t)batch * S * row_groups(out) * 64 * sizeof(double));
 }
 
 __device__ __forceinline__ double wave_max(double v) {
@@ -110,228 +102,417 @@ __device__ __forceinline__ double wave_max(double v) {
   for (int s = 32; s >= 1; s >>= 1) v = fmax(v, __shfl_xor(v, s, 64));
   return v;
 }
-__device__ __forceinline__ long long wave_sum(long long v) {
+__device__ __forceinline__ int wave_sum(int v) {
 #pragma unroll
   for (int s = 32; s >= 1; s >>= 1) v += __shfl_xor(v, s, 64);
   return v;
 }
 
-// One workgroup per (K range r, path p, batch row b): exponent, Σ u_fx and
-// the A-operand images of the range's column groups.
-__global__ __launch_bounds__(256) void k_gemv_prep(const uint16_t* __restrict__ x,
-                                                   const uint16_t* __restrict__ h, int in, Plan P,
-                                                   GemvWs ws) {
-  const int r = blockIdx.x, p = blockIdx.y, b = blockIdx.z;
-  const uint16_t* xb = x + (size_t)b * in;
-  const uint16_t* hp = h + (size_t)p * in;
-  const int kgA = min(P.KG, r * P.kg_per), kgB = min(P.KG, kgA + P.kg_per);
-  const int c0 = kgA * 128, c1 = min(in, kgB * 128);
-  __shared__ double smax[4];
-  __shared__ long long ssum[4];
-
-  double m = 0.0;
-  for (int j = c0 + (int)threadIdx.x; j < c1; j += 256) m = fmax(m, fabs(u_exact(hp, xb, j)));
-  m = wave_max(m);
-  if ((threadIdx.x & 63) == 0) smax[threadIdx.x >> 6] = m;
-  __syncthreads();
-  m = fmax(fmax(smax[0], smax[1]), fmax(smax[2], smax[3]));
-  const int sh = (m > 0.0) ? 29 - ilogb(m) : 0;
-
-  long long su = 0;
-  for (int j = c0 + (int)threadIdx.x; j < c1; j += 256) su += (long long)ufx_at(hp, xb, in, j, sh);
-  su = wave_sum(su);
-  if ((threadIdx.x & 63) == 0) ssum[threadIdx.x >> 6] = su;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    ws.rshift[((size_t)b * 2 + p) * P.S + r] = sh;
-    ws.rusum[((size_t)b * 2 + p) * P.S + r] = ((ssum[0] + ssum[1]) + ssum[2]) + ssum[3];
-  }
-
-  const int ndw = (kgB - kgA) * 128;
-  for (int d = threadIdx.x; d < ndw; d += 256) {
-    const int kg = kgA + (d >> 7), L = (d >> 1) & 63, v = d & 1;
-    const int c = 16 * v + (L >> 2);  // (word, slice) pair of this A image
-    const int q = c >> 3, t = c & 7, i = L & 3;
-    const int base = 128 * kg + 32 * q + t;
-    uint32_t dw = 0;
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr)
-      dw |= digit_byte(ufx_at(hp, xb, in, base + 8 * rr, sh), i) << (8 * rr);
-    ws.abuf[(((size_t)b * (P.KG + 1) + kg) * 64 + L) * 4 + p * 2 + v] = dw;
-  }
-  if (r == 0 && p == 0) ws.abuf[((size_t)b * (P.KG + 1) + P.KG) * 256 + threadIdx.x] = 0;
+// fp4 slice t of four stored words (see the header comment)
+template <int T>
+__device__ __forceinline__ v8i slice4(const uint4& w) {
+  auto f = [](uint32_t v) -> int {
+    if (T == 0) return (int)(v & 0x11111111u);
+    if (T == 1) return (int)(v & 0x22222222u);
+    if (T == 2) return (int)((v >> 1) & 0x22222222u);
+    return (int)((v >> 3) & 0x11111111u);
+  };
+  return (v8i){f(w.x), f(w.y), f(w.z), f(w.w), 0, 0, 0, 0};
 }
 
-// exact integer masked sum of one lane's row from its 8 slice accumulators
-__device__ __forceinline__ long long combine_slices(const v4i (&acc)[8]) {
-  long long m = 0;
+// 6 dwords of 32 fp6 fields, every field = code
+__device__ __forceinline__ void fill_code(uint32_t (&dw)[kImgDw], uint32_t code) {
 #pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    long long xd = 0;
+  for (int d = 0; d < kImgDw; ++d) dw[d] = 0;
 #pragma unroll
-    for (int t = 0; t < 7; ++t) xd += (long long)(acc[t][d] >> t);
-    xd -= (long long)(acc[7][d] >> 7);  // slice 7 carries the factor -128
-    m += xd * (1ll << (8 * d));
-  }
-  return m;
-}
-
-__device__ __forceinline__ void store_y(void* y, int y_dtype, size_t idx, double v) {
-  if (y_dtype == RABIT_OUT_F32)
-    ((float*)y)[idx] = (float)v;
-  else
-    ((uint16_t*)y)[idx] = f64_to_bf16_rne(v);
-}
-
-// 32 MFMAs: one 128-column unit of one path (4 words x 8 slices)
-__device__ __forceinline__ void mfma_unit(v4i (&acc)[8], const uint4& w, const uint2& a) {
-  const uint32_t ws4[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int av = (int)((q < 2) ? a.x : a.y);
-#define RABIT_SLICE(T)                                                                     \
-  {                                                                                        \
-    const int bw = (int)(ws4[q] & (0x01010101u << (T)));                                  \
-    if (q & 1)                                                                             \
-      acc[T] = __builtin_amdgcn_mfma_i32_4x4x4i8(av, bw, acc[T], 4, 8 + (T), 0);         \
-    else                                                                                   \
-      acc[T] = __builtin_amdgcn_mfma_i32_4x4x4i8(av, bw, acc[T], 4, (T), 0);             \
-  }
-    RABIT_SLICE(0) RABIT_SLICE(1) RABIT_SLICE(2) RABIT_SLICE(3)
-    RABIT_SLICE(4) RABIT_SLICE(5) RABIT_SLICE(6) RABIT_SLICE(7)
-#undef RABIT_SLICE
+  for (int x = 0; x < 32; ++x) {
+    const int bit = 6 * x;
+    dw[bit >> 5] |= code << (bit & 31);
+    if ((bit & 31) > 26) dw[(bit >> 5) + 1] |= code >> (32 - (bit & 31));
   }
 }
 
-// Workgroup = 4 waves on one 64-row group, wave w takes K range 4*sg + w.
-// blockIdx.y = batch row. RING column groups (both paths) are in flight per
-// wave. The loop has no data-dependent branch: the trip count is rounded up
-// to a multiple of RING, and surplus groups read their A operand from a zero
-// image (their weights are a clamped re-read), so they add exactly 0.
-template <int RING>
-__global__ __launch_bounds__(256) void k_gemv_main(const uint4* __restrict__ planes,
-                                                   const uint16_t* __restrict__ g, int out,
-                                                   Plan P, GemvWs ws, void* y, int y_dtype) {
-  const int rg = blockIdx.x / P.SG, sg = blockIdx.x - rg * P.SG;
-  const int b = blockIdx.y;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63;
-  const int r = sg * kWaves + w;
-  const int kgA = min(P.KG, r * P.kg_per), kgB = min(P.KG, kgA + P.kg_per);
-  const int nk = __builtin_amdgcn_readfirstlane(kgB - kgA);
-  const int nkr = __builtin_amdgcn_readfirstlane(((nk + RING - 1) / RING) * RING);
-
-  const uint4* __restrict__ wbase = planes + unit_index(rg, kgA, 0, l, P.KG);
-  const uint4* __restrict__ abase = (const uint4*)(ws.abuf + (((size_t)b * (P.KG + 1) + kgA) * 64 + l) * 4);
-  const uint4* __restrict__ azero = (const uint4*)(ws.abuf + (((size_t)b * (P.KG + 1) + P.KG) * 64 + l) * 4);
-
-  v4i acc0[8], acc1[8];
+// digit row: field x = digit `dig` of vals[x], shifted left by SH (code 2d)
+template <int SH>
+__device__ __forceinline__ void deposit_digits(uint32_t (&dw)[kImgDw], const int (&vals)[32],
+                                               int dig) {
 #pragma unroll
-  for (int t = 0; t < 8; ++t) acc0[t] = acc1[t] = (v4i){0, 0, 0, 0};
-  long long M0 = 0, M1 = 0;
-  if (nk > 0) {
-    uint4 w0[RING], w1[RING], av[RING];
+  for (int d = 0; d < kImgDw; ++d) dw[d] = 0;
 #pragma unroll
-    for (int i = 0; i < RING; ++i) {
-      const int k = min(i, nk - 1);
-      av[i] = *((i < nk) ? abase + (size_t)i * 64 : azero);
-      w0[i] = load_nt(wbase + (size_t)k * 128);
-      w1[i] = load_nt(wbase + (size_t)k * 128 + 64);
-      __builtin_amdgcn_sched_barrier(0);
+  for (int x = 0; x < 32; ++x) {
+    const uint32_t f = __builtin_amdgcn_ubfe((uint32_t)vals[x], 3 * dig, 3);
+    const int bit = 6 * x + SH;
+    dw[bit >> 5] |= f << (bit & 31);
+    if ((bit & 31) > 29) dw[(bit >> 5) + 1] |= f >> (32 - (bit & 31));
+  }
+}
+
+// Workgroup: 4 waves; segment/row block rbg, K range r (512 columns), batch
+// pairs [NBP*blockIdx.y, NBP*blockIdx.y + NBP). Round k: wave w takes row
+// group 4 m rb + 4 k + w. Lane l = j + 16 g loads, per tile tau and path p,
+// the 16-byte unit (rg, 4 r + g, p, 16 tau + j): 128 columns of row
+// 16 tau + j, bit 4e + t of dword q being column 32 q + 4 e + t of the group.
+template <int NBP>
+__global__ __launch_bounds__(256) void k_gemv(Args A) {
+  const int r = blockIdx.x % A.S;
+  const int rbg = blockIdx.x / A.S;
+  // segment of this row block (uniform selects, no indexing of the arguments)
+  const int si = (A.nseg > 2 && rbg >= A.seg[2].rb0) ? 2 : (A.nseg > 1 && rbg >= A.seg[1].rb0) ? 1 : 0;
+  const uint4* planes = si == 2 ? A.seg[2].planes : si == 1 ? A.seg[1].planes : A.seg[0].planes;
+  const uint16_t* gsc = si == 2 ? A.seg[2].g : si == 1 ? A.seg[1].g : A.seg[0].g;
+  const uint16_t* hsc = si == 2 ? A.seg[2].h : si == 1 ? A.seg[1].h : A.seg[0].h;
+  void* yout = si == 2 ? A.seg[2].y : si == 1 ? A.seg[1].y : A.seg[0].y;
+  double* part = si == 2 ? A.seg[2].part : si == 1 ? A.seg[1].part : A.seg[0].part;
+  const int out = si == 2 ? A.seg[2].out : si == 1 ? A.seg[1].out : A.seg[0].out;
+  const int RG = si == 2 ? A.seg[2].RG : si == 1 ? A.seg[1].RG : A.seg[0].RG;
+  const int rb = rbg - (si == 2 ? A.seg[2].rb0 : si == 1 ? A.seg[1].rb0 : A.seg[0].rb0);
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
+  const int j = l & 15, gl = l >> 4;
+  const int bp0 = blockIdx.y * NBP;
+  const int in = A.in, batch = A.batch, m = A.m;
+  const int col0 = r * kChunk;
+
+  // weights of round k (clamped row group: loads stay in bounds, results unused)
+  // and the row scales g_p of this lane's 4 output rows
+  auto load_round = [&](uint4 (&wt)[8], uint16_t (&gt)[8], int k) {
+    const int rg = min(RG - 1, 4 * m * rb + 4 * k + w);
+    const int kg = min(A.KG - 1, 4 * r + gl);
+#pragma unroll
+    for (int tau = 0; tau < 4; ++tau)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) wt[tau * 2 + p] = load_nt(planes + unit_index(rg, kg, p, 16 * tau + j, A.KG));
+#pragma unroll
+    for (int tau = 0; tau < 4; ++tau)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) gt[tau * 2 + p] = gsc[(size_t)p * out + min(rg * 64 + 16 * tau + j, out - 1)];
+  };
+
+  __shared__ __align__(16) uint32_t s_img[NBP * kPairDwords];
+  __shared__ __align__(16) int s_v[2][2][kChunk];     // [hb][p][t*128 + g*32 + x] = v + kOff
+  __shared__ double s_max[4][2][2];     // per wave [hb][p]
+  __shared__ int s_sum[4][2][2];
+  __shared__ int s_sh[NBP][2][2];
+  __shared__ int s_U[NBP][2][2];
+
+  // ---- digit operand of this range, pair by pair ---------------------------
+  // element e = tid + 256 k (k = 0, 1) of the range: column col0 + e
+  // loads are unconditional (clamped indices) and masked afterwards, so that
+  // no branch separates them and they are all in flight together
+  uint16_t hv[2][2], xv[NBP][2][2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int col = col0 + tid + 256 * k;
+    const int cc = min(col, in - 1);
+#pragma unroll
+    for (int p = 0; p < 2; ++p) hv[p][k] = hsc[(size_t)p * in + cc];
+#pragma unroll
+    for (int q = 0; q < NBP; ++q)
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        const int b = 2 * (bp0 + q) + hb;
+        xv[q][hb][k] = A.x[(size_t)min(b, batch - 1) * in + cc];
+      }
+  }
+  // the first round's weights are issued after x and h: waiting for those
+  // (loads complete in order) then does not wait for the weights
+  uint4 w0[8], w1[8];
+  uint16_t g0[8], g1[8];
+  __builtin_amdgcn_sched_barrier(0);
+  load_round(w0, g0, 0);
+  __builtin_amdgcn_sched_barrier(0);  // keep every load above the first use of x and h
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const bool ok = col0 + tid + 256 * k < in;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) hv[p][k] = ok ? hv[p][k] : (uint16_t)0;
+#pragma unroll
+    for (int q = 0; q < NBP; ++q)
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+        xv[q][hb][k] = (ok && 2 * (bp0 + q) + hb < batch) ? xv[q][hb][k] : (uint16_t)0;
+  }
+
+#pragma unroll
+  for (int q = 0; q < NBP; ++q) {
+    double u[2][2][2];
+    double mx[2][2];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        mx[hb][p] = 0.0;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          u[hb][p][k] = (double)f16_bits_to_f32(hv[p][k]) * (double)bf16_bits_to_f32(xv[q][hb][k]);
+          mx[hb][p] = fmax(mx[hb][p], fabs(u[hb][p][k]));
+        }
+        mx[hb][p] = wave_max(mx[hb][p]);
+      }
+    if (l == 0)
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+        for (int p = 0; p < 2; ++p) s_max[w][hb][p] = mx[hb][p];
+    __syncthreads();
+    int sh[2][2];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const double M = fmax(fmax(s_max[0][hb][p], s_max[1][hb][p]), fmax(s_max[2][hb][p], s_max[3][hb][p]));
+        sh[hb][p] = M > 0.0 ? kFxTop - ilogb(M) : 0;
+        int su = 0;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int v = (int)rint(ldexp(u[hb][p][k], sh[hb][p]));
+          su += v;
+          const int e = tid + 256 * k;
+          const int t = e & 3, g = e >> 7, x = 8 * ((e >> 5) & 3) + ((e >> 2) & 7);
+          s_v[hb][p][t * 128 + g * 32 + x] = v + kOff;
+        }
+        su = wave_sum(su);
+        if (l == 0) s_sum[w][hb][p] = su;
+      }
+    __syncthreads();
+    if (tid < 4) {
+      const int hb = tid >> 1, p = tid & 1;
+      // same value as sh[hb][p], selected without indexing a register array
+      const int shs = (hb ? (p ? sh[1][1] : sh[1][0]) : (p ? sh[0][1] : sh[0][0]));
+      s_sh[q][hb][p] = shs;
+      s_U[q][hb][p] = ((s_sum[0][hb][p] + s_sum[1][hb][p]) + s_sum[2][hb][p]) + s_sum[3][hb][p];
     }
-    for (int k0 = 0; k0 < nkr; k0 += RING) {
+    // image rows: lane L = (8 hb + dr) + 16 g of image (p, t); the slice t is
+    // wave-uniform, so the code shift is a compile-time constant per branch
 #pragma unroll
-      for (int i = 0; i < RING; ++i) {
-        mfma_unit(acc0, w0[i], make_uint2(av[i].x, av[i].y));
-        mfma_unit(acc1, w1[i], make_uint2(av[i].z, av[i].w));
-        // keep each slot's three loads together and in ring order: loads
-        // complete in order, so the wait before a slot then covers only it
-        __builtin_amdgcn_sched_barrier(0);
-        const int kn = k0 + i + RING;
-        const int k = min(kn, nk - 1);
-        av[i] = *((kn < nk) ? abase + (size_t)kn * 64 : azero);
-        w0[i] = load_nt(wbase + (size_t)k * 128);
-        w1[i] = load_nt(wbase + (size_t)k * 128 + 64);
-        __builtin_amdgcn_sched_barrier(0);
+    for (int it = 0; it < 2; ++it) {
+      const int combo = w + 4 * it;  // (p, t)
+      const int p = combo >> 2, t = combo & 3;
+      const int dr = l & 7, hb = (l >> 3) & 1, g = l >> 4;
+      const int L = 8 * hb + dr + 16 * g;
+      const bool live = 2 * (bp0 + q) + hb < batch;
+      uint32_t dw[kImgDw];
+      int vals[32];
+      const int* src = &s_v[hb][p][t * 128 + g * 32];
+#pragma unroll
+      for (int x = 0; x < 32; x += 4) {
+        const int4 v4 = *(const int4*)(src + x);
+        vals[x] = v4.x;
+        vals[x + 1] = v4.y;
+        vals[x + 2] = v4.z;
+        vals[x + 3] = v4.w;
+      }
+      const bool dbl = (t == 0 || t == 3);  // slices of value 0.5: code 2d
+      if (dbl)
+        deposit_digits<1>(dw, vals, dr);
+      else
+        deposit_digits<0>(dw, vals, dr);
+      if (dr == 7) fill_code(dw, dbl ? 2u : 1u);  // row of ones: set-bit count
+      uint32_t* dst = s_img + q * kPairDwords + (p * 4 + t) * kImgDwords + L * kImgDw;
+#pragma unroll
+      for (int d = 0; d < kImgDw; d += 2)
+        *(uint2*)(dst + d) = make_uint2(live ? dw[d] : 0u, live ? dw[d + 1] : 0u);
+    }
+    __syncthreads();
+  }
+
+  // ---- stream the planes -----------------------------------------------------
+  // C lane l, reg k = row i = 4 gl + k of the digit operand (digit i % 8 of
+  // batch row 2 q + i / 8; i % 8 == 7 is the ones row), column j = row 16 tau + j.
+  const int hbl = gl >> 1;
+  double wdig[4];
+  if (gl & 1) {
+    wdig[0] = 32768.0;
+    wdig[1] = 262144.0;
+    wdig[2] = 2097152.0;
+    wdig[3] = -8.0 * kOff;
+  } else {
+    wdig[0] = 8.0;
+    wdig[1] = 64.0;
+    wdig[2] = 512.0;
+    wdig[3] = 4096.0;
+  }
+
+  // this lane's row of image (pair q, path/slice ps)
+  auto image_row = [&](int q, int ps) -> v8i {
+    const uint32_t* s = s_img + q * kPairDwords + ps * kImgDwords + l * kImgDw;
+    const uint2 a0 = *(const uint2*)(s), a1 = *(const uint2*)(s + 2), a2 = *(const uint2*)(s + 4);
+    return (v8i){(int)a0.x, (int)a0.y, (int)a1.x, (int)a1.y, (int)a2.x, (int)a2.y, 0, 0};
+  };
+  // with one batch pair the 8 operand rows of this lane stay in registers
+  v8i areg[8];
+#pragma unroll
+  for (int ps = 0; ps < 8; ++ps) areg[ps] = NBP == 1 ? image_row(0, ps) : (v8i){};
+
+  // one round: row group 4 m rb + 4 k + w from the weights in wt
+  auto round = [&](const uint4 (&wt)[8], const uint16_t (&gt)[8], int k) {
+    const int rg = 4 * m * rb + 4 * k + w;
+    double res[NBP][4];
+#pragma unroll
+    for (int q = 0; q < NBP; ++q)
+#pragma unroll
+      for (int tau = 0; tau < 4; ++tau) res[q][tau] = 0.0;
+
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      v4f acc[NBP][4];
+#pragma unroll
+      for (int q = 0; q < NBP; ++q)
+#pragma unroll
+        for (int tau = 0; tau < 4; ++tau) acc[q][tau] = (v4f){0.f, 0.f, 0.f, 0.f};
+      auto slice_step = [&](auto tc) {
+        constexpr int T = decltype(tc)::value;
+        v8i a[NBP];
+#pragma unroll
+        for (int q = 0; q < NBP; ++q) a[q] = NBP == 1 ? areg[p * 4 + T] : image_row(q, p * 4 + T);
+#pragma unroll
+        for (int tau = 0; tau < 4; ++tau) {
+          const v8i bv = slice4<T>(wt[tau * 2 + p]);
+#pragma unroll
+          for (int q = 0; q < NBP; ++q)
+            acc[q][tau] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                a[q], bv, acc[q][tau], 2 /*A: fp6 e2m3*/, 4 /*B: fp4 e2m1*/, 0, 127, 0, 127);
+        }
+      };
+      slice_step(std::integral_constant<int, 0>());
+      slice_step(std::integral_constant<int, 1>());
+      slice_step(std::integral_constant<int, 2>());
+      slice_step(std::integral_constant<int, 3>());
+
+#pragma unroll
+      for (int q = 0; q < NBP; ++q) {
+        const int shv = s_sh[q][hbl][p];
+        const double U = (double)s_U[q][hbl][p];
+#pragma unroll
+        for (int tau = 0; tau < 4; ++tau) {
+          const v4f c = acc[q][tau];
+          double v = wdig[0] * c[0] + wdig[1] * c[1] + wdig[2] * c[2] + wdig[3] * c[3];
+          v += __shfl_down(v, 16, 64);  // digits 4..6 and the count term
+          const double gp = (double)f16_bits_to_f32(gt[tau * 2 + p]);
+          res[q][tau] += gp * ldexp(U - 2.0 * v, -shv);
+        }
       }
     }
-    M0 = combine_slices(acc0);
-    M1 = combine_slices(acc1);
-  }
 
-  const int row = rg * 64 + l;
-  const size_t ri0 = ((size_t)b * 2 + 0) * P.S + r, ri1 = ((size_t)b * 2 + 1) * P.S + r;
-  double part = 0.0;
-  if (nk > 0 && row < out) {
-    const double s0 = ldexp((double)(ws.rusum[ri0] - 2 * M0), -ws.rshift[ri0]);
-    const double s1 = ldexp((double)(ws.rusum[ri1] - 2 * M1), -ws.rshift[ri1]);
-    part = (double)f16_bits_to_f32(g[row]) * s0 + (double)f16_bits_to_f32(g[out + row]) * s1;
-  }
-  __shared__ double red[kWaves][64];
-  red[w][l] = part;
-  __syncthreads();
-  if (w == 0) {
-    double v = red[0][l];
-    v += red[1][l];
-    v += red[2][l];
-    v += red[3][l];
-    if (P.SG == 1) {
-      if (row < out) store_y(y, y_dtype, (size_t)b * out + row, v);
-    } else {
-      ws.part[((size_t)b * P.SG + sg) * P.RG * 64 + row] = v;
+    if (rg < RG && (gl & 1) == 0) {
+#pragma unroll
+      for (int q = 0; q < NBP; ++q) {
+        const int b = 2 * (bp0 + q) + hbl;
+        if (b >= batch) continue;
+#pragma unroll
+        for (int tau = 0; tau < 4; ++tau) {
+          const int row = rg * 64 + 16 * tau + j;
+          if (row >= out) continue;
+          if (A.direct) {
+            if (A.y_dtype == RABIT_OUT_F32)
+              ((float*)yout)[(size_t)b * out + row] = (float)res[q][tau];
+            else
+              ((uint16_t*)yout)[(size_t)b * out + row] = f64_to_bf16_rne(res[q][tau]);
+          } else {
+            part[((size_t)b * A.S + r) * RG * 64 + row] = res[q][tau];
+          }
+        }
+      }
+    }
+  };
+
+  // rounds in pairs, so that each ring buffer is a fixed register array
+#pragma unroll 1
+  for (int k = 0; k < m; k += 2) {
+    if (k + 1 < m) load_round(w1, g1, k + 1);
+    round(w0, g0, k);
+    if (k + 1 < m) {
+      if (k + 2 < m) load_round(w0, g0, k + 2);
+      round(w1, g1, k + 1);
     }
   }
 }
 
-// y = Σ_sg part (ascending sg)
-__global__ __launch_bounds__(256) void k_gemv_reduce(int out, Plan P, GemvWs ws, void* y,
-                                                     int y_dtype) {
+// y = Σ_r part (ascending r)
+__global__ __launch_bounds__(256) void k_gemv_reduce(const double* __restrict__ part, int out,
+                                                     int RG, int S, void* y, int y_dtype) {
   const int row = blockIdx.x * 256 + threadIdx.x, b = blockIdx.y;
   if (row >= out) return;
-  const double* pp = ws.part + (size_t)b * P.SG * P.RG * 64 + row;
+  const double* pp = part + (size_t)b * S * RG * 64 + row;
   double v = 0.0;
-  for (int s = 0; s < P.SG; ++s) v += pp[(size_t)s * P.RG * 64];
-  store_y(y, y_dtype, (size_t)b * out + row, v);
+  for (int s = 0; s < S; ++s) v += pp[(size_t)s * RG * 64];
+  if (y_dtype == RABIT_OUT_F32)
+    ((float*)y)[(size_t)b * out + row] = (float)v;
+  else
+    ((uint16_t*)y)[(size_t)b * out + row] = f64_to_bf16_rne(v);
+}
+
+hipError_t launch_main(const Plan& P, const Args& A, int batch, hipStream_t st) {
+  int nrb = 0;
+  for (int s = 0; s < A.nseg; ++s) nrb += P.RB[s];
+  const int pairs = (batch + 1) / 2;
+  const dim3 grid(nrb * P.S, (pairs + P.NBP - 1) / P.NBP);
+  switch (P.NBP) {
+    case 1: hipLaunchKernelGGL(k_gemv<1>, grid, dim3(256), 0, st, A); break;
+    case 2: hipLaunchKernelGGL(k_gemv<2>, grid, dim3(256), 0, st, A); break;
+    case 4: hipLaunchKernelGGL(k_gemv<4>, grid, dim3(256), 0, st, A); break;
+    default: hipLaunchKernelGGL(k_gemv<4>, grid, dim3(256), 0, st, A); break;
+  }
+  return hipGetLastError();
+}
+
+Args make_args(const Plan& P, const uint4* planes, const uint16_t* g, const uint16_t* h, int out,
+               int in, const uint16_t* x, int batch, void* y, int y_dtype, void* ws, bool direct) {
+  Args A = {};
+  A.seg[0].planes = planes;
+  A.seg[0].g = g;
+  A.seg[0].h = h;
+  A.seg[0].y = y;
+  A.seg[0].part = (double*)ws;
+  A.seg[0].out = out;
+  A.seg[0].RG = row_groups(out);
+  A.seg[0].rb0 = 0;
+  A.x = x;
+  A.nseg = 1;
+  A.in = in;
+  A.KG = P.KG;
+  A.S = P.S;
+  A.m = P.m;
+  A.batch = batch;
+  A.y_dtype = y_dtype;
+  A.direct = direct ? 1 : 0;
+  return A;
 }
 
 }  // namespace
 
 size_t gemv_workspace_bytes(int out, int in, int batch) {
-  return ws_layout(make_plan(out, in), batch, nullptr, nullptr);
+  const int S = (in + kChunk - 1) / kChunk;
+  return part_bytes(out, S, batch);
 }
 
-hipError_t launch_gemv_prepare(const uint16_t* h, int out, int in, const uint16_t* x, int batch,
-                               void* ws, hipStream_t st) {
-  const Plan P = make_plan(out, in);
-  GemvWs w;
-  ws_layout(P, batch, ws, &w);
-  hipLaunchKernelGGL(k_gemv_prep, dim3(P.S, 2, batch), dim3(256), 0, st, x, h, in, P, w);
-  return hipGetLastError();
+hipError_t launch_gemv_partial(const uint4* planes, const uint16_t* g, const uint16_t* h, int out,
+                               int in, const uint16_t* x, int batch, void* ws, hipStream_t st) {
+  const Plan P = make_plan(&out, 1, in, batch);
+  const Args A = make_args(P, planes, g, h, out, in, x, batch, nullptr, RABIT_OUT_F32, ws, false);
+  return launch_main(P, A, batch, st);
 }
 
-hipError_t launch_gemv_run(const uint4* planes, const uint16_t* g, int out, int in, int batch,
-                           void* y, int y_dtype, void* ws, hipStream_t st) {
-  const Plan P = make_plan(out, in);
-  GemvWs w;
-  ws_layout(P, batch, ws, &w);
-  const dim3 grid(P.RG * P.SG, batch);
-  if (P.ring == 1)
-    hipLaunchKernelGGL(k_gemv_main<1>, grid, dim3(256), 0, st, planes, g, out, P, w, y, y_dtype);
-  else if (P.ring == 2)
-    hipLaunchKernelGGL(k_gemv_main<2>, grid, dim3(256), 0, st, planes, g, out, P, w, y, y_dtype);
-  else
-    hipLaunchKernelGGL(k_gemv_main<3>, grid, dim3(256), 0, st, planes, g, out, P, w, y, y_dtype);
-  if (P.SG > 1)
-    hipLaunchKernelGGL(k_gemv_reduce, dim3((out + 255) / 256, batch), dim3(256), 0, st, out, P, w,
-                       y, y_dtype);
+hipError_t launch_gemv_reduce(int out, int in, int batch, void* y, int y_dtype, const void* ws,
+                              hipStream_t st) {
+  const int S = (in + kChunk - 1) / kChunk;
+  hipLaunchKernelGGL(k_gemv_reduce, dim3((out + 255) / 256, batch), dim3(256), 0, st,
+                     (const double*)ws, out, row_groups(out), S, y, y_dtype);
   return hipGetLastError();
 }
 
 hipError_t launch_gemv(const uint4* planes, const uint16_t* g, const uint16_t* h, int out, int in,
                        const uint16_t* x, int batch, void* y, int y_dtype, void* ws,
                        hipStream_t st) {
-  hipError_t e = launch_gemv_prepare(h, out, in, x, batch, ws, st);
+  const Plan P = make_plan(&out, 1, in, batch);
+  if (P.S == 1) {
+    const Args A = make_args(P, planes, g, h, out, in, x, batch, y, y_dtype, ws, true);
+    return launch_main(P, A, batch, st);
+  }
+  hipError_t e = launch_gemv_partial(planes, g, h, out, in, x, batch, ws, st);
   if (e != hipSuccess) return e;
-  return launch_gemv_run(planes, g, out, in, batch, y, y_dtype, ws, st);
+  return launch_gemv_reduce(out, in, batch, y, y_dtype, ws, st);
 }
 
 }  // namespace rabit

@@ -148,27 +148,37 @@ int rabit_gemv(const rabit_layer* L, const uint16_t* x, int32_t batch, void* y, 
   if (batch < 1 || batch > RABIT_MAX_GEMV_BATCH) return RABIT_ESHAPE;
   if ((s = check_gemv_x(L, x)) || (s = check_gemv_y(L, batch, y, y_dtype, x))) return s;
   if ((s = check_gemv_common(L, batch, workspace, workspace_bytes))) return s;
+  const size_t wsb = gemv_workspace_bytes(L->out_features, L->in_features, batch);
+  const size_t yb = (size_t)batch * L->out_features * (y_dtype == RABIT_OUT_F32 ? 4 : 2);
+  if (overlap(workspace, wsb, x, (size_t)batch * L->in_features * 2) ||
+      overlap(workspace, wsb, y, yb))
+    return RABIT_EINVAL;
   return dev_status(launch_gemv((const uint4*)L->planes, L->g, L->h, L->out_features,
                                 L->in_features, x, batch, y, y_dtype, workspace,
                                 (hipStream_t)stream));
 }
 
-int rabit_gemv_prepare(const rabit_layer* L, const uint16_t* x, int32_t batch, void* workspace,
+int rabit_gemv_partial(const rabit_layer* L, const uint16_t* x, int32_t batch, void* workspace,
                        size_t workspace_bytes, void* stream) {
   int s = check_gemv_common(L, batch, workspace, workspace_bytes);
   if (s) return s;
   if ((s = check_gemv_x(L, x))) return s;
-  return dev_status(launch_gemv_prepare(L->h, L->out_features, L->in_features, x, batch, workspace,
-                                        (hipStream_t)stream));
+  const size_t wsb = gemv_workspace_bytes(L->out_features, L->in_features, batch);
+  if (overlap(workspace, wsb, x, (size_t)batch * L->in_features * 2)) return RABIT_EINVAL;
+  return dev_status(launch_gemv_partial((const uint4*)L->planes, L->g, L->h, L->out_features,
+                                        L->in_features, x, batch, workspace, (hipStream_t)stream));
 }
 
-int rabit_gemv_run(const rabit_layer* L, int32_t batch, void* y, int32_t y_dtype, void* workspace,
-                   size_t workspace_bytes, void* stream) {
+int rabit_gemv_reduce(const rabit_layer* L, int32_t batch, void* y, int32_t y_dtype, void* workspace,
+                      size_t workspace_bytes, void* stream) {
   int s = check_gemv_common(L, batch, workspace, workspace_bytes);
   if (s) return s;
   if ((s = check_gemv_y(L, batch, y, y_dtype, nullptr))) return s;
-  return dev_status(launch_gemv_run((const uint4*)L->planes, L->g, L->out_features, L->in_features,
-                                    batch, y, y_dtype, workspace, (hipStream_t)stream));
+  const size_t yb = (size_t)batch * L->out_features * (y_dtype == RABIT_OUT_F32 ? 4 : 2);
+  if (overlap(workspace, gemv_workspace_bytes(L->out_features, L->in_features, batch), y, yb))
+    return RABIT_EINVAL;
+  return dev_status(launch_gemv_reduce(L->out_features, L->in_features, batch, y, y_dtype,
+                                       workspace, (hipStream_t)stream));
 }
 
 int rabit_gemm(const rabit_layer* L, const uint16_t* X, int32_t m, void* Y, int32_t y_dtype,

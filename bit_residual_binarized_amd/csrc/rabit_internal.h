@@ -92,10 +92,10 @@ hipError_t launch_unpack(const uint4* planes, int out, int in, uint32_t* words, 
 size_t gemv_workspace_bytes(int out, int in, int batch);
 hipError_t launch_gemv(const uint4* planes, const uint16_t* g, const uint16_t* h, int out, int in,
                        const uint16_t* x, int batch, void* y, int y_dtype, void* ws, hipStream_t st);
-hipError_t launch_gemv_prepare(const uint16_t* h, int out, int in, const uint16_t* x, int batch,
-                               void* ws, hipStream_t st);
-hipError_t launch_gemv_run(const uint4* planes, const uint16_t* g, int out, int in, int batch,
-                           void* y, int y_dtype, void* ws, hipStream_t st);
+hipError_t launch_gemv_partial(const uint4* planes, const uint16_t* g, const uint16_t* h, int out,
+                               int in, const uint16_t* x, int batch, void* ws, hipStream_t st);
+hipError_t launch_gemv_reduce(int out, int in, int batch, void* y, int y_dtype, const void* ws,
+                              hipStream_t st);
 
 size_t gemm_workspace_bytes(int out, int in, int m);
 hipError_t launch_gemm(const uint4* planes, const uint16_t* g, const uint16_t* h, int out, int in,

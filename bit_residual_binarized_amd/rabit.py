@@ -34,7 +34,7 @@ EXPORTS = [
     "rabit_planes_bytes", "rabit_pack_workspace_bytes", "rabit_gemv_workspace_bytes",
     "rabit_gemm_workspace_bytes", "rabit_pack", "rabit_unpack", "rabit_gemv", "rabit_gemm",
     "rabit_decode_workspace_bytes", "rabit_decode_step", "rabit_status_string",
-    "rabit_layout_version", "rabit_test_f64_to_16", "rabit_gemv_prepare", "rabit_gemv_run",
+    "rabit_layout_version", "rabit_test_f64_to_16", "rabit_gemv_partial", "rabit_gemv_reduce",
 ]
 
 
@@ -92,8 +92,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "rabit_unpack": (ctypes.c_int, [lp, vp, vp]),
         "rabit_gemv": (ctypes.c_int, [lp, vp, i32, vp, i32, vp, sz, vp]),
         "rabit_gemm": (ctypes.c_int, [lp, vp, i32, vp, i32, vp, sz, vp]),
-        "rabit_gemv_prepare": (ctypes.c_int, [lp, vp, i32, vp, sz, vp]),
-        "rabit_gemv_run": (ctypes.c_int, [lp, i32, vp, i32, vp, sz, vp]),
+        "rabit_gemv_partial": (ctypes.c_int, [lp, vp, i32, vp, sz, vp]),
+        "rabit_gemv_reduce": (ctypes.c_int, [lp, i32, vp, i32, vp, sz, vp]),
         "rabit_decode_workspace_bytes": (sz, [ctypes.POINTER(DecoderCfgC), i32]),
         "rabit_decode_step": (ctypes.c_int, [ctypes.POINTER(DecoderCfgC), lp, vp, i32, vp, vp, sz, vp]),
         "rabit_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -209,18 +209,20 @@ def gemv(layer: PackedLayer, x: torch.Tensor, y_dtype: int = RABIT_OUT_F32,
     return y
 
 
-def gemv_prepare(layer: PackedLayer, x: torch.Tensor, workspace: torch.Tensor, stream=None) -> None:
+def gemv_partial(layer: PackedLayer, x: torch.Tensor, workspace: torch.Tensor, stream=None) -> None:
+    """rabit_gemv_partial: one launch over every plane byte; partials stay in workspace."""
     assert x.dtype == torch.bfloat16 and x.is_contiguous()
     lc = layer.c()
-    _check(load().rabit_gemv_prepare(ctypes.byref(lc), _ptr(x), x.shape[0], _ptr(workspace),
-                                     workspace.numel(), _stream(stream)), "rabit_gemv_prepare")
+    _check(load().rabit_gemv_partial(ctypes.byref(lc), _ptr(x), x.shape[0], _ptr(workspace),
+                                     workspace.numel(), _stream(stream)), "rabit_gemv_partial")
 
 
-def gemv_run(layer: PackedLayer, batch: int, y: torch.Tensor, workspace: torch.Tensor,
-             y_dtype: int = RABIT_OUT_F32, stream=None) -> torch.Tensor:
+def gemv_reduce(layer: PackedLayer, batch: int, y: torch.Tensor, workspace: torch.Tensor,
+                y_dtype: int = RABIT_OUT_F32, stream=None) -> torch.Tensor:
+    """rabit_gemv_reduce: sums the partials of the last gemv_partial into y."""
     lc = layer.c()
-    _check(load().rabit_gemv_run(ctypes.byref(lc), batch, _ptr(y), y_dtype, _ptr(workspace),
-                                 workspace.numel(), _stream(stream)), "rabit_gemv_run")
+    _check(load().rabit_gemv_reduce(ctypes.byref(lc), batch, _ptr(y), y_dtype, _ptr(workspace),
+                                    workspace.numel(), _stream(stream)), "rabit_gemv_reduce")
     return y
 
 

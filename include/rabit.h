@@ -146,11 +146,13 @@ int rabit_unpack(const rabit_layer *layer, uint32_t *words, void *stream);
  * y       device [batch][out], float32 (RABIT_OUT_F32) or bfloat16
  *         (RABIT_OUT_BF16), written entirely.
  * Arithmetic: h_p*x is formed exactly and held as a fixed-point integer per
- * (batch row, path), scaled by a power of two so that the largest |h_p*x|
- * maps into [2^29, 2^30) (per-element error <= 2^-30 of that largest value);
- * the signed sums are exact integers; the final combination is done in
- * float64 and rounded once.
+ * (batch row, path, range of 512 input columns), scaled by a power of two so
+ * that the range's largest |h_p*x| maps into [2^18, 2^19) (per-element error
+ * <= 2^-19 of that largest value); the signed sums are exact integers; each
+ * range's g_1 S_1 + g_2 S_2 is formed in float64, the ranges are summed in
+ * float64 in ascending order and the result is rounded once.
  * Result is bitwise repeatable (no order-dependent arithmetic).
+ * workspace must not overlap x or y.
  */
 int rabit_gemv(const rabit_layer *layer, const uint16_t *x, int32_t batch,
                void *y, int32_t y_dtype, void *workspace, size_t workspace_bytes,
@@ -158,16 +160,16 @@ int rabit_gemv(const rabit_layer *layer, const uint16_t *x, int32_t batch,
 
 /*
  * The two halves of rabit_gemv, for callers that time or schedule them apart.
- * rabit_gemv_prepare forms the activation operand of every path (u_p = h_p ⊙
- * x in fixed point, its per-row shift and Σ u) in the workspace and clears
- * the split-K state; rabit_gemv_run streams the planes and writes y. A run
- * consumes the workspace of the last prepare for the same layer and batch;
- * rabit_gemv is prepare followed by run. Errors as rabit_gemv.
+ * rabit_gemv_partial streams every plane byte in one kernel launch and leaves
+ * in the workspace the float64 partial result of each range of 512 input
+ * columns; rabit_gemv_reduce sums those partials (ascending range) into y.
+ * A reduce consumes the workspace of the last partial for the same layer and
+ * batch; the pair gives the same bits as rabit_gemv. Errors as rabit_gemv.
  */
-int rabit_gemv_prepare(const rabit_layer *layer, const uint16_t *x, int32_t batch,
+int rabit_gemv_partial(const rabit_layer *layer, const uint16_t *x, int32_t batch,
                        void *workspace, size_t workspace_bytes, void *stream);
-int rabit_gemv_run(const rabit_layer *layer, int32_t batch, void *y, int32_t y_dtype,
-                   void *workspace, size_t workspace_bytes, void *stream);
+int rabit_gemv_reduce(const rabit_layer *layer, int32_t batch, void *y, int32_t y_dtype,
+                      void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Prefill GEMM: Y[m][i] = Σ_p g_p[i] * Σ_j B_p[i][j] * h_p[j] * X[m][j].

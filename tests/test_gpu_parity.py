@@ -53,6 +53,33 @@ def check_pack(rabit, layer, d, out, inp, check_scales=True):
             assert bad.size == 0, f"{name}: {bad.size} fp16 scales differ, first at {bad[:5]}"
 
 
+def fx_bound(d, xv):
+    """Elementwise error bound of the GEMV arithmetic stated in rabit.h.
+
+    Per (batch row, path, range of 512 columns) h_p*x is rounded to a grid of
+    step 2^(ilogb(max |h_p*x|) - 18), so each element is off by at most half a
+    step; the signed sums are exact and g_p is applied in float64. The fp32
+    output rounding is covered separately (2^-23 |y|)."""
+    xb = np.atleast_2d(xv)
+    B, K = xb.shape
+    bound = np.zeros((B, d.g1.shape[0]))
+    for g, h in ((d.g1, d.h1), (d.g2, d.h2)):
+        u = np.abs(h.astype(np.float64)[None, :] * xb)
+        tot = np.zeros(B)
+        for c0 in range(0, K, 512):
+            mr = u[:, c0:c0 + 512].max(axis=1)
+            _, e = np.frexp(mr)  # mr = f 2^e, f in [0.5, 1): ilogb = e - 1
+            tot += np.where(mr > 0, min(512, K - c0) * np.exp2(e - 1.0 - 19.0), 0.0)
+        bound += np.abs(g.astype(np.float64))[None, :] * tot[:, None]
+    return bound
+
+
+def check_fx(y, ref, d, xv):
+    bound = fx_bound(d, xv) + 2.0 ** -23 * np.abs(ref) + 1e-300
+    bad = np.argwhere(np.abs(y - ref) > bound)
+    assert bad.size == 0, f"{len(bad)} outputs outside the fixed-point bound, first {bad[:3].tolist()}"
+
+
 PACK_SHAPES = [(4, 8), (64, 256), (100, 300), (130, 1000), (1, 1), (65, 129), (256, 4096),
                (1024, 4096), (4096, 4096)]
 
@@ -144,6 +171,7 @@ def test_gemv_batch1(gpu_lib, shape):
     err = oracle.normwise_rel_err(y, ref)
     say("  normwise err", err)
     assert err < TOL
+    check_fx(y, ref, d, bf16_values(x))
     y2 = gpu_lib.gemv(layer, x.cuda()).cpu().numpy()
     assert np.array_equal(y.astype(np.float32), y2), "not repeatable"
 
@@ -161,6 +189,7 @@ def test_gemv_batches(gpu_lib, batch):
     err = oracle.normwise_rel_err(y, ref)
     say("  normwise err", err)
     assert err < TOL
+    check_fx(y, ref, d, bf16_values(x))
 
 
 def test_gemv_unit_vector_probe_bit_exact(gpu_lib):
@@ -188,21 +217,24 @@ def test_gemv_bf16_output_and_outlier_input(gpu_lib):
     x[1, 100:110] = 1e-30
     ref = oracle.gemv(d, bf16_values(x))
     yf = gpu_lib.gemv(layer, x.cuda()).cpu().numpy().astype(np.float64)
-    assert oracle.normwise_rel_err(yf, ref) < 1e-6
+    assert oracle.normwise_rel_err(yf, ref) < TOL
+    check_fx(yf, ref, d, bf16_values(x))
     yb = gpu_lib.gemv(layer, x.cuda(), y_dtype=gpu_lib.RABIT_OUT_BF16).cpu().to(torch.float32).numpy()
     assert oracle.normwise_rel_err(yb.astype(np.float64), ref) < 2 ** -8
 
 
-def test_gemv_prepare_run_equals_gemv(gpu_lib):
-    out, inp = 1000, 3000
-    say("gemv prepare/run")
+@pytest.mark.parametrize("shape", [(1000, 3000), (300, 512), (4096, 11008)])
+def test_gemv_partial_reduce_equals_gemv(gpu_lib, shape):
+    out, inp = shape
+    say("gemv partial/reduce", shape)
     layer = pack_gpu(gpu_lib, weight_f32(out, inp, 8))
-    x = act_bf16(1, inp, 9).cuda()
-    ws = gpu_lib.gemv_workspace(layer, 1)
-    y = torch.empty(1, out, device="cuda")
-    gpu_lib.gemv_prepare(layer, x, ws)
-    gpu_lib.gemv_run(layer, 1, y, ws)
-    assert torch.equal(y, gpu_lib.gemv(layer, x))
+    for batch in (1, 3):
+        x = act_bf16(batch, inp, 9 + batch).cuda()
+        ws = gpu_lib.gemv_workspace(layer, batch)
+        y = torch.empty(batch, out, device="cuda")
+        gpu_lib.gemv_partial(layer, x, ws)
+        gpu_lib.gemv_reduce(layer, batch, y, ws)
+        assert torch.equal(y, gpu_lib.gemv(layer, x))
 
 
 GEMM_CASES = [(64, 256, 1), (130, 1000, 37), (256, 4096, 512), (1024, 4096, 130), (300, 1100, 257)]
