@@ -3,6 +3,8 @@
 // residual add). The pages time Llama2 decoding (RaBiT paper Table 7, App.
 // E.2) without defining these ops; they are not part of the timed linear
 // layers. Each rounds its result once to bfloat16 from float64.
+#include <algorithm>
+
 #include "rabit_internal.h"
 
 namespace rabit {
@@ -62,7 +64,97 @@ __global__ void k_residual_add(const uint16_t* __restrict__ x, const float* __re
   out[i] = f64_to_bf16_rne((double)bf16_bits_to_f32(x[i]) + (double)d[i]);
 }
 
+// ---- consumers of GEMV partials (fused with the ops that follow a layer) ----
+// part: float64 [batch][S][stride] with S = ceil(in/512) ranges of the
+// producing GEMV and stride = 64 ceil(n/64); ranges are added in ascending
+// order, as rabit_gemv_reduce does.
+__device__ __forceinline__ double sum_ranges(const double* __restrict__ part, int b, int S,
+                                             int stride, int i) {
+  const double* pp = part + (size_t)b * S * stride + i;
+  double v = 0.0;
+  for (int r = 0; r < S; ++r) v += pp[(size_t)r * stride];
+  return v;
+}
+
+// Block (i, b) covers elements [i span, (i + 1) span) of row b: x_out =
+// bf16(x + Σ part) (or x itself without part) and the sum of x_out^2 over
+// the block, combined in a fixed order, into stats[b][i].
+__global__ __launch_bounds__(256) void k_resid_stats(const double* __restrict__ part, int S,
+                                                     const uint16_t* x, uint16_t* x_out,
+                                                     double* __restrict__ stats, int n) {
+  const int i = blockIdx.x, b = blockIdx.y;
+  const int span = (n + RABIT_STAT_PARTS - 1) / RABIT_STAT_PARTS;
+  const int e0 = i * span, e1 = min(n, e0 + span);
+  const int stride = 64 * ((n + 63) / 64);
+  double ss = 0.0;
+  for (int e = e0 + (int)threadIdx.x; e < e1; e += 256) {
+    double v = (double)bf16_bits_to_f32(x[(size_t)b * n + e]);
+    if (part) {
+      const uint16_t o = f64_to_bf16_rne(v + sum_ranges(part, b, S, stride, e));
+      x_out[(size_t)b * n + e] = o;
+      v = (double)bf16_bits_to_f32(o);
+    }
+    ss += v * v;
+  }
+  ss = wave_sum_f64(ss);
+  __shared__ double s_w[4];
+  if ((threadIdx.x & 63) == 0) s_w[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  if (threadIdx.x == 0) stats[(size_t)b * RABIT_STAT_PARTS + i] = ((s_w[0] + s_w[1]) + s_w[2]) + s_w[3];
+}
+
+__global__ __launch_bounds__(256) void k_reduce_silu(const double* __restrict__ pg,
+                                                     const double* __restrict__ pu, int S,
+                                                     uint16_t* __restrict__ a, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x, b = blockIdx.y;
+  if (i >= n) return;
+  const int stride = 64 * ((n + 63) / 64);
+  const double g = sum_ranges(pg, b, S, stride, i), u = sum_ranges(pu, b, S, stride, i);
+  a[(size_t)b * n + i] = f64_to_bf16_rne(g / (1.0 + exp(-g)) * u);
+}
+
+// qk: [batch][n_q + kv] fp32 (q then k); attn: [batch][n_q] bf16
+__global__ __launch_bounds__(256) void k_reduce_attn(const double* __restrict__ pq,
+                                                     const double* __restrict__ pk,
+                                                     const double* __restrict__ pv, int S,
+                                                     float* __restrict__ qk,
+                                                     uint16_t* __restrict__ attn, int n_q, int kv,
+                                                     int rep, int head_dim) {
+  const int i = blockIdx.x * 256 + threadIdx.x, b = blockIdx.y;
+  const int sq = 64 * ((n_q + 63) / 64), skv = 64 * ((kv + 63) / 64);
+  if (i < n_q) {
+    qk[(size_t)b * (n_q + kv) + i] = (float)sum_ranges(pq, b, S, sq, i);
+    const int h = i / head_dim, d = i - h * head_dim;
+    attn[(size_t)b * n_q + i] = f64_to_bf16_rne(sum_ranges(pv, b, S, skv, (h / rep) * head_dim + d));
+  }
+  if (i < kv) qk[(size_t)b * (n_q + kv) + n_q + i] = (float)sum_ranges(pk, b, S, skv, i);
+}
+
 }  // namespace
+
+hipError_t launch_resid_stats(const double* part, int in_of_part, const uint16_t* x, uint16_t* x_out,
+                              double* stats, int batch, int n, hipStream_t st) {
+  hipLaunchKernelGGL(k_resid_stats, dim3(RABIT_STAT_PARTS, batch), dim3(256), 0, st, part,
+                     (in_of_part + 511) / 512, x, x_out, stats, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_reduce_silu(const double* pg, const double* pu, int in_of_part, uint16_t* a,
+                              int batch, int n, hipStream_t st) {
+  hipLaunchKernelGGL(k_reduce_silu, dim3((n + 255) / 256, batch), dim3(256), 0, st, pg, pu,
+                     (in_of_part + 511) / 512, a, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_reduce_attn(const double* pq, const double* pk, const double* pv,
+                              int in_of_part, float* qk, uint16_t* attn, int batch, int n_heads,
+                              int n_kv_heads, int head_dim, hipStream_t st) {
+  const int n_q = n_heads * head_dim, kv = n_kv_heads * head_dim;
+  hipLaunchKernelGGL(k_reduce_attn, dim3((std::max(n_q, kv) + 255) / 256, batch), dim3(256), 0, st,
+                     pq, pk, pv, (in_of_part + 511) / 512, qk, attn, n_q, kv, n_heads / n_kv_heads,
+                     head_dim);
+  return hipGetLastError();
+}
 
 hipError_t launch_rmsnorm(const uint16_t* x, uint16_t* y, int batch, int n, float eps,
                           hipStream_t st) {

@@ -25,10 +25,10 @@
 //    and h (no separate activation pass), then its 4 waves stream 64-row
 //    groups of planes through the matrix cores (one 8 KiB slab per wave and
 //    row group, prefetched one row group ahead).
-//  * Per range, g_1 S_1 + g_2 S_2 is formed in float64 from exact integers.
-//    With one range it is the output; otherwise the ranges' partials are
-//    summed in a fixed order by a small kernel, so the output is bitwise
-//    repeatable. No atomics, no fences.
+//  * Per range, g_1 S_1 + g_2 S_2 is formed in float64 from exact integers;
+//    the ranges' partials are summed in a fixed order by the consumer (a
+//    small reduce kernel, or the fused op that follows the layer), so the
+//    output is bitwise repeatable. No atomics, no fences.
 #include <algorithm>
 #include <type_traits>
 
@@ -47,6 +47,8 @@ constexpr int kImgDwords = 64 * kImgDw;        // one (path, slice) image
 constexpr int kPairDwords = 8 * kImgDwords;    // 2 paths x 4 slices, one batch pair (12 KiB)
 constexpr int kFxTop = 18;                     // max |v| of a range in [2^18, 2^19]
 constexpr int kOff = 1 << 20;                  // v + kOff in [0, 2^21): 7 digits of base 8
+constexpr int kNoExp = -100000;                // exponent of an all-zero range
+constexpr int kStatParts = RABIT_STAT_PARTS;   // partial sums of x^2 per row (RMSNorm input)
 
 // One matrix of a launch. All segments of a launch share the input x (and so
 // in_features); their row blocks are numbered consecutively.
@@ -54,8 +56,7 @@ struct Seg {
   const uint4* planes;
   const uint16_t* g;
   const uint16_t* h;
-  void* y;       // output [batch][out] (direct mode)
-  double* part;  // partials [batch][S][RG*64] (split mode)
+  double* part;  // partials [batch][S][RG*64]
   int out, RG, rb0;
 };
 
@@ -63,8 +64,10 @@ constexpr int kMaxSeg = 3;
 
 struct Args {
   Seg seg[kMaxSeg];
-  const uint16_t* x;  // bf16 [batch][in]
-  int nseg, in, KG, S, m, batch, y_dtype, direct;
+  const uint16_t* x;      // bf16 [batch][in]
+  const double* stats;    // norm mode: [batch][kStatParts] partial sums of x^2
+  int nseg, in, KG, S, m, batch, norm;
+  float eps;
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -97,29 +100,6 @@ __host__ inline size_t part_bytes(int out, int S, int batch) {
   return align256((size_t)batch * S * row_groups(out) * 64 * sizeof(double));
 }
 
-__device__ __forceinline__ double wave_max(double v) {
-#pragma unroll
-  for (int s = 32; s >= 1; s >>= 1) v = fmax(v, __shfl_xor(v, s, 64));
-  return v;
-}
-__device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-  for (int s = 32; s >= 1; s >>= 1) v += __shfl_xor(v, s, 64);
-  return v;
-}
-
-// fp4 slice t of four stored words (see the header comment)
-template <int T>
-__device__ __forceinline__ v8i slice4(const uint4& w) {
-  auto f = [](uint32_t v) -> int {
-    if (T == 0) return (int)(v & 0x11111111u);
-    if (T == 1) return (int)(v & 0x22222222u);
-    if (T == 2) return (int)((v >> 1) & 0x22222222u);
-    return (int)((v >> 3) & 0x11111111u);
-  };
-  return (v8i){f(w.x), f(w.y), f(w.z), f(w.w), 0, 0, 0, 0};
-}
-
 // 6 dwords of 32 fp6 fields, every field = code
 __device__ __forceinline__ void fill_code(uint32_t (&dw)[kImgDw], uint32_t code) {
 #pragma unroll
@@ -132,16 +112,14 @@ __device__ __forceinline__ void fill_code(uint32_t (&dw)[kImgDw], uint32_t code)
   }
 }
 
-// digit row: field x = digit `dig` of vals[x], shifted left by SH (code 2d)
-template <int SH>
-__device__ __forceinline__ void deposit_digits(uint32_t (&dw)[kImgDw], const int (&vals)[32],
-                                               int dig) {
+// digit row: field x = digit `dig` of vals[x] (code d, value d/8)
+__device__ __forceinline__ void deposit_digits(uint32_t (&dw)[kImgDw], const int (&vals)[32], int dig) {
 #pragma unroll
   for (int d = 0; d < kImgDw; ++d) dw[d] = 0;
 #pragma unroll
   for (int x = 0; x < 32; ++x) {
     const uint32_t f = __builtin_amdgcn_ubfe((uint32_t)vals[x], 3 * dig, 3);
-    const int bit = 6 * x + SH;
+    const int bit = 6 * x;
     dw[bit >> 5] |= f << (bit & 31);
     if ((bit & 31) > 29) dw[(bit >> 5) + 1] |= f >> (32 - (bit & 31));
   }
@@ -161,7 +139,6 @@ __global__ __launch_bounds__(256) void k_gemv(Args A) {
   const uint4* planes = si == 2 ? A.seg[2].planes : si == 1 ? A.seg[1].planes : A.seg[0].planes;
   const uint16_t* gsc = si == 2 ? A.seg[2].g : si == 1 ? A.seg[1].g : A.seg[0].g;
   const uint16_t* hsc = si == 2 ? A.seg[2].h : si == 1 ? A.seg[1].h : A.seg[0].h;
-  void* yout = si == 2 ? A.seg[2].y : si == 1 ? A.seg[1].y : A.seg[0].y;
   double* part = si == 2 ? A.seg[2].part : si == 1 ? A.seg[1].part : A.seg[0].part;
   const int out = si == 2 ? A.seg[2].out : si == 1 ? A.seg[1].out : A.seg[0].out;
   const int RG = si == 2 ? A.seg[2].RG : si == 1 ? A.seg[1].RG : A.seg[0].RG;
@@ -191,7 +168,7 @@ __global__ __launch_bounds__(256) void k_gemv(Args A) {
 
   __shared__ __align__(16) uint32_t s_img[NBP * kPairDwords];
   __shared__ __align__(16) int s_v[2][2][kChunk];     // [hb][p][t*128 + g*32 + x] = v + kOff
-  __shared__ double s_max[4][2][2];     // per wave [hb][p]
+  __shared__ int s_ex[4][2][2];         // per wave [hb][p]
   __shared__ int s_sum[4][2][2];
   __shared__ int s_sh[NBP][2][2];
   __shared__ int s_U[NBP][2][2];
@@ -215,6 +192,17 @@ __global__ __launch_bounds__(256) void k_gemv(Args A) {
         xv[q][hb][k] = A.x[(size_t)min(b, batch - 1) * in + cc];
       }
   }
+  // RMSNorm input: the kStatParts partial sums of x^2 of each batch row
+  double stp[NBP][2][kStatParts];
+  if (A.norm) {
+#pragma unroll
+    for (int q = 0; q < NBP; ++q)
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+        for (int i = 0; i < kStatParts; ++i)
+          stp[q][hb][i] = A.stats[(size_t)min(2 * (bp0 + q) + hb, batch - 1) * kStatParts + i];
+  }
   // the first round's weights are issued after x and h: waiting for those
   // (loads complete in order) then does not wait for the weights
   uint4 w0[8], w1[8];
@@ -222,6 +210,20 @@ __global__ __launch_bounds__(256) void k_gemv(Args A) {
   __builtin_amdgcn_sched_barrier(0);
   load_round(w0, g0, 0);
   __builtin_amdgcn_sched_barrier(0);  // keep every load above the first use of x and h
+  if (A.norm) {
+    // x <- bf16(x / sqrt(mean(x^2) + eps)), the partial sums added in order
+#pragma unroll
+    for (int q = 0; q < NBP; ++q)
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        double ss = 0.0;
+#pragma unroll
+        for (int i = 0; i < kStatParts; ++i) ss += stp[q][hb][i];
+        const double den = sqrt(ss / (double)in + (double)A.eps);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) xv[q][hb][k] = f64_to_bf16_rne_fast((double)bf16_bits_to_f32(xv[q][hb][k]) / den);
+      }
+  }
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const bool ok = col0 + tid + 256 * k < in;
@@ -236,33 +238,41 @@ __global__ __launch_bounds__(256) void k_gemv(Args A) {
 
 #pragma unroll
   for (int q = 0; q < NBP; ++q) {
+    // which rows of this pair exist (uniform); absent rows get zero operands
+    const bool live0 = 2 * (bp0 + q) < batch, live1 = 2 * (bp0 + q) + 1 < batch;
+    // range exponent: the largest binary exponent of a nonzero |u| (frexp:
+    // |u| = f 2^e, f in [1/2, 1)), so that max |u| 2^sh lies in [2^18, 2^19)
     double u[2][2][2];
-    double mx[2][2];
+    int ex[2][2];
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
-        mx[hb][p] = 0.0;
+        ex[hb][p] = kNoExp;
+        if (hb == 1 && !live1) continue;
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
           u[hb][p][k] = (double)f16_bits_to_f32(hv[p][k]) * (double)bf16_bits_to_f32(xv[q][hb][k]);
-          mx[hb][p] = fmax(mx[hb][p], fabs(u[hb][p][k]));
+          int e;
+          frexp(u[hb][p][k], &e);
+          ex[hb][p] = max(ex[hb][p], u[hb][p][k] != 0.0 ? e : kNoExp);
         }
-        mx[hb][p] = wave_max(mx[hb][p]);
+        ex[hb][p] = wave_max_i32(ex[hb][p]);
       }
     if (l == 0)
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-        for (int p = 0; p < 2; ++p) s_max[w][hb][p] = mx[hb][p];
+        for (int p = 0; p < 2; ++p) s_ex[w][hb][p] = ex[hb][p];
     __syncthreads();
     int sh[2][2];
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
-        const double M = fmax(fmax(s_max[0][hb][p], s_max[1][hb][p]), fmax(s_max[2][hb][p], s_max[3][hb][p]));
-        sh[hb][p] = M > 0.0 ? kFxTop - ilogb(M) : 0;
+        const int E = max(max(s_ex[0][hb][p], s_ex[1][hb][p]), max(s_ex[2][hb][p], s_ex[3][hb][p]));
+        sh[hb][p] = E == kNoExp ? 0 : kFxTop + 1 - E;
+        if (hb == 1 && !live1) continue;
         int su = 0;
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
@@ -272,7 +282,7 @@ __global__ __launch_bounds__(256) void k_gemv(Args A) {
           const int t = e & 3, g = e >> 7, x = 8 * ((e >> 5) & 3) + ((e >> 2) & 7);
           s_v[hb][p][t * 128 + g * 32 + x] = v + kOff;
         }
-        su = wave_sum(su);
+        su = wave_sum_i32(su);
         if (l == 0) s_sum[w][hb][p] = su;
       }
     __syncthreads();
@@ -280,39 +290,47 @@ __global__ __launch_bounds__(256) void k_gemv(Args A) {
       const int hb = tid >> 1, p = tid & 1;
       // same value as sh[hb][p], selected without indexing a register array
       const int shs = (hb ? (p ? sh[1][1] : sh[1][0]) : (p ? sh[0][1] : sh[0][0]));
+      const bool lv = hb ? live1 : live0;
       s_sh[q][hb][p] = shs;
-      s_U[q][hb][p] = ((s_sum[0][hb][p] + s_sum[1][hb][p]) + s_sum[2][hb][p]) + s_sum[3][hb][p];
+      s_U[q][hb][p] = lv ? ((s_sum[0][hb][p] + s_sum[1][hb][p]) + s_sum[2][hb][p]) + s_sum[3][hb][p] : 0;
     }
-    // image rows: lane L = (8 hb + dr) + 16 g of image (p, t); the slice t is
-    // wave-uniform, so the code shift is a compile-time constant per branch
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int combo = w + 4 * it;  // (p, t)
-      const int p = combo >> 2, t = combo & 3;
-      const int dr = l & 7, hb = (l >> 3) & 1, g = l >> 4;
-      const int L = 8 * hb + dr + 16 * g;
-      const bool live = 2 * (bp0 + q) + hb < batch;
-      uint32_t dw[kImgDw];
-      int vals[32];
-      const int* src = &s_v[hb][p][t * 128 + g * 32];
-#pragma unroll
-      for (int x = 0; x < 32; x += 4) {
-        const int4 v4 = *(const int4*)(src + x);
-        vals[x] = v4.x;
-        vals[x + 1] = v4.y;
-        vals[x + 2] = v4.z;
-        vals[x + 3] = v4.w;
-      }
+    // image rows: wave w builds slice t = w, lane (p, g, dr) the row
+    // L = 8 hb + dr + 16 g of image (p, t) for each batch row hb of the pair
+    {
+      const int t = w, p = l >> 5, g = (l >> 3) & 3, dr = l & 7;
       const bool dbl = (t == 0 || t == 3);  // slices of value 0.5: code 2d
-      if (dbl)
-        deposit_digits<1>(dw, vals, dr);
-      else
-        deposit_digits<0>(dw, vals, dr);
-      if (dr == 7) fill_code(dw, dbl ? 2u : 1u);  // row of ones: set-bit count
-      uint32_t* dst = s_img + q * kPairDwords + (p * 4 + t) * kImgDwords + L * kImgDw;
 #pragma unroll
-      for (int d = 0; d < kImgDw; d += 2)
-        *(uint2*)(dst + d) = make_uint2(live ? dw[d] : 0u, live ? dw[d + 1] : 0u);
+      for (int hb = 0; hb < 2; ++hb) {
+        const bool lv = hb ? live1 : live0;
+        uint32_t* dst = s_img + q * kPairDwords + (p * 4 + t) * kImgDwords + (8 * hb + dr + 16 * g) * kImgDw;
+        if (!lv) {
+#pragma unroll
+          for (int d = 0; d < kImgDw; d += 2) *(uint2*)(dst + d) = make_uint2(0u, 0u);
+          continue;
+        }
+        int vals[32];
+        const int* src = &s_v[hb][p][t * 128 + g * 32];
+#pragma unroll
+        for (int x = 0; x < 32; x += 4) {
+          const int4 v4 = *(const int4*)(src + x);
+          vals[x] = v4.x;
+          vals[x + 1] = v4.y;
+          vals[x + 2] = v4.z;
+          vals[x + 3] = v4.w;
+        }
+        uint32_t dw[kImgDw];
+        deposit_digits(dw, vals, dr);
+        if (dr == 7) fill_code(dw, 1u);  // row of ones: set-bit count
+        if (dbl) {
+          // codes 2d: shift the lane's 192-bit field vector left by one (each
+          // digit sits in the low 3 bits of its 6-bit field, so none crosses)
+#pragma unroll
+          for (int d = kImgDw - 1; d > 0; --d) dw[d] = (dw[d] << 1) | (dw[d - 1] >> 31);
+          dw[0] <<= 1;
+        }
+#pragma unroll
+        for (int d = 0; d < kImgDw; d += 2) *(uint2*)(dst + d) = make_uint2(dw[d], dw[d + 1]);
+      }
     }
     __syncthreads();
   }
@@ -320,18 +338,21 @@ __global__ __launch_bounds__(256) void k_gemv(Args A) {
   // ---- stream the planes -----------------------------------------------------
   // C lane l, reg k = row i = 4 gl + k of the digit operand (digit i % 8 of
   // batch row 2 q + i / 8; i % 8 == 7 is the ones row), column j = row 16 tau + j.
+  // Each accumulator is (1/8) Σ bit·digit (or (1/8) Σ bit for the ones row):
+  // times 8^(k+1) (or -8 kOff) it is an exact integer below 2^31, and the
+  // lane's four terms plus its partner lane's (l + 16) give Σ bit·v exactly.
   const int hbl = gl >> 1;
-  double wdig[4];
+  float wsc[4];
   if (gl & 1) {
-    wdig[0] = 32768.0;
-    wdig[1] = 262144.0;
-    wdig[2] = 2097152.0;
-    wdig[3] = -8.0 * kOff;
+    wsc[0] = 32768.f;
+    wsc[1] = 262144.f;
+    wsc[2] = 2097152.f;
+    wsc[3] = -8.f * kOff;
   } else {
-    wdig[0] = 8.0;
-    wdig[1] = 64.0;
-    wdig[2] = 512.0;
-    wdig[3] = 4096.0;
+    wsc[0] = 8.f;
+    wsc[1] = 64.f;
+    wsc[2] = 512.f;
+    wsc[3] = 4096.f;
   }
 
   // this lane's row of image (pair q, path/slice ps)
@@ -361,14 +382,19 @@ __global__ __launch_bounds__(256) void k_gemv(Args A) {
       for (int q = 0; q < NBP; ++q)
 #pragma unroll
         for (int tau = 0; tau < 4; ++tau) acc[q][tau] = (v4f){0.f, 0.f, 0.f, 0.f};
+      // slice T of a stored word (see the header comment)
       auto slice_step = [&](auto tc) {
         constexpr int T = decltype(tc)::value;
+        constexpr int sT = T == 2 ? 1 : (T == 3 ? 3 : 0);
+        constexpr uint32_t mT = (T == 1 || T == 2) ? 0x22222222u : 0x11111111u;
         v8i a[NBP];
 #pragma unroll
         for (int q = 0; q < NBP; ++q) a[q] = NBP == 1 ? areg[p * 4 + T] : image_row(q, p * 4 + T);
 #pragma unroll
         for (int tau = 0; tau < 4; ++tau) {
-          const v8i bv = slice4<T>(wt[tau * 2 + p]);
+          const uint4 wv = wt[tau * 2 + p];
+          const v8i bv = (v8i){(int)((wv.x >> sT) & mT), (int)((wv.y >> sT) & mT),
+                               (int)((wv.z >> sT) & mT), (int)((wv.w >> sT) & mT), 0, 0, 0, 0};
 #pragma unroll
           for (int q = 0; q < NBP; ++q)
             acc[q][tau] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
@@ -383,14 +409,14 @@ __global__ __launch_bounds__(256) void k_gemv(Args A) {
 #pragma unroll
       for (int q = 0; q < NBP; ++q) {
         const int shv = s_sh[q][hbl][p];
-        const double U = (double)s_U[q][hbl][p];
+        const int U = s_U[q][hbl][p];
 #pragma unroll
         for (int tau = 0; tau < 4; ++tau) {
           const v4f c = acc[q][tau];
-          double v = wdig[0] * c[0] + wdig[1] * c[1] + wdig[2] * c[2] + wdig[3] * c[3];
-          v += __shfl_down(v, 16, 64);  // digits 4..6 and the count term
+          int mv = (int)(c[0] * wsc[0]) + (int)(c[1] * wsc[1]) + (int)(c[2] * wsc[2]) + (int)(c[3] * wsc[3]);
+          mv += __shfl_down(mv, 16, 64);  // digits 4..6 and the count term
           const double gp = (double)f16_bits_to_f32(gt[tau * 2 + p]);
-          res[q][tau] += gp * ldexp(U - 2.0 * v, -shv);
+          res[q][tau] += gp * ldexp((double)(U - 2 * mv), -shv);
         }
       }
     }
@@ -404,14 +430,7 @@ __global__ __launch_bounds__(256) void k_gemv(Args A) {
         for (int tau = 0; tau < 4; ++tau) {
           const int row = rg * 64 + 16 * tau + j;
           if (row >= out) continue;
-          if (A.direct) {
-            if (A.y_dtype == RABIT_OUT_F32)
-              ((float*)yout)[(size_t)b * out + row] = (float)res[q][tau];
-            else
-              ((uint16_t*)yout)[(size_t)b * out + row] = f64_to_bf16_rne(res[q][tau]);
-          } else {
             part[((size_t)b * A.S + r) * RG * 64 + row] = res[q][tau];
-          }
         }
       }
     }
@@ -458,12 +477,11 @@ hipError_t launch_main(const Plan& P, const Args& A, int batch, hipStream_t st) 
 }
 
 Args make_args(const Plan& P, const uint4* planes, const uint16_t* g, const uint16_t* h, int out,
-               int in, const uint16_t* x, int batch, void* y, int y_dtype, void* ws, bool direct) {
+               int in, const uint16_t* x, int batch, void* ws) {
   Args A = {};
   A.seg[0].planes = planes;
   A.seg[0].g = g;
   A.seg[0].h = h;
-  A.seg[0].y = y;
   A.seg[0].part = (double*)ws;
   A.seg[0].out = out;
   A.seg[0].RG = row_groups(out);
@@ -475,8 +493,9 @@ Args make_args(const Plan& P, const uint4* planes, const uint16_t* g, const uint
   A.S = P.S;
   A.m = P.m;
   A.batch = batch;
-  A.y_dtype = y_dtype;
-  A.direct = direct ? 1 : 0;
+  A.norm = 0;
+  A.stats = nullptr;
+  A.eps = 0.f;
   return A;
 }
 
@@ -490,7 +509,7 @@ size_t gemv_workspace_bytes(int out, int in, int batch) {
 hipError_t launch_gemv_partial(const uint4* planes, const uint16_t* g, const uint16_t* h, int out,
                                int in, const uint16_t* x, int batch, void* ws, hipStream_t st) {
   const Plan P = make_plan(&out, 1, in, batch);
-  const Args A = make_args(P, planes, g, h, out, in, x, batch, nullptr, RABIT_OUT_F32, ws, false);
+  const Args A = make_args(P, planes, g, h, out, in, x, batch, ws);
   return launch_main(P, A, batch, st);
 }
 
@@ -502,14 +521,44 @@ hipError_t launch_gemv_reduce(int out, int in, int batch, void* y, int y_dtype, 
   return hipGetLastError();
 }
 
+size_t gemv_part_bytes(int out, int in, int batch) {
+  return part_bytes(out, (in + kChunk - 1) / kChunk, batch);
+}
+
+hipError_t launch_gemv_multi(const LinSeg* segs, int nseg, int in, const uint16_t* x, int batch,
+                             const double* stats, float eps, hipStream_t st) {
+  if (nseg < 1 || nseg > kMaxSeg) return hipErrorInvalidValue;
+  int outs[kMaxSeg];
+  for (int s = 0; s < nseg; ++s) outs[s] = segs[s].out;
+  const Plan P = make_plan(outs, nseg, in, batch);
+  Args A = {};
+  int rb0 = 0;
+  for (int s = 0; s < nseg; ++s) {
+    A.seg[s].planes = segs[s].planes;
+    A.seg[s].g = segs[s].g;
+    A.seg[s].h = segs[s].h;
+    A.seg[s].part = segs[s].part;
+    A.seg[s].out = segs[s].out;
+    A.seg[s].RG = row_groups(segs[s].out);
+    A.seg[s].rb0 = rb0;
+    rb0 += P.RB[s];
+  }
+  A.x = x;
+  A.stats = stats;
+  A.nseg = nseg;
+  A.in = in;
+  A.KG = P.KG;
+  A.S = P.S;
+  A.m = P.m;
+  A.batch = batch;
+  A.norm = stats ? 1 : 0;
+  A.eps = eps;
+  return launch_main(P, A, batch, st);
+}
+
 hipError_t launch_gemv(const uint4* planes, const uint16_t* g, const uint16_t* h, int out, int in,
                        const uint16_t* x, int batch, void* y, int y_dtype, void* ws,
                        hipStream_t st) {
-  const Plan P = make_plan(&out, 1, in, batch);
-  if (P.S == 1) {
-    const Args A = make_args(P, planes, g, h, out, in, x, batch, y, y_dtype, ws, true);
-    return launch_main(P, A, batch, st);
-  }
   hipError_t e = launch_gemv_partial(planes, g, h, out, in, x, batch, ws, st);
   if (e != hipSuccess) return e;
   return launch_gemv_reduce(out, in, batch, y, y_dtype, ws, st);

@@ -208,6 +208,9 @@ namespace {
 struct DecodeWs {
   uint16_t *xa, *xb, *n, *attn, *z;
   float *q, *k, *v, *o, *gate, *up, *down;
+  // GEMV path (batch <= RABIT_MAX_GEMV_BATCH): partials and row statistics
+  double *stats, *pq, *pk, *pv, *po, *pg, *pu, *pd;
+  float* qk;
   void* lin;
   size_t lin_bytes;
 };
@@ -245,25 +248,80 @@ size_t lin_ws(const rabit_decoder_cfg* c, int batch) {
 size_t decode_ws(const rabit_decoder_cfg* c, int batch, DecodeWs* w, void* base) {
   const int H = c->hidden, F = c->ffn;
   const int kv = c->mlp_only ? 0 : c->n_kv_heads * c->head_dim;
-  const size_t sz[12] = {a256((size_t)batch * H * 2), a256((size_t)batch * H * 2),
-                         a256((size_t)batch * H * 2), a256((size_t)batch * H * 2),
-                         a256((size_t)batch * F * 2), a256((size_t)batch * H * 4),
-                         a256((size_t)batch * std::max(kv, 1) * 4),
-                         a256((size_t)batch * std::max(kv, 1) * 4), a256((size_t)batch * H * 4),
-                         a256((size_t)batch * F * 4), a256((size_t)batch * F * 4),
-                         a256((size_t)batch * H * 4)};
+  const int kv1 = std::max(kv, 1);
+  const bool gv = batch <= RABIT_MAX_GEMV_BATCH;
   size_t off = 0;
   char* p = (char*)base;
-  void** slots[12] = {(void**)&w->xa,   (void**)&w->xb, (void**)&w->n,    (void**)&w->attn,
-                      (void**)&w->z,    (void**)&w->q,  (void**)&w->k,    (void**)&w->v,
-                      (void**)&w->o,    (void**)&w->gate, (void**)&w->up, (void**)&w->down};
-  for (int i = 0; i < 12; ++i) {
-    if (base) *slots[i] = p + off;
-    off += sz[i];
-  }
-  w->lin = base ? p + off : nullptr;
-  w->lin_bytes = lin_ws(c, batch);
+  auto take = [&](void** slot, size_t bytes) {
+    *slot = (base && bytes) ? (void*)(p + off) : nullptr;
+    off += a256(bytes);
+  };
+  take((void**)&w->xa, (size_t)batch * H * 2);
+  take((void**)&w->xb, (size_t)batch * H * 2);
+  take((void**)&w->attn, (size_t)batch * H * 2);
+  take((void**)&w->z, (size_t)batch * F * 2);
+  // GEMM path: normalised input and fp32 outputs of every linear layer
+  take((void**)&w->n, gv ? 0 : (size_t)batch * H * 2);
+  take((void**)&w->q, gv ? 0 : (size_t)batch * H * 4);
+  take((void**)&w->k, gv ? 0 : (size_t)batch * kv1 * 4);
+  take((void**)&w->v, gv ? 0 : (size_t)batch * kv1 * 4);
+  take((void**)&w->o, gv ? 0 : (size_t)batch * H * 4);
+  take((void**)&w->gate, gv ? 0 : (size_t)batch * F * 4);
+  take((void**)&w->up, gv ? 0 : (size_t)batch * F * 4);
+  take((void**)&w->down, gv ? 0 : (size_t)batch * H * 4);
+  // GEMV path: x^2 partial sums, q/k outputs and the per-range partials
+  take((void**)&w->stats, gv ? (size_t)batch * RABIT_STAT_PARTS * 8 : 0);
+  take((void**)&w->qk, gv ? (size_t)batch * (H + kv1) * 4 : 0);
+  take((void**)&w->pq, gv && kv ? gemv_part_bytes(H, H, batch) : 0);
+  take((void**)&w->pk, gv && kv ? gemv_part_bytes(kv, H, batch) : 0);
+  take((void**)&w->pv, gv && kv ? gemv_part_bytes(kv, H, batch) : 0);
+  take((void**)&w->po, gv && kv ? gemv_part_bytes(H, H, batch) : 0);
+  take((void**)&w->pg, gv ? gemv_part_bytes(F, H, batch) : 0);
+  take((void**)&w->pu, gv ? gemv_part_bytes(F, H, batch) : 0);
+  take((void**)&w->pd, gv ? gemv_part_bytes(H, F, batch) : 0);
+  w->lin_bytes = gv ? 0 : lin_ws(c, batch);
+  w->lin = (base && w->lin_bytes) ? p + off : nullptr;
   return off + w->lin_bytes;
+}
+
+LinSeg seg_of(const rabit_layer& L, double* part) {
+  return LinSeg{(const uint4*)L.planes, L.g, L.h, L.out_features, part};
+}
+
+// One decode step at batch <= RABIT_MAX_GEMV_BATCH. Per layer: [q,k,v] GEMV
+// on RMSNorm(x) -> q/k/v sums + attention -> o GEMV -> x + o and its x^2
+// sums -> [gate,up] GEMV on RMSNorm -> SiLU(gate)*up -> down GEMV -> x + down
+// and its x^2 sums: 8 launches (4 without attention), plus one for the
+// statistics of the step input.
+hipError_t decode_gemv_path(const rabit_decoder_cfg* cfg, const rabit_layer* layers,
+                            const uint16_t* x, int batch, uint16_t* out, const DecodeWs& w,
+                            hipStream_t st) {
+  const int H = cfg->hidden, F = cfg->ffn;
+  hipError_t e = launch_resid_stats(nullptr, 0, x, nullptr, w.stats, batch, H, st);
+  const uint16_t* cur = x;
+  for (int l = 0; l < cfg->n_layers && e == hipSuccess; ++l) {
+    const rabit_layer* Ls = layers + l * 7;
+    uint16_t* nxt = (l == cfg->n_layers - 1) ? out : (cur == w.xa ? w.xb : w.xa);
+    if (!cfg->mlp_only) {
+      const LinSeg qkv[3] = {seg_of(Ls[0], w.pq), seg_of(Ls[1], w.pk), seg_of(Ls[2], w.pv)};
+      if (!e) e = launch_gemv_multi(qkv, 3, H, cur, batch, w.stats, cfg->rms_eps, st);
+      if (!e) e = launch_reduce_attn(w.pq, w.pk, w.pv, H, w.qk, w.attn, batch, cfg->n_heads,
+                                     cfg->n_kv_heads, cfg->head_dim, st);
+      const LinSeg o = seg_of(Ls[3], w.po);
+      if (!e) e = launch_gemv_multi(&o, 1, H, w.attn, batch, nullptr, 0.f, st);
+      if (!e) e = launch_resid_stats(w.po, H, cur, nxt, w.stats, batch, H, st);
+      cur = nxt;
+    }
+    const LinSeg gu[2] = {seg_of(Ls[4], w.pg), seg_of(Ls[5], w.pu)};
+    if (!e) e = launch_gemv_multi(gu, 2, H, cur, batch, w.stats, cfg->rms_eps, st);
+    if (!e) e = launch_reduce_silu(w.pg, w.pu, H, w.z, batch, F, st);
+    const LinSeg dn = seg_of(Ls[6], w.pd);
+    if (!e) e = launch_gemv_multi(&dn, 1, F, w.z, batch, nullptr, 0.f, st);
+    // x + down may be written in place (cur == nxt when attention ran)
+    if (!e) e = launch_resid_stats(w.pd, F, cur, nxt, w.stats, batch, H, st);
+    cur = nxt;
+  }
+  return e;
 }
 
 hipError_t linear(const rabit_layer& L, const uint16_t* x, int batch, float* y, const DecodeWs& w,
@@ -309,6 +367,8 @@ int rabit_decode_step(const rabit_decoder_cfg* cfg, const rabit_layer* layers, c
   if (!aligned16(workspace)) return RABIT_EALIGN;
   decode_ws(cfg, batch, &w, workspace);
   hipStream_t st = (hipStream_t)stream;
+  if (batch <= RABIT_MAX_GEMV_BATCH)
+    return dev_status(decode_gemv_path(cfg, layers, x, batch, out, w, st));
   hipError_t e = hipSuccess;
   const uint16_t* cur = x;
   for (int l = 0; l < cfg->n_layers && e == hipSuccess; ++l) {

@@ -18,6 +18,66 @@ __device__ __forceinline__ uint4 load_nt(const uint4* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Wave-wide reductions with DPP row operations (no LDS round trips): xor 1,
+// xor 2, half-row mirror, row mirror, then the row broadcasts 15 and 31; the
+// result is in lane 63 and is returned to every lane. The combination order
+// is fixed, so every workgroup computing the same reduction gets the same bits.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_i32(int v, int ident) {
+  return __builtin_amdgcn_update_dpp(ident, v, CTRL, ROWS, 0xf, false);
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double dpp_f64(double v, double ident) {
+  const long long b = __double_as_longlong(v), o = __double_as_longlong(ident);
+  const int lo = __builtin_amdgcn_update_dpp((int)o, (int)b, CTRL, ROWS, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp((int)(o >> 32), (int)(b >> 32), CTRL, ROWS, 0xf, false);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+__device__ __forceinline__ double lane63_f64(double v) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane((int)b, 63), hi = __builtin_amdgcn_readlane((int)(b >> 32), 63);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+__device__ __forceinline__ double wave_max_f64(double v) {
+  const double z = 0.0;  // identity: only non-negative values are reduced
+  v = fmax(v, dpp_f64<0xB1, 0xf>(v, z));
+  v = fmax(v, dpp_f64<0x4E, 0xf>(v, z));
+  v = fmax(v, dpp_f64<0x141, 0xf>(v, z));
+  v = fmax(v, dpp_f64<0x140, 0xf>(v, z));
+  v = fmax(v, dpp_f64<0x142, 0xa>(v, z));
+  v = fmax(v, dpp_f64<0x143, 0xc>(v, z));
+  return lane63_f64(v);
+}
+__device__ __forceinline__ int wave_max_i32(int v) {
+  const int lo = -2147483647 - 1;
+  v = max(v, dpp_i32<0xB1, 0xf>(v, lo));
+  v = max(v, dpp_i32<0x4E, 0xf>(v, lo));
+  v = max(v, dpp_i32<0x141, 0xf>(v, lo));
+  v = max(v, dpp_i32<0x140, 0xf>(v, lo));
+  v = max(v, dpp_i32<0x142, 0xa>(v, lo));
+  v = max(v, dpp_i32<0x143, 0xc>(v, lo));
+  return __builtin_amdgcn_readlane(v, 63);
+}
+__device__ __forceinline__ int wave_sum_i32(int v) {
+  v += dpp_i32<0xB1, 0xf>(v, 0);
+  v += dpp_i32<0x4E, 0xf>(v, 0);
+  v += dpp_i32<0x141, 0xf>(v, 0);
+  v += dpp_i32<0x140, 0xf>(v, 0);
+  v += dpp_i32<0x142, 0xa>(v, 0);
+  v += dpp_i32<0x143, 0xc>(v, 0);
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  v += dpp_f64<0xB1, 0xf>(v, 0.0);
+  v += dpp_f64<0x4E, 0xf>(v, 0.0);
+  v += dpp_f64<0x141, 0xf>(v, 0.0);
+  v += dpp_f64<0x140, 0xf>(v, 0.0);
+  v += dpp_f64<0x142, 0xa>(v, 0.0);
+  v += dpp_f64<0x143, 0xc>(v, 0.0);
+  return lane63_f64(v);
+}
+
 // ---------------------------------------------------------------------------
 // Format helpers (device)
 // ---------------------------------------------------------------------------
@@ -64,6 +124,27 @@ __device__ __forceinline__ uint16_t f64_to_f16_rne(double d) {
 __device__ __forceinline__ uint16_t f64_to_bf16_rne(double d) {
   return f64_to_small_rne<7, 127, -126, 127, 0x7FC0>(d);
 }
+// out of line: the rare general case stays out of the hot instruction stream
+static __device__ __attribute__((noinline)) uint16_t f64_to_bf16_rne_slow(double d) {
+  return f64_to_bf16_rne(d);
+}
+
+// Same result as f64_to_bf16_rne, with a short branch-free path for values
+// whose bfloat16 rounding lies in the normal range (float64 binades -126 ..
+// 127): the exponent is rebiased and the 52-bit mantissa rounded half to even
+// at bit 45; a carry out of the mantissa moves into the exponent (up to the
+// infinity pattern). Everything else takes the general conversion.
+__device__ __forceinline__ uint16_t f64_to_bf16_rne_fast(double d) {
+  const uint64_t b = (uint64_t)__double_as_longlong(d);
+  const uint32_t e = (uint32_t)(b >> 52) & 0x7FFu;
+  if (e >= 897u && e <= 1150u) {
+    const uint64_t r = (b & 0x7FFFFFFFFFFFFFFFull) - ((uint64_t)896 << 52);
+    const uint64_t q = (r + 0x1FFFFFFFFFFFull + ((r >> 45) & 1)) >> 45;
+    return (uint16_t)(((b >> 63) << 15) | q);
+  }
+  return f64_to_bf16_rne_slow(d);
+}
+
 // float32 -> bfloat16, round to nearest even (NaN kept quiet)
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
@@ -97,6 +178,22 @@ hipError_t launch_gemv_partial(const uint4* planes, const uint16_t* g, const uin
 hipError_t launch_gemv_reduce(int out, int in, int batch, void* y, int y_dtype, const void* ws,
                               hipStream_t st);
 
+// Several matrices that read the same input in one launch (q/k/v, gate/up):
+// each leaves float64 partials [batch][ceil(in/512)][64*ceil(out/64)] in part.
+// With stats != nullptr the input is RMSNorm(x) (unit weight, eps), rounded to
+// bfloat16, with stats[b][RABIT_STAT_PARTS] the partial sums of x^2 of row b.
+struct LinSeg {
+  const uint4* planes;
+  const uint16_t* g;
+  const uint16_t* h;
+  int out;
+  double* part;
+};
+#define RABIT_STAT_PARTS 8
+size_t gemv_part_bytes(int out, int in, int batch);
+hipError_t launch_gemv_multi(const LinSeg* segs, int nseg, int in, const uint16_t* x, int batch,
+                             const double* stats, float eps, hipStream_t st);
+
 size_t gemm_workspace_bytes(int out, int in, int m);
 hipError_t launch_gemm(const uint4* planes, const uint16_t* g, const uint16_t* h, int out, int in,
                        const uint16_t* X, int m, void* Y, int y_dtype, void* ws, hipStream_t st);
@@ -109,6 +206,19 @@ hipError_t launch_silu_mul(const float* gate, const float* up, uint16_t* z, int 
                            hipStream_t st);
 hipError_t launch_residual_add(const uint16_t* x, const float* d, uint16_t* out, int batch, int n,
                                hipStream_t st);
+// fused consumers of GEMV partials (S = ceil(in/512) ranges, row stride 64*ceil(out/64))
+// x_out = bf16(x + Σ part) (part == nullptr: x_out unused, x itself), and the
+// RABIT_STAT_PARTS partial sums of x_out^2 per row
+hipError_t launch_resid_stats(const double* part, int in_of_part, const uint16_t* x, uint16_t* x_out,
+                              double* stats, int batch, int n, hipStream_t st);
+// a = bf16(silu(Σ gate part) * Σ up part)
+hipError_t launch_reduce_silu(const double* pg, const double* pu, int in_of_part, uint16_t* a,
+                              int batch, int n, hipStream_t st);
+// q, k: fp32 sums (kept in qk); v = bf16(Σ part); attention over a one-token
+// context returns, per head, its key/value group's v
+hipError_t launch_reduce_attn(const double* pq, const double* pk, const double* pv,
+                              int in_of_part, float* qk, uint16_t* attn, int batch, int n_heads,
+                              int n_kv_heads, int head_dim, hipStream_t st);
 hipError_t launch_test_f64_to_16(const double* in, uint16_t* out, int n, int bf16, hipStream_t st);
 
 }  // namespace rabit

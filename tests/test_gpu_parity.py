@@ -312,7 +312,17 @@ def test_decode_mlp_block(gpu_lib):
     assert ok
 
 
-@pytest.mark.parametrize("batch", [1, 4, 20])
+def test_decode_llama7b_mlp_block(gpu_lib):
+    # the benchmarked workload: one Llama-2-7B-shaped MLP block at batch 1
+    say("decode llama-2-7b mlp block")
+    cfg = gpu_lib.DecoderCfg(hidden=4096, ffn=11008, n_layers=1, mlp_only=True)
+    y, ref = _decode_case(gpu_lib, cfg, True, 1, 700)
+    ok, nbad = bf16_close(y, ref)
+    say("  normwise err", oracle.normwise_rel_err(y, ref), "elements outside bound", nbad)
+    assert ok
+
+
+@pytest.mark.parametrize("batch", [1, 2, 4, 20])
 def test_decode_attention_block(gpu_lib, batch):
     say("decode attention block batch", batch)
     cfg = gpu_lib.DecoderCfg(hidden=512, ffn=1376, n_heads=8, n_kv_heads=2, head_dim=64, n_layers=2)
