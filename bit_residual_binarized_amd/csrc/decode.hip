@@ -72,7 +72,14 @@ __device__ __forceinline__ double sum_ranges(const double* __restrict__ part, in
                                              int stride, int i) {
   const double* pp = part + (size_t)b * S * stride + i;
   double v = 0.0;
-  for (int r = 0; r < S; ++r) v += pp[(size_t)r * stride];
+  // eight loads in flight at a time (clamped index, masked), added in order
+  for (int r = 0; r < S; r += 8) {
+    double t[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) t[u] = pp[(size_t)min(r + u, S - 1) * stride];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v += r + u < S ? t[u] : 0.0;
+  }
   return v;
 }
 
@@ -84,7 +91,7 @@ __global__ __launch_bounds__(256) void k_resid_stats(const double* __restrict__ 
                                                      double* __restrict__ stats, int n) {
   const int i = blockIdx.x, b = blockIdx.y;
   const int span = (n + RABIT_STAT_PARTS - 1) / RABIT_STAT_PARTS;
-  const int e0 = i * span, e1 = min(n, e0 + span);
+  const int e0 = min(n, i * span), e1 = min(n, e0 + span);
   const int stride = 64 * ((n + 63) / 64);
   double ss = 0.0;
   for (int e = e0 + (int)threadIdx.x; e < e1; e += 256) {

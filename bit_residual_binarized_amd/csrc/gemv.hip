@@ -13,14 +13,19 @@
 //    largest |u| maps into [2^18, 2^19); v + 2^20 is written in 7 base-8
 //    digits 0..7.
 //  * A stored word w (32 columns of one row, bit t of nibble e = column
-//    4e + t) gives four fp4 slices: w & 0x1..1 (value 0.5 per set bit),
-//    w & 0x2..2 (1.0), (w >> 1) & 0x2..2 (1.0), (w >> 3) & 0x1..1 (0.5).
-//  * V_MFMA_SCALE_F32_16X16X128_F8F6F4 (unit scales) multiplies one slice
-//    (16 rows x 128 columns, fp4) by an fp6 e2m3 operand whose rows are the
-//    digits, coded so that every product is digit/8 (fp6 codes d or 2d are
-//    exact and linear below 16). One extra row of ones yields the set-bit
-//    count. Every product and fp32 partial sum is an exact multiple of 1/8
-//    below 2^11, so Σ bit·v is recovered exactly as an integer.
+//    4e + t) gives four fp4 slices with one VALU op each: w & 0x1..1 (value
+//    0.5 per set bit), w & 0x2..2 (1.0), w & 0x4..4 (2.0) and
+//    (w & 0x8..8) | 0x1..1 (+0.5 for a clear bit, -0.5 for a set one).
+//  * V_MFMA_SCALE_F32_16X16X128_F8F6F4 multiplies one slice (16 rows x 128
+//    columns, fp4) by an fp6 e2m3 operand whose rows are the digits: codes
+//    2d, d, d and -d (values d/4, d/8, d/8, -d/8; e2m3 codes below 16 are
+//    linear), with the per-row E8M0 operand scale 2^(3 (digit + 1)) (halved
+//    for the 2.0 slice), so a set bit in column j adds 8^k d_k(j) to row k.
+//    The fourth slice's constant part (-d/16 per column) is removed exactly
+//    by starting the accumulators from one product against all -0.5. One
+//    extra row of ones yields the set-bit count. Every fp32 partial sum is an
+//    exact multiple of a power of two with few significant bits, so Σ bit·v
+//    is recovered exactly as an integer.
 //  * Each workgroup builds the digit operand of its own range in LDS from x
 //    and h (no separate activation pass), then its 4 waves stream 64-row
 //    groups of planes through the matrix cores (one 8 KiB slab per wave and
@@ -192,16 +197,15 @@ __global__ __launch_bounds__(256) void k_gemv(Args A) {
         xv[q][hb][k] = A.x[(size_t)min(b, batch - 1) * in + cc];
       }
   }
-  // RMSNorm input: the kStatParts partial sums of x^2 of each batch row
-  double stp[NBP][2][kStatParts];
+  // RMSNorm input: lane l < kStatParts holds partial sum l of x^2 of each
+  // batch row (added by a fixed DPP tree below)
+  double stp[NBP][2];
   if (A.norm) {
 #pragma unroll
     for (int q = 0; q < NBP; ++q)
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-        for (int i = 0; i < kStatParts; ++i)
-          stp[q][hb][i] = A.stats[(size_t)min(2 * (bp0 + q) + hb, batch - 1) * kStatParts + i];
+        stp[q][hb] = A.stats[(size_t)min(2 * (bp0 + q) + hb, batch - 1) * kStatParts + (l & (kStatParts - 1))];
   }
   // the first round's weights are issued after x and h: waiting for those
   // (loads complete in order) then does not wait for the weights
@@ -216,9 +220,7 @@ __global__ __launch_bounds__(256) void k_gemv(Args A) {
     for (int q = 0; q < NBP; ++q)
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) {
-        double ss = 0.0;
-#pragma unroll
-        for (int i = 0; i < kStatParts; ++i) ss += stp[q][hb][i];
+        const double ss = wave_sum_f64(l < kStatParts ? stp[q][hb] : 0.0);
         const double den = sqrt(ss / (double)in + (double)A.eps);
 #pragma unroll
         for (int k = 0; k < 2; ++k) xv[q][hb][k] = f64_to_bf16_rne_fast((double)bf16_bits_to_f32(xv[q][hb][k]) / den);
@@ -298,7 +300,7 @@ __global__ __launch_bounds__(256) void k_gemv(Args A) {
     // L = 8 hb + dr + 16 g of image (p, t) for each batch row hb of the pair
     {
       const int t = w, p = l >> 5, g = (l >> 3) & 3, dr = l & 7;
-      const bool dbl = (t == 0 || t == 3);  // slices of value 0.5: code 2d
+      const bool dbl = t == 0;  // slice of value 0.5: code 2d
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) {
         const bool lv = hb ? live1 : live0;
@@ -327,6 +329,12 @@ __global__ __launch_bounds__(256) void k_gemv(Args A) {
 #pragma unroll
           for (int d = kImgDw - 1; d > 0; --d) dw[d] = (dw[d] << 1) | (dw[d - 1] >> 31);
           dw[0] <<= 1;
+        } else if (t == 3) {
+          // sign bit in every field: values -d/8 against the +-0.5 slice
+          uint32_t sg[kImgDw];
+          fill_code(sg, 32u);
+#pragma unroll
+          for (int d = 0; d < kImgDw; ++d) dw[d] |= sg[d];
         }
 #pragma unroll
         for (int d = 0; d < kImgDw; d += 2) *(uint2*)(dst + d) = make_uint2(dw[d], dw[d + 1]);
@@ -338,23 +346,17 @@ __global__ __launch_bounds__(256) void k_gemv(Args A) {
   // ---- stream the planes -----------------------------------------------------
   // C lane l, reg k = row i = 4 gl + k of the digit operand (digit i % 8 of
   // batch row 2 q + i / 8; i % 8 == 7 is the ones row), column j = row 16 tau + j.
-  // Each accumulator is (1/8) Σ bit·digit (or (1/8) Σ bit for the ones row):
-  // times 8^(k+1) (or -8 kOff) it is an exact integer below 2^31, and the
-  // lane's four terms plus its partner lane's (l + 16) give Σ bit·v exactly.
+  // Row i of the digit operand carries the E8M0 scale 2^(3 (i % 8 + 1)) for
+  // digit rows (lane i + 16 g supplies the scale of row i, K block g) and
+  // 2^0 for the ones row, so accumulator rows are 8^d D_d (D_d = Σ bit·digit_d,
+  // an integer) and P/8 (P = set-bit count). In fp32, exactly: lanes gl even
+  // hold digits 0..3 (sum below 2^22), lanes gl odd digits 4..6 and the count
+  // term -kOff P (multiples of 4096 in (-2^30, 2^30)); with the partner lane
+  // (l + 16) they give Σ bit·v exactly.
   const int hbl = gl >> 1;
-  float wsc[4];
-  if (gl & 1) {
-    wsc[0] = 32768.f;
-    wsc[1] = 262144.f;
-    wsc[2] = 2097152.f;
-    wsc[3] = -8.f * kOff;
-  } else {
-    wsc[0] = 8.f;
-    wsc[1] = 64.f;
-    wsc[2] = 512.f;
-    wsc[3] = 4096.f;
-  }
-
+  const int arow = l & 7;  // digit of operand row l & 15 (7: the ones row)
+  const int ascale = arow == 7 ? 127 : 127 + 3 * (arow + 1);
+  const float kc3 = (gl & 1) ? -8.f * kOff : 1.f;
   // this lane's row of image (pair q, path/slice ps)
   auto image_row = [&](int q, int ps) -> v8i {
     const uint32_t* s = s_img + q * kPairDwords + ps * kImgDwords + l * kImgDw;
@@ -365,6 +367,20 @@ __global__ __launch_bounds__(256) void k_gemv(Args A) {
   v8i areg[8];
 #pragma unroll
   for (int ps = 0; ps < 8; ++ps) areg[ps] = NBP == 1 ? image_row(0, ps) : (v8i){};
+
+  // Slice 3 is read as (0.5 - bit) against digits coded -d/8, which adds a
+  // constant -(1/16) Σ d per operand row over the chunk's slice-3 columns; the
+  // accumulators start from that constant's negation, computed exactly by one
+  // matrix op against an all -0.5 operand (fp4 code 0b1001).
+  v4f ainit[NBP][2];
+#pragma unroll
+  for (int q = 0; q < NBP; ++q)
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+      ainit[q][p] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+          NBP == 1 ? areg[p * 4 + 3] : image_row(q, p * 4 + 3),
+          (v8i){(int)0x99999999u, (int)0x99999999u, (int)0x99999999u, (int)0x99999999u, 0, 0, 0, 0},
+          (v4f){0.f, 0.f, 0.f, 0.f}, 2, 4, 0, ascale, 0, 127);
 
   // one round: row group 4 m rb + 4 k + w from the weights in wt
   auto round = [&](const uint4 (&wt)[8], const uint16_t (&gt)[8], int k) {
@@ -381,24 +397,27 @@ __global__ __launch_bounds__(256) void k_gemv(Args A) {
 #pragma unroll
       for (int q = 0; q < NBP; ++q)
 #pragma unroll
-        for (int tau = 0; tau < 4; ++tau) acc[q][tau] = (v4f){0.f, 0.f, 0.f, 0.f};
+        for (int tau = 0; tau < 4; ++tau) acc[q][tau] = ainit[q][p];
       // slice T of a stored word (see the header comment)
       auto slice_step = [&](auto tc) {
         constexpr int T = decltype(tc)::value;
-        constexpr int sT = T == 2 ? 1 : (T == 3 ? 3 : 0);
-        constexpr uint32_t mT = (T == 1 || T == 2) ? 0x22222222u : 0x11111111u;
+        // T0: w & 0x1..1 (0.5), T1: w & 0x2..2 (1.0), T2: w & 0x4..4 (2.0, the
+        // operand scale halved), T3: (w & 0x8..8) | 0x1..1 (+0.5 or -0.5)
+        constexpr uint32_t mT = T == 0 ? 0x11111111u : T == 1 ? 0x22222222u : T == 2 ? 0x44444444u : 0x88888888u;
+        constexpr uint32_t oT = T == 3 ? 0x11111111u : 0u;
+        const int sc = T == 2 ? ascale - 1 : ascale;
         v8i a[NBP];
 #pragma unroll
         for (int q = 0; q < NBP; ++q) a[q] = NBP == 1 ? areg[p * 4 + T] : image_row(q, p * 4 + T);
 #pragma unroll
         for (int tau = 0; tau < 4; ++tau) {
           const uint4 wv = wt[tau * 2 + p];
-          const v8i bv = (v8i){(int)((wv.x >> sT) & mT), (int)((wv.y >> sT) & mT),
-                               (int)((wv.z >> sT) & mT), (int)((wv.w >> sT) & mT), 0, 0, 0, 0};
+          const v8i bv = (v8i){(int)((wv.x & mT) | oT), (int)((wv.y & mT) | oT),
+                               (int)((wv.z & mT) | oT), (int)((wv.w & mT) | oT), 0, 0, 0, 0};
 #pragma unroll
           for (int q = 0; q < NBP; ++q)
             acc[q][tau] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                a[q], bv, acc[q][tau], 2 /*A: fp6 e2m3*/, 4 /*B: fp4 e2m1*/, 0, 127, 0, 127);
+                a[q], bv, acc[q][tau], 2 /*A: fp6 e2m3*/, 4 /*B: fp4 e2m1*/, 0, sc, 0, 127);
         }
       };
       slice_step(std::integral_constant<int, 0>());
@@ -413,7 +432,7 @@ __global__ __launch_bounds__(256) void k_gemv(Args A) {
 #pragma unroll
         for (int tau = 0; tau < 4; ++tau) {
           const v4f c = acc[q][tau];
-          int mv = (int)(c[0] * wsc[0]) + (int)(c[1] * wsc[1]) + (int)(c[2] * wsc[2]) + (int)(c[3] * wsc[3]);
+          int mv = (int)__builtin_fmaf(c[3], kc3, (c[0] + c[1]) + c[2]);
           mv += __shfl_down(mv, 16, 64);  // digits 4..6 and the count term
           const double gp = (double)f16_bits_to_f32(gt[tau * 2 + p]);
           res[q][tau] += gp * ldexp((double)(U - 2 * mv), -shv);

@@ -169,6 +169,34 @@ int rabit_gemv_partial(const rabit_layer* L, const uint16_t* x, int32_t batch, v
                                         L->in_features, x, batch, workspace, (hipStream_t)stream));
 }
 
+int rabit_gemv_partial_multi(const rabit_layer* Ls, int32_t n, const uint16_t* x, int32_t batch,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  if (!Ls) return RABIT_EINVAL;
+  if (n < 1 || n > 3) return RABIT_ESHAPE;
+  if (batch < 1 || batch > RABIT_MAX_GEMV_BATCH) return RABIT_ESHAPE;
+  int s;
+  if ((s = check_gemv_x(&Ls[0], x))) return s;
+  const int in = Ls[0].in_features;
+  LinSeg segs[3];
+  size_t off = 0;
+  for (int i = 0; i < n; ++i) {
+    if ((s = check_layer(&Ls[i]))) return s;
+    if (Ls[i].in_features != in) return RABIT_ESHAPE;
+    segs[i] = LinSeg{(const uint4*)Ls[i].planes, Ls[i].g, Ls[i].h, Ls[i].out_features,
+                     (double*)((char*)workspace + off)};
+    off += gemv_workspace_bytes(Ls[i].out_features, in, batch);
+  }
+  if (!workspace || workspace_bytes < off) return RABIT_EWORKSPACE;
+  if (!aligned16(workspace)) return RABIT_EALIGN;
+  if (overlap(workspace, off, x, (size_t)batch * in * 2)) return RABIT_EINVAL;
+  for (int i = 0; i < n; ++i)
+    if (overlap(workspace, off, Ls[i].planes, rabit_planes_bytes(Ls[i].out_features, in, 2)) ||
+        overlap(workspace, off, Ls[i].g, (size_t)4 * Ls[i].out_features) ||
+        overlap(workspace, off, Ls[i].h, (size_t)4 * in))
+      return RABIT_EINVAL;
+  return dev_status(launch_gemv_multi(segs, n, in, x, batch, nullptr, 0.f, (hipStream_t)stream));
+}
+
 int rabit_gemv_reduce(const rabit_layer* L, int32_t batch, void* y, int32_t y_dtype, void* workspace,
                       size_t workspace_bytes, void* stream) {
   int s = check_gemv_common(L, batch, workspace, workspace_bytes);

@@ -189,7 +189,7 @@ struct LinSeg {
   int out;
   double* part;
 };
-#define RABIT_STAT_PARTS 8
+#define RABIT_STAT_PARTS 32
 size_t gemv_part_bytes(int out, int in, int batch);
 hipError_t launch_gemv_multi(const LinSeg* segs, int nseg, int in, const uint16_t* x, int batch,
                              const double* stats, float eps, hipStream_t st);

@@ -35,6 +35,7 @@ EXPORTS = [
     "rabit_gemm_workspace_bytes", "rabit_pack", "rabit_unpack", "rabit_gemv", "rabit_gemm",
     "rabit_decode_workspace_bytes", "rabit_decode_step", "rabit_status_string",
     "rabit_layout_version", "rabit_test_f64_to_16", "rabit_gemv_partial", "rabit_gemv_reduce",
+    "rabit_gemv_partial_multi",
 ]
 
 
@@ -94,6 +95,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "rabit_gemm": (ctypes.c_int, [lp, vp, i32, vp, i32, vp, sz, vp]),
         "rabit_gemv_partial": (ctypes.c_int, [lp, vp, i32, vp, sz, vp]),
         "rabit_gemv_reduce": (ctypes.c_int, [lp, i32, vp, i32, vp, sz, vp]),
+        "rabit_gemv_partial_multi": (ctypes.c_int, [lp, i32, vp, i32, vp, sz, vp]),
         "rabit_decode_workspace_bytes": (sz, [ctypes.POINTER(DecoderCfgC), i32]),
         "rabit_decode_step": (ctypes.c_int, [ctypes.POINTER(DecoderCfgC), lp, vp, i32, vp, vp, sz, vp]),
         "rabit_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -215,6 +217,28 @@ def gemv_partial(layer: PackedLayer, x: torch.Tensor, workspace: torch.Tensor, s
     lc = layer.c()
     _check(load().rabit_gemv_partial(ctypes.byref(lc), _ptr(x), x.shape[0], _ptr(workspace),
                                      workspace.numel(), _stream(stream)), "rabit_gemv_partial")
+
+
+def gemv_partial_multi(layers: list, x: torch.Tensor, workspace: torch.Tensor, stream=None) -> list:
+    """rabit_gemv_partial_multi: partials of 1..3 layers sharing x in one launch.
+    Returns each layer's view of the workspace (pass it to gemv_reduce)."""
+    assert x.dtype == torch.bfloat16 and x.is_contiguous()
+    lib = load()
+    arr = (RabitLayerC * len(layers))(*[L.c() for L in layers])
+    _check(lib.rabit_gemv_partial_multi(arr, len(layers), _ptr(x), x.shape[0], _ptr(workspace),
+                                        workspace.numel(), _stream(stream)), "rabit_gemv_partial_multi")
+    views, off = [], 0
+    for L in layers:
+        nb = lib.rabit_gemv_workspace_bytes(L.out_features, L.in_features, x.shape[0])
+        views.append(workspace[off:off + nb])
+        off += nb
+    return views
+
+
+def gemv_multi_workspace(layers: list, batch: int) -> torch.Tensor:
+    lib = load()
+    nb = sum(lib.rabit_gemv_workspace_bytes(L.out_features, L.in_features, batch) for L in layers)
+    return _ws(nb, layers[0].planes.device)
 
 
 def gemv_reduce(layer: PackedLayer, batch: int, y: torch.Tensor, workspace: torch.Tensor,

@@ -172,6 +172,20 @@ int rabit_gemv_reduce(const rabit_layer *layer, int32_t batch, void *y, int32_t 
                       void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * rabit_gemv_partial for n = 1..3 layers that read the same x (equal
+ * in_features; e.g. q/k/v or gate/up of a decoder layer), in one kernel
+ * launch. workspace holds the layers' partial buffers back to back: layer i's
+ * starts at the sum of rabit_gemv_workspace_bytes(out_k, in, batch) over
+ * k < i (each a multiple of 256), and rabit_gemv_reduce on layer i with a
+ * pointer to its buffer gives the same bits as rabit_gemv. workspace_bytes
+ * must cover all n buffers. Errors as rabit_gemv; RABIT_ESHAPE if n is out of
+ * range or in_features differ.
+ */
+int rabit_gemv_partial_multi(const rabit_layer *layers, int32_t n, const uint16_t *x,
+                             int32_t batch, void *workspace, size_t workspace_bytes,
+                             void *stream);
+
+/*
  * Prefill GEMM: Y[m][i] = Σ_p g_p[i] * Σ_j B_p[i][j] * h_p[j] * X[m][j].
  *
  * X       device bfloat16 bit patterns [M][in], row-major.

@@ -86,6 +86,28 @@ def test_gemv_argument_errors(lib):
     assert gemv(lib, L, ws=FAKE + 4 + (5 << 30)) == rabit.RABIT_EALIGN
 
 
+def test_gemv_partial_multi_errors(lib):
+    def multi(layers, n=None, x=FAKE + (3 << 30), batch=1, ws=FAKE + (5 << 30), wsb=1 << 30):
+        arr = (rabit.RabitLayerC * max(1, len(layers)))(*layers)
+        return lib.rabit_gemv_partial_multi(arr if layers else None, len(layers) if n is None else n,
+                                            x, batch, ws, wsb, None)
+    a = fake_layer()
+    b = fake_layer(out=128, planes=FAKE + (6 << 30), g=FAKE + (7 << 30), h=FAKE + (8 << 30))
+    assert multi([]) == rabit.RABIT_EINVAL
+    assert multi([a, b], n=0) == rabit.RABIT_ESHAPE
+    assert multi([a, b], n=4) == rabit.RABIT_ESHAPE
+    assert multi([a, fake_layer(inp=256, planes=FAKE + (6 << 30), g=FAKE + (7 << 30), h=FAKE + (8 << 30))]) \
+        == rabit.RABIT_ESHAPE                                             # in_features differ
+    assert multi([a, b], batch=17) == rabit.RABIT_ESHAPE
+    assert multi([a, b], x=0) == rabit.RABIT_EINVAL
+    assert multi([a, fake_layer(version=3)]) == rabit.RABIT_EINVAL
+    need = (lib.rabit_gemv_workspace_bytes(256, 512, 1) + lib.rabit_gemv_workspace_bytes(128, 512, 1))
+    assert multi([a, b], wsb=need - 1) == rabit.RABIT_EWORKSPACE
+    assert multi([a, b], ws=FAKE + 8 + (5 << 30)) == rabit.RABIT_EALIGN
+    assert multi([a, b], ws=FAKE + (3 << 30)) == rabit.RABIT_EINVAL     # workspace aliases x
+    assert multi([a, b], ws=FAKE + (6 << 30)) == rabit.RABIT_EINVAL     # workspace aliases planes
+
+
 def test_pack_argument_errors(lib):
     L = fake_layer()
     w = FAKE + (6 << 30)

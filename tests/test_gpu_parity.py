@@ -237,6 +237,20 @@ def test_gemv_partial_reduce_equals_gemv(gpu_lib, shape):
         assert torch.equal(y, gpu_lib.gemv(layer, x))
 
 
+def test_gemv_partial_multi_equals_gemv(gpu_lib):
+    say("gemv partial multi")
+    inp = 1100
+    layers = [pack_gpu(gpu_lib, weight_f32(o, inp, 20 + o)) for o in (300, 64, 130)]
+    for batch in (1, 2, 5):
+        x = act_bf16(batch, inp, 30 + batch).cuda()
+        ws = gpu_lib.gemv_multi_workspace(layers, batch)
+        views = gpu_lib.gemv_partial_multi(layers, x, ws)
+        for L, v in zip(layers, views):
+            y = torch.empty(batch, L.out_features, device="cuda")
+            gpu_lib.gemv_reduce(L, batch, y, v)
+            assert torch.equal(y, gpu_lib.gemv(L, x))
+
+
 GEMM_CASES = [(64, 256, 1), (130, 1000, 37), (256, 4096, 512), (1024, 4096, 130), (300, 1100, 257)]
 
 
