@@ -176,6 +176,10 @@ def main():
     ap.add_argument("--cpu-budget-s", type=float, default=8.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of graph replay")
+    ap.add_argument("--workload", default="mlp7b",
+                    choices=["mlp7b", "layer4096", "llama3-8b", "gemm", "llama70b"],
+                    help="mlp7b (default): the headline decode workload; the others measure the "
+                         "remaining configurations (one JSON line each)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -189,6 +193,11 @@ def main():
 
     rabit.load()
     torch.cuda.set_device(0)
+    if args.workload != "mlp7b":
+        extra = {"layer4096": bench_layer4096, "llama3-8b": bench_llama3_8b, "gemm": bench_gemm,
+                 "llama70b": bench_llama70b}[args.workload]
+        print(json.dumps(extra(args, rabit, torch)), flush=True)
+        return
     hidden, ffn = 4096, 11008
     shapes = mlp_shapes(hidden, ffn)
     cfg = rabit.DecoderCfg(hidden=hidden, ffn=ffn, n_layers=args.layers, mlp_only=True)
@@ -324,6 +333,184 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
+
+
+# ---------------------------------------------------------------------------
+# The other configurations (not the headline line; one JSON line each)
+# ---------------------------------------------------------------------------
+def _pack_layer(rabit, torch, out, inp, seed, ws_holder):
+    from synth.inputs import weight_f32
+    w = weight_f32(out, inp, seed, device="cuda")
+    pl = rabit.PackedLayer.empty(out, inp)
+    need = rabit.load().rabit_pack_workspace_bytes(out, inp)
+    if ws_holder[0] is None or ws_holder[0].numel() < need:
+        ws_holder[0] = torch.empty(need, dtype=torch.uint8, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    rabit.pack(w, pl, workspace=ws_holder[0])
+    e1.record()
+    e1.synchronize()
+    del w
+    return pl, e0.elapsed_time(e1)
+
+
+def _events_ms(torch, fn, n):
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(n):
+        fn(i)
+    b.record()
+    b.synchronize()
+    return a.elapsed_time(b) / n
+
+
+def _line(metric, value, unit, config, higher=True, **kw):
+    d = {"metric": metric, "value": value, "unit": unit, "n_gpus": 1, "higher_is_better": higher,
+         "vs_baseline": None, "data": "synthetic", "config": config}
+    d.update(kw)
+    return d
+
+
+def bench_layer4096(args, rabit, torch):
+    """One 4096x4096 layer: derive+pack then batch-1 GEMV, over 128 cold copies."""
+    from synth.inputs import act_bf16, seed_w, seed_x
+    n, wsh, packs = 128, [None], []
+    layers = []
+    for c in range(n):
+        pl, ms = _pack_layer(rabit, torch, 4096, 4096, seed_w(1, c, "q"), wsh)
+        layers.append(pl)
+        packs.append(ms)
+    x = act_bf16(1, 4096, seed_x(1, 1)).cuda()
+    ws = rabit.gemv_workspace(layers[0], 1)
+    y = torch.empty(1, 4096, device="cuda")
+    for i in range(n):
+        rabit.gemv(layers[i], x, y=y, workspace=ws)
+    full = _events_ms(torch, lambda i: rabit.gemv(layers[i % n], x, y=y, workspace=ws), 4 * n)
+    part = _events_ms(torch, lambda i: rabit.gemv_partial(layers[i % n], x, ws), 4 * n)
+    pb = rabit.planes_bytes(4096, 4096)
+    pk = sorted(packs[2:])[len(packs[2:]) // 2]
+    alg = gemv_alg_bytes(4096, 4096)
+    return _line("4096x4096 residual-binary GEMV packed-weight GB/s (batch 1, cold)",
+                 round(pb / (full * 1e-3) / 1e9, 1), "GB/s",
+                 {"workload": "single-layer-4096x4096-b1", "copies": n}, dtype="fp4xfp6",
+                 us_per_gemv=round(full * 1e3, 2), us_per_partial_kernel=round(part * 1e3, 2),
+                 roofline={"bound": "hbm", "achieved": round(alg / (part * 1e-3) / 1e9, 1),
+                           "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": round(alg / (part * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                           "kernel": "k_gemv<1>"},
+                 derive_pack={"ms": round(pk, 4), "gbs": round(8.25 * 4096 * 4096 / (pk * 1e-3) / 1e9, 1)})
+
+
+def _decoder_layers(rabit, torch, cfg_id, H, F, kv, n_layers):
+    names = {"q": (H, H), "k": (kv, H), "v": (kv, H), "o": (H, H), "gate": (F, H), "up": (F, H),
+             "down": (H, F)}
+    from synth.inputs import seed_w
+    wsh, layers, pack = [None], [], []
+    for li in range(n_layers):
+        d = {}
+        for nm, (o, i) in names.items():
+            d[nm], ms = _pack_layer(rabit, torch, o, i, seed_w(cfg_id, li, nm), wsh)
+            pack.append((o * i, ms))
+        layers.append(d)
+    wsh[0] = None
+    torch.cuda.empty_cache()
+    planes = sum(rabit.planes_bytes(o, i) for o, i in names.values()) * n_layers
+    return layers, planes, pack
+
+
+def _time_decode(rabit, torch, cfg, layers, batch, steps, graph=True):
+    from synth.inputs import act_bf16, seed_x
+    arr = rabit.layer_array(cfg, layers)
+    x0 = act_bf16(batch, cfg.hidden, seed_x(3, batch)).cuda()
+    bufs = [x0.clone(), torch.empty_like(x0)]
+    ws = rabit.decode_workspace(cfg, batch)
+
+    def step(i):
+        rabit.decode_step(cfg, arr, bufs[i % 2], out=bufs[(i + 1) % 2], workspace=ws)
+
+    step(0)
+    step(1)
+    torch.cuda.synchronize()
+    if graph:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            step(0)
+        torch.cuda.current_stream().wait_stream(s)
+        gs = []
+        for par in (0, 1):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(par)
+            gs.append(g)
+        run = lambda i: gs[i % 2].replay()
+    else:
+        run = step
+    for i in range(2):
+        run(i)
+    ms = _events_ms(torch, run, steps)
+    del ws
+    return ms
+
+
+def bench_llama3_8b(args, rabit, torch):
+    """Llama-3-8B-shaped decode step (32 layers of the layer set) at batch 1..16."""
+    H, F, kv, L = 4096, 14336, 1024, 32
+    layers, planes, _ = _decoder_layers(rabit, torch, 3, H, F, kv, L)
+    cfg = rabit.DecoderCfg(hidden=H, ffn=F, n_heads=32, n_kv_heads=8, head_dim=128, n_layers=L)
+    sweep = {}
+    for b in (1, 2, 4, 8, 16):
+        ms = _time_decode(rabit, torch, cfg, layers, b, 10)
+        sweep[b] = {"ms_per_step": round(ms, 4), "plane_gbs": round(planes / (ms * 1e-3) / 1e9, 1),
+                    "tokens_per_s": round(b * 1e3 / ms, 1)}
+        log(f"llama3-8b batch {b}: {ms:.3f} ms/step, {sweep[b]['plane_gbs']} GB/s")
+    return _line("Llama-3-8B decode step, packed-weight GB/s at batch 1 (sweep 1..16)",
+                 sweep[1]["plane_gbs"], "GB/s",
+                 {"workload": "llama3-8b-decode-32-layers", "batch": [1, 2, 4, 8, 16],
+                  "plane_bytes_per_step": planes}, dtype="fp4xfp6", sweep=sweep)
+
+
+def bench_gemm(args, rabit, torch):
+    """Prefill GEMM with the Llama-3-8B MLP shapes at M = 512, 2048, 8192."""
+    from synth.inputs import act_bf16, seed_w, seed_x
+    wsh, res = [None], {}
+    for (N, K) in ((14336, 4096), (4096, 14336)):
+        pl, _ = _pack_layer(rabit, torch, N, K, seed_w(4, 0, "gate" if N > K else "down"), wsh)
+        for M in (512, 2048, 8192):
+            X = act_bf16(M, K, seed_x(4, M)).cuda()
+            ws = rabit.gemm_workspace(pl, M)
+            Y = torch.empty(M, N, device="cuda")
+            rabit.gemm(pl, X, y=Y, workspace=ws)
+            ms = _events_ms(torch, lambda i: rabit.gemm(pl, X, y=Y, workspace=ws), 10)
+            tf = 4.0 * M * N * K / (ms * 1e-3) / 1e12
+            res[f"{N}x{K}_M{M}"] = {"ms": round(ms, 4), "tflops": round(tf, 1),
+                                    "mfma_frac_fp16": round(tf / 2500.0, 4)}
+            log(f"gemm {N}x{K} M={M}: {ms:.3f} ms {tf:.1f} TFLOP/s")
+            del X, ws, Y
+    best = max(v["tflops"] for v in res.values())
+    return _line("Residual-binary prefill GEMM TFLOP/s (4 M N K, fp16 MFMA)", best, "TFLOP/s",
+                 {"workload": "llama3-8b-mlp-gemm", "M": [512, 2048, 8192]}, dtype="fp16",
+                 runs=res, roofline={"bound": "mfma", "peak": 2500.0, "unit": "TFLOP/s",
+                                     "achieved": best, "frac": round(best / 2500.0, 4)})
+
+
+def bench_llama70b(args, rabit, torch):
+    """Llama-2-70B-shaped stack: derive+pack all 80 layers, then decode at batch 1 and 32."""
+    H, F, kv, L = 8192, 28672, 1024, 80
+    t0 = time.time()
+    layers, planes, pack = _decoder_layers(rabit, torch, 5, H, F, kv, L)
+    log(f"packed 80 layers ({planes / 1e9:.2f} GB of planes) in {time.time() - t0:.1f} s")
+    weights = sum(w for w, _ in pack)
+    pack_ms = sum(ms for _, ms in pack)
+    cfg = rabit.DecoderCfg(hidden=H, ffn=F, n_heads=64, n_kv_heads=8, head_dim=128, n_layers=L)
+    ms1 = _time_decode(rabit, torch, cfg, layers, 1, 5)
+    ms32 = _time_decode(rabit, torch, cfg, layers, 32, 3, graph=False)
+    return _line("Llama-2-70B decode step, packed-weight GB/s at batch 1", round(planes / (ms1 * 1e-3) / 1e9, 1),
+                 "GB/s", {"workload": "llama2-70b-80-layers", "plane_bytes_per_step": planes},
+                 dtype="fp4xfp6", ms_per_step_b1=round(ms1, 3), tokens_per_s_b1=round(1e3 / ms1, 1),
+                 ms_per_step_b32=round(ms32, 3), tokens_per_s_b32=round(32e3 / ms32, 1),
+                 derive_pack={"weights": weights, "ms": round(pack_ms, 2),
+                              "gbs": round(8.25 * weights / (pack_ms * 1e-3) / 1e9, 1)})
 
 
 if __name__ == "__main__":

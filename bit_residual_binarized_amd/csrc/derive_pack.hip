@@ -134,16 +134,25 @@ __global__ __launch_bounds__(256) void k_finalize(const double* __restrict__ row
                                                   uint16_t* __restrict__ g_out,
                                                   uint16_t* __restrict__ h_out) {
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
-  if (t < out) {
-    double s = 0.0;
-    for (int c = 0; c < nct; ++c) s += rowpart[(size_t)c * out + t];
-    g_out[t] = f64_to_f16_rne(s / (double)in);
-  } else if (t < out + in) {
-    const int j = t - out;
-    double s = 0.0;
-    for (int r = 0; r < nrt; ++r) s += colpart[(size_t)r * in + j];
-    h_out[j] = f64_to_f16_rne(s / (double)out);
+  if (t >= out + in) return;
+  const bool row = t < out;
+  const double* p = row ? rowpart + t : colpart + (t - out);
+  const int n = row ? nct : nrt;
+  const size_t stride = row ? (size_t)out : (size_t)in;
+  // the tile partials are added strictly in order; the loads of 32 of them
+  // are in flight at a time (clamped index, masked)
+  double s = 0.0;
+  for (int c0 = 0; c0 < n; c0 += 32) {
+    double v[32];
+#pragma unroll
+    for (int u = 0; u < 32; ++u) v[u] = p[(size_t)min(c0 + u, n - 1) * stride];
+#pragma unroll
+    for (int u = 0; u < 32; ++u) s += c0 + u < n ? v[u] : 0.0;
   }
+  if (row)
+    g_out[t] = f64_to_f16_rne(s / (double)in);
+  else
+    h_out[t - out] = f64_to_f16_rne(s / (double)out);
 }
 
 // Device layout -> canonical words (test hook).

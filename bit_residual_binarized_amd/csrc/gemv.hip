@@ -117,16 +117,30 @@ __device__ __forceinline__ void fill_code(uint32_t (&dw)[kImgDw], uint32_t code)
   }
 }
 
-// digit row: field x = digit `dig` of vals[x] (code d, value d/8)
-__device__ __forceinline__ void deposit_digits(uint32_t (&dw)[kImgDw], const int (&vals)[32], int dig) {
+// digit row: field x = digit `dig` of src[x] (code d, value d/8); the 32
+// values are read from LDS in two halves to bound the live registers
+__device__ __forceinline__ void deposit_digits(uint32_t (&dw)[kImgDw], const int* src, int dig) {
 #pragma unroll
   for (int d = 0; d < kImgDw; ++d) dw[d] = 0;
 #pragma unroll
-  for (int x = 0; x < 32; ++x) {
-    const uint32_t f = __builtin_amdgcn_ubfe((uint32_t)vals[x], 3 * dig, 3);
-    const int bit = 6 * x;
-    dw[bit >> 5] |= f << (bit & 31);
-    if ((bit & 31) > 29) dw[(bit >> 5) + 1] |= f >> (32 - (bit & 31));
+  for (int half = 0; half < 2; ++half) {
+    int vals[16];
+#pragma unroll
+    for (int x = 0; x < 16; x += 4) {
+      const int4 v4 = *(const int4*)(src + 16 * half + x);
+      vals[x] = v4.x;
+      vals[x + 1] = v4.y;
+      vals[x + 2] = v4.z;
+      vals[x + 3] = v4.w;
+    }
+#pragma unroll
+    for (int xx = 0; xx < 16; ++xx) {
+      const int x = 16 * half + xx;
+      const uint32_t f = __builtin_amdgcn_ubfe((uint32_t)vals[xx], 3 * dig, 3);
+      const int bit = 6 * x;
+      dw[bit >> 5] |= f << (bit & 31);
+      if ((bit & 31) > 29) dw[(bit >> 5) + 1] |= f >> (32 - (bit & 31));
+    }
   }
 }
 
@@ -135,7 +149,7 @@ __device__ __forceinline__ void deposit_digits(uint32_t (&dw)[kImgDw], const int
 // group 4 m rb + 4 k + w. Lane l = j + 16 g loads, per tile tau and path p,
 // the 16-byte unit (rg, 4 r + g, p, 16 tau + j): 128 columns of row
 // 16 tau + j, bit 4e + t of dword q being column 32 q + 4 e + t of the group.
-template <int NBP>
+template <int NBP, bool RING>
 __global__ __launch_bounds__(256) void k_gemv(Args A) {
   const int r = blockIdx.x % A.S;
   const int rbg = blockIdx.x / A.S;
@@ -310,18 +324,9 @@ __global__ __launch_bounds__(256) void k_gemv(Args A) {
           for (int d = 0; d < kImgDw; d += 2) *(uint2*)(dst + d) = make_uint2(0u, 0u);
           continue;
         }
-        int vals[32];
         const int* src = &s_v[hb][p][t * 128 + g * 32];
-#pragma unroll
-        for (int x = 0; x < 32; x += 4) {
-          const int4 v4 = *(const int4*)(src + x);
-          vals[x] = v4.x;
-          vals[x + 1] = v4.y;
-          vals[x + 2] = v4.z;
-          vals[x + 3] = v4.w;
-        }
         uint32_t dw[kImgDw];
-        deposit_digits(dw, vals, dr);
+        deposit_digits(dw, src, dr);
         if (dr == 7) fill_code(dw, 1u);  // row of ones: set-bit count
         if (dbl) {
           // codes 2d: shift the lane's 192-bit field vector left by one (each
@@ -364,9 +369,12 @@ __global__ __launch_bounds__(256) void k_gemv(Args A) {
     return (v8i){(int)a0.x, (int)a0.y, (int)a1.x, (int)a1.y, (int)a2.x, (int)a2.y, 0, 0};
   };
   // with one batch pair the 8 operand rows of this lane stay in registers
+  // (with the ring, NBP == 1); without it they are read from LDS per use,
+  // which frees 48 registers for more resident waves
+  constexpr bool kAreg = NBP == 1 && RING;
   v8i areg[8];
 #pragma unroll
-  for (int ps = 0; ps < 8; ++ps) areg[ps] = NBP == 1 ? image_row(0, ps) : (v8i){};
+  for (int ps = 0; ps < 8; ++ps) areg[ps] = kAreg ? image_row(0, ps) : (v8i){};
 
   // Slice 3 is read as (0.5 - bit) against digits coded -d/8, which adds a
   // constant -(1/16) Σ d per operand row over the chunk's slice-3 columns; the
@@ -378,7 +386,7 @@ __global__ __launch_bounds__(256) void k_gemv(Args A) {
 #pragma unroll
     for (int p = 0; p < 2; ++p)
       ainit[q][p] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-          NBP == 1 ? areg[p * 4 + 3] : image_row(q, p * 4 + 3),
+          kAreg ? areg[p * 4 + 3] : image_row(q, p * 4 + 3),
           (v8i){(int)0x99999999u, (int)0x99999999u, (int)0x99999999u, (int)0x99999999u, 0, 0, 0, 0},
           (v4f){0.f, 0.f, 0.f, 0.f}, 2, 4, 0, ascale, 0, 127);
 
@@ -408,7 +416,7 @@ __global__ __launch_bounds__(256) void k_gemv(Args A) {
         const int sc = T == 2 ? ascale - 1 : ascale;
         v8i a[NBP];
 #pragma unroll
-        for (int q = 0; q < NBP; ++q) a[q] = NBP == 1 ? areg[p * 4 + T] : image_row(q, p * 4 + T);
+        for (int q = 0; q < NBP; ++q) a[q] = kAreg ? areg[p * 4 + T] : image_row(q, p * 4 + T);
 #pragma unroll
         for (int tau = 0; tau < 4; ++tau) {
           const uint4 wv = wt[tau * 2 + p];
@@ -458,6 +466,17 @@ __global__ __launch_bounds__(256) void k_gemv(Args A) {
   // rounds in pairs, so that each ring buffer is a fixed register array
 #pragma unroll 1
   for (int k = 0; k < m; k += 2) {
+    if (!RING) {
+      // one buffer: the next round's weights are loaded after this round
+      // (fewer registers, more resident waves to cover the latency)
+      round(w0, g0, k);
+      if (k + 1 < m) {
+        load_round(w0, g0, k + 1);
+        round(w0, g0, k + 1);
+        if (k + 2 < m) load_round(w0, g0, k + 2);
+      }
+      continue;
+    }
     if (k + 1 < m) load_round(w1, g1, k + 1);
     round(w0, g0, k);
     if (k + 1 < m) {
@@ -487,10 +506,14 @@ hipError_t launch_main(const Plan& P, const Args& A, int batch, hipStream_t st) 
   const int pairs = (batch + 1) / 2;
   const dim3 grid(nrb * P.S, (pairs + P.NBP - 1) / P.NBP);
   switch (P.NBP) {
-    case 1: hipLaunchKernelGGL(k_gemv<1>, grid, dim3(256), 0, st, A); break;
-    case 2: hipLaunchKernelGGL(k_gemv<2>, grid, dim3(256), 0, st, A); break;
-    case 4: hipLaunchKernelGGL(k_gemv<4>, grid, dim3(256), 0, st, A); break;
-    default: hipLaunchKernelGGL(k_gemv<4>, grid, dim3(256), 0, st, A); break;
+    case 1:
+      if (A.m > 1)
+        hipLaunchKernelGGL((k_gemv<1, true>), grid, dim3(256), 0, st, A);
+      else
+        hipLaunchKernelGGL((k_gemv<1, false>), grid, dim3(256), 0, st, A);
+      break;
+    case 2: hipLaunchKernelGGL((k_gemv<2, false>), grid, dim3(256), 0, st, A); break;
+    default: hipLaunchKernelGGL((k_gemv<4, false>), grid, dim3(256), 0, st, A); break;
   }
   return hipGetLastError();
 }
