@@ -23,18 +23,29 @@ namespace {
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-constexpr int kBM = 128, kBN = 128, kBK = 32;
-constexpr int kLdsStride = 20;  // dwords per 32-column row in LDS (16 + 4 padding)
+constexpr int kBM = 128, kBN = 128, kBK = 64;
+constexpr int kLdsStride = 36;  // dwords per 64-column row in LDS (32 + 4 padding)
 
 struct GemmWs {
   uint16_t* xh;      // fp16 [m][Kp], κ-permuted inside 32-column blocks
   int* rowexp;       // [m] power-of-two exponent applied to row m
   uint32_t* hpairs;  // [2][Kp/32][16] fp16 pairs (h[32b+m], h[32b+m+16])
+  float* part;       // split K: [Z][m][out] partial g_1 acc_1 + g_2 acc_2
 };
 
 __host__ inline size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-__host__ inline GemmWs carve(void* ws, int in, int m) {
+// split of K over grid.z: enough workgroups to fill the chip, at least four
+// 64-column steps per slice
+__host__ inline int split_k(int out, int in, int m) {
+  const int Kp = col_groups(in) * 128;
+  const int tiles = ((out + kBN - 1) / kBN) * ((m + kBM - 1) / kBM);
+  int z = std::max(1, (512 + tiles - 1) / tiles);
+  z = std::min(z, std::max(1, Kp / (4 * kBK)));
+  return std::min(z, 16);
+}
+
+__host__ inline GemmWs carve(void* ws, int out, int in, int m) {
   const size_t Kp = (size_t)col_groups(in) * 128;
   char* p = (char*)ws;
   GemmWs w;
@@ -43,12 +54,16 @@ __host__ inline GemmWs carve(void* ws, int in, int m) {
   w.rowexp = (int*)p;
   p += a256((size_t)m * 4);
   w.hpairs = (uint32_t*)p;
+  p += a256(2 * (Kp / 32) * 16 * 4);
+  w.part = (float*)p;
   return w;
 }
 
-__host__ inline size_t ws_bytes(int in, int m) {
+__host__ inline size_t ws_bytes(int out, int in, int m) {
   const size_t Kp = (size_t)col_groups(in) * 128;
-  return a256((size_t)m * Kp * 2) + a256((size_t)m * 4) + a256(2 * (Kp / 32) * 16 * 4);
+  const int z = split_k(out, in, m);
+  return a256((size_t)m * Kp * 2) + a256((size_t)m * 4) + a256(2 * (Kp / 32) * 16 * 4) +
+         (z > 1 ? a256((size_t)z * m * out * 4) : 0);
 }
 
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
@@ -95,18 +110,23 @@ __global__ void k_gemm_prep_h(const uint16_t* __restrict__ h, int in, int Kp, Ge
   ws.hpairs[idx] = lo | (hi << 16);
 }
 
-// 128 x 128 output tile per workgroup, 4 waves in 2 x 2, 64 x 64 per wave.
+// 128 x 128 output tile per workgroup and K slice blockIdx.z, 4 waves in
+// 2 x 2 (64 x 64 per wave), 64 columns per step. The next step's operands are
+// loaded into registers while the current step runs on the matrix cores.
 __global__ __launch_bounds__(256) void k_gemm(const uint4* __restrict__ planes,
                                               const uint16_t* __restrict__ g, int out, int M,
-                                              int Kp, GemmWs ws, void* Y, int y_dtype) {
+                                              int Kp, int ksteps, GemmWs ws, void* Y, int y_dtype) {
   const int n0 = blockIdx.x * kBN, m0 = blockIdx.y * kBM;
   const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63;
   const int wm = (wv >> 1) * 64, wn = (wv & 1) * 64;
   const int KG = Kp / 128;
   const int out_pad = row_groups(out) * 64;
+  const int ks0 = blockIdx.z * ksteps, ks1 = min(Kp / kBK, ks0 + ksteps);
+  // 16-row MFMA tiles of this wave that hold rows of X (uniform)
+  const int mtiles = __builtin_amdgcn_readfirstlane(min(4, max(0, (M - m0 - wm + 15) / 16)));
 
-  __shared__ uint32_t sA[kBM * kLdsStride];
-  __shared__ uint32_t sB[2][kBN * kLdsStride];
+  __shared__ __align__(16) uint32_t sA[kBM * kLdsStride];
+  __shared__ __align__(16) uint32_t sB[2][kBN * kLdsStride];
 
   v4f acc[2][4][4];
 #pragma unroll
@@ -116,56 +136,72 @@ __global__ __launch_bounds__(256) void k_gemm(const uint4* __restrict__ planes,
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[p][i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-  // B loader: thread -> (row n0 + (tid & 127), path tid >> 7)
-  const int bn = n0 + (tid & 127), bp = tid >> 7;
-  const bool bvalid = bn < out_pad;
+  // B loader: thread -> (row n0 + (tid & 127), path tid >> 7): two words
+  const int bn = min(n0 + (tid & 127), out_pad - 1), bp = tid >> 7;
   const uint32_t* wsrc = (const uint32_t*)(planes + unit_index(bn >> 6, 0, bp, bn & 63, KG));
-  // A loader: thread -> row m0 + (tid >> 1), half (tid & 1) of the 32 columns
+  // A loader: thread -> row m0 + (tid >> 1), half (tid & 1) of the 64 columns
   const int am = m0 + (tid >> 1), ah = tid & 1;
   const bool avalid = am < M;
-  const uint4* asrc = (const uint4*)(ws.xh + (size_t)(avalid ? am : 0) * Kp) + ah * 2;
+  const uint4* asrc = (const uint4*)(ws.xh + (size_t)min(am, M - 1) * Kp) + ah * 4;
+  const uint4* hsrc = (const uint4*)(ws.hpairs + (size_t)bp * (Kp / 32) * 16);
 
-  for (int k0 = 0; k0 < Kp; k0 += kBK) {
-    const int kb = k0 >> 5;
-    // stage A (two 16-byte chunks per thread)
-    uint4 a0 = make_uint4(0, 0, 0, 0), a1 = a0;
-    if (avalid) {
-      a0 = asrc[(size_t)kb * 4 + 0];
-      a1 = asrc[(size_t)kb * 4 + 1];
-    }
-    // stage B: one canonical word, 16 sign-flipped fp16 pairs
-    uint32_t w = 0;
-    if (bvalid) w = wsrc[(size_t)(kb >> 2) * 128 * 4 + (kb & 3)];
-    const uint32_t* hp = ws.hpairs + ((size_t)bp * (Kp / 32) + kb) * 16;
-    uint32_t e[16];
+  uint4 ra[4];
+  uint2 rw;
+  uint4 rh[8];
+  auto load = [&](int ks) {
 #pragma unroll
-    for (int mm = 0; mm < 16; ++mm) e[mm] = hp[mm] ^ ((w << (15 - mm)) & 0x80008000u);
-    __syncthreads();
-    uint32_t* da = sA + (tid >> 1) * kLdsStride + ah * 8;
-    *(uint4*)(da) = a0;
-    *(uint4*)(da + 4) = a1;
+    for (int q = 0; q < 4; ++q) ra[q] = asrc[(size_t)ks * 8 + q];
+    // words 2 ks, 2 ks + 1 of the row: unit kg = ks / 2, dwords 2 (ks & 1) ..
+    rw = *(const uint2*)(wsrc + (size_t)(ks >> 1) * 128 * 4 + 2 * (ks & 1));
+#pragma unroll
+    for (int q = 0; q < 8; ++q) rh[q] = hsrc[(size_t)ks * 8 + q];  // 2 blocks x 16 pairs
+  };
+  if (ks0 < ks1) load(ks0);
+
+  for (int ks = ks0; ks < ks1; ++ks) {
+    __syncthreads();  // the previous step's LDS reads are done
+    uint32_t* da = sA + (tid >> 1) * kLdsStride + ah * 16;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) *(uint4*)(da + 4 * q) = avalid ? ra[q] : make_uint4(0, 0, 0, 0);
     uint32_t* db = sB[bp] + (tid & 127) * kLdsStride;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) *(uint4*)(db + 4 * q) = make_uint4(e[4 * q], e[4 * q + 1], e[4 * q + 2], e[4 * q + 3]);
+    for (int blk = 0; blk < 2; ++blk) {
+      const uint32_t w = blk ? rw.y : rw.x;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint4 hh = rh[blk * 4 + q];
+        uint4 e;
+        e.x = hh.x ^ ((w << (15 - (4 * q + 0))) & 0x80008000u);
+        e.y = hh.y ^ ((w << (15 - (4 * q + 1))) & 0x80008000u);
+        e.z = hh.z ^ ((w << (15 - (4 * q + 2))) & 0x80008000u);
+        e.w = hh.w ^ ((w << (15 - (4 * q + 3))) & 0x80008000u);
+        *(uint4*)(db + 16 * blk + 4 * q) = e;
+      }
+    }
     __syncthreads();
+    if (ks + 1 < ks1) load(ks + 1);  // in flight during the matrix ops
 
     const int fr = l & 15, fg = l >> 4;
-    v8h fa[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fa[i] = *(const v8h*)(sA + (wm + 16 * i + fr) * kLdsStride + 4 * fg);
+    for (int sub = 0; sub < 2; ++sub) {
+      v8h fa[4];
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
+      for (int i = 0; i < 4; ++i) fa[i] = *(const v8h*)(sA + (wm + 16 * i + fr) * kLdsStride + 16 * sub + 4 * fg);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const v8h fb = *(const v8h*)(sB[p] + (wn + 16 * j + fr) * kLdsStride + 4 * fg);
+      for (int p = 0; p < 2; ++p) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          acc[p][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[i], fb, acc[p][i][j], 0, 0, 0);
+        for (int j = 0; j < 4; ++j) {
+          const v8h fb = *(const v8h*)(sB[p] + (wn + 16 * j + fr) * kLdsStride + 16 * sub + 4 * fg);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (i < mtiles) acc[p][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[i], fb, acc[p][i][j], 0, 0, 0);
+        }
       }
     }
   }
 
   // epilogue: C[i][j] of a 16x16 tile: lane l, reg r -> row 4(l/16)+r, col l%16
+  const bool split = gridDim.z > 1;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int n = n0 + wn + 16 * j + (l & 15);
@@ -177,32 +213,57 @@ __global__ __launch_bounds__(256) void k_gemm(const uint4* __restrict__ planes,
       for (int r = 0; r < 4; ++r) {
         const int m = m0 + wm + 16 * i + 4 * (l >> 4) + r;
         if (m >= M) continue;
-        const float v = ldexpf(g0 * acc[0][i][j][r] + g1 * acc[1][i][j][r], -ws.rowexp[m]);
-        if (y_dtype == RABIT_OUT_F32)
-          ((float*)Y)[(size_t)m * out + n] = v;
-        else
-          ((uint16_t*)Y)[(size_t)m * out + n] = f32_to_bf16_rne(v);
+        const float v = g0 * acc[0][i][j][r] + g1 * acc[1][i][j][r];
+        if (split) {
+          ws.part[((size_t)blockIdx.z * M + m) * out + n] = v;
+        } else {
+          const float y = ldexpf(v, -ws.rowexp[m]);
+          if (y_dtype == RABIT_OUT_F32)
+            ((float*)Y)[(size_t)m * out + n] = y;
+          else
+            ((uint16_t*)Y)[(size_t)m * out + n] = f32_to_bf16_rne(y);
+        }
       }
     }
   }
 }
 
+// split K: Y = 2^-rowexp Σ_z part[z] (ascending z)
+__global__ __launch_bounds__(256) void k_gemm_reduce(GemmWs ws, int out, int M, int Z, void* Y,
+                                                     int y_dtype) {
+  const size_t idx = blockIdx.x * (size_t)256 + threadIdx.x;
+  if (idx >= (size_t)M * out) return;
+  const int m = (int)(idx / out);
+  float v = 0.f;
+  for (int z = 0; z < Z; ++z) v += ws.part[(size_t)z * M * out + idx];
+  const float y = ldexpf(v, -ws.rowexp[m]);
+  if (y_dtype == RABIT_OUT_F32)
+    ((float*)Y)[idx] = y;
+  else
+    ((uint16_t*)Y)[idx] = f32_to_bf16_rne(y);
+}
+
 }  // namespace
 
-size_t gemm_workspace_bytes(int out, int in, int m) {
-  (void)out;
-  return ws_bytes(in, m);
-}
+size_t gemm_workspace_bytes(int out, int in, int m) { return ws_bytes(out, in, m); }
 
 hipError_t launch_gemm(const uint4* planes, const uint16_t* g, const uint16_t* h, int out, int in,
                        const uint16_t* X, int m, void* Y, int y_dtype, void* ws, hipStream_t st) {
   const int Kp = col_groups(in) * 128;
-  GemmWs w = carve(ws, in, m);
+  GemmWs w = carve(ws, out, in, m);
   hipLaunchKernelGGL(k_gemm_prep_x, dim3(m), dim3(256), 0, st, X, in, Kp, w);
   const int nh = 2 * (Kp / 32) * 16;
   hipLaunchKernelGGL(k_gemm_prep_h, dim3((nh + 255) / 256), dim3(256), 0, st, h, in, Kp, w);
-  const dim3 grid((out + kBN - 1) / kBN, (m + kBM - 1) / kBM);
-  hipLaunchKernelGGL(k_gemm, grid, dim3(256), 0, st, planes, g, out, m, Kp, w, Y, y_dtype);
+  const int Z = split_k(out, in, m);
+  const int steps = Kp / kBK;
+  const int per = (steps + Z - 1) / Z;
+  const dim3 grid((out + kBN - 1) / kBN, (m + kBM - 1) / kBM, Z);
+  hipLaunchKernelGGL(k_gemm, grid, dim3(256), 0, st, planes, g, out, m, Kp, per, w, Y, y_dtype);
+  if (Z > 1) {
+    const size_t n = (size_t)m * out;
+    hipLaunchKernelGGL(k_gemm_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, w, out,
+                       m, Z, Y, y_dtype);
+  }
   return hipGetLastError();
 }
 
