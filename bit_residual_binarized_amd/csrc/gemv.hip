@@ -393,12 +393,8 @@ __global__ __launch_bounds__(256) void k_gemv(Args A) {
   // one round: row group 4 m rb + 4 k + w from the weights in wt
   auto round = [&](const uint4 (&wt)[8], const uint16_t (&gt)[8], int k) {
     const int rg = 4 * m * rb + 4 * k + w;
-    double res[NBP][4];
-#pragma unroll
-    for (int q = 0; q < NBP; ++q)
-#pragma unroll
-      for (int tau = 0; tau < 4; ++tau) res[q][tau] = 0.0;
-
+    // per lane and path: this lane's exact share of Σ bit·v (see above)
+    int mv[NBP][2][4];
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       v4f acc[NBP][4];
@@ -434,17 +430,28 @@ __global__ __launch_bounds__(256) void k_gemv(Args A) {
       slice_step(std::integral_constant<int, 3>());
 
 #pragma unroll
-      for (int q = 0; q < NBP; ++q) {
-        const int shv = s_sh[q][hbl][p];
-        const int U = s_U[q][hbl][p];
+      for (int q = 0; q < NBP; ++q)
 #pragma unroll
         for (int tau = 0; tau < 4; ++tau) {
           const v4f c = acc[q][tau];
-          int mv = (int)__builtin_fmaf(c[3], kc3, (c[0] + c[1]) + c[2]);
-          mv += __shfl_down(mv, 16, 64);  // digits 4..6 and the count term
-          const double gp = (double)f16_bits_to_f32(gt[tau * 2 + p]);
-          res[q][tau] += gp * ldexp((double)(U - 2 * mv), -shv);
+          mv[q][p][tau] = (int)__builtin_fmaf(c[3], kc3, (c[0] + c[1]) + c[2]);
         }
+    }
+
+    // lanes of rows 0 and 2 (gl even) add the share of the lane 16 above
+    // (a VALU row swap) and form g_1 S_1 + g_2 S_2 in float64
+    double res[NBP][4];
+#pragma unroll
+    for (int q = 0; q < NBP; ++q) {
+      const int sh0 = s_sh[q][hbl][0], sh1 = s_sh[q][hbl][1];
+      const int U0 = s_U[q][hbl][0], U1 = s_U[q][hbl][1];
+#pragma unroll
+      for (int tau = 0; tau < 4; ++tau) {
+        const int m0 = mv[q][0][tau] + (int)__builtin_amdgcn_permlane16_swap(mv[q][0][tau], mv[q][0][tau], false, false)[1];
+        const int m1 = mv[q][1][tau] + (int)__builtin_amdgcn_permlane16_swap(mv[q][1][tau], mv[q][1][tau], false, false)[1];
+        const double g0 = ldexp((double)f16_bits_to_f32(gt[tau * 2 + 0]), -sh0);
+        const double g1 = ldexp((double)f16_bits_to_f32(gt[tau * 2 + 1]), -sh1);
+        res[q][tau] = g0 * (double)(U0 - 2 * m0) + g1 * (double)(U1 - 2 * m1);
       }
     }
 
