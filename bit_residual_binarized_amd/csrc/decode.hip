@@ -66,23 +66,8 @@ __global__ void k_residual_add(const uint16_t* __restrict__ x, const float* __re
 
 // ---- consumers of GEMV partials (fused with the ops that follow a layer) ----
 // part: float64 [batch][S][stride] with S = ceil(in/512) ranges of the
-// producing GEMV and stride = 64 ceil(n/64); ranges are added in ascending
-// order, as rabit_gemv_reduce does.
-__device__ __forceinline__ double sum_ranges(const double* __restrict__ part, int b, int S,
-                                             int stride, int i) {
-  const double* pp = part + (size_t)b * S * stride + i;
-  double v = 0.0;
-  // eight loads in flight at a time (clamped index, masked), added in order
-  for (int r = 0; r < S; r += 8) {
-    double t[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) t[u] = pp[(size_t)min(r + u, S - 1) * stride];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) v += r + u < S ? t[u] : 0.0;
-  }
-  return v;
-}
-
+// producing GEMV and stride = 64 ceil(n/64); sum_ranges adds the ranges in
+// ascending order, as rabit_gemv_reduce does.
 // Block (i, b) covers elements [i span, (i + 1) span) of row b: x_out =
 // bf16(x + Σ part) (or x itself without part) and the sum of x_out^2 over
 // the block, combined in a fixed order, into stats[b][i].

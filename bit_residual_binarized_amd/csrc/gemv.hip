@@ -35,6 +35,7 @@
 //    small reduce kernel, or the fused op that follows the layer), so the
 //    output is bitwise repeatable. No atomics, no fences.
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "rabit_internal.h"
@@ -77,6 +78,9 @@ struct Args {
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+constexpr int kMaxRounds = 8;   // row groups per wave and launch
+constexpr int kMaxDevices = 64;
+
 struct Plan {
   int KG, S, m, NBP;  // NBP: batch pairs per workgroup
   int RB[kMaxSeg];    // row blocks per segment (4 m row groups each)
@@ -87,19 +91,6 @@ __host__ inline int nbp_for(int batch) {
   return pairs <= 1 ? 1 : pairs <= 2 ? 2 : 4;
 }
 
-__host__ inline Plan make_plan(const int* outs, int nseg, int in, int batch) {
-  Plan P;
-  P.KG = col_groups(in);
-  P.S = (in + kChunk - 1) / kChunk;
-  P.NBP = nbp_for(batch);
-  int quads = 0;
-  for (int s = 0; s < nseg; ++s) quads += (row_groups(outs[s]) + 3) / 4;
-  // rows per workgroup: enough workgroups to fill the chip a few times over,
-  // more row groups per workgroup (amortising its digit build) beyond that
-  P.m = std::max(1, std::min(8, quads * P.S / 512));
-  for (int s = 0; s < nseg; ++s) P.RB[s] = (row_groups(outs[s]) + 4 * P.m - 1) / (4 * P.m);
-  return P;
-}
 
 __host__ inline size_t part_bytes(int out, int S, int batch) {
   return align256((size_t)batch * S * row_groups(out) * 64 * sizeof(double));
@@ -498,13 +489,70 @@ __global__ __launch_bounds__(256) void k_gemv_reduce(const double* __restrict__ 
                                                      int RG, int S, void* y, int y_dtype) {
   const int row = blockIdx.x * 256 + threadIdx.x, b = blockIdx.y;
   if (row >= out) return;
-  const double* pp = part + (size_t)b * S * RG * 64 + row;
-  double v = 0.0;
-  for (int s = 0; s < S; ++s) v += pp[(size_t)s * RG * 64];
+  const double v = sum_ranges(part, b, S, RG * 64, row);
   if (y_dtype == RABIT_OUT_F32)
     ((float*)y)[(size_t)b * out + row] = (float)v;
   else
     ((uint16_t*)y)[(size_t)b * out + row] = f64_to_bf16_rne(v);
+}
+
+// Workgroups of one variant that fit on the device at once (occupancy from
+// the runtime, queried once per device and variant).
+int resident_wgs(int NBP, bool ring) {
+  static std::atomic<int> cache[kMaxDevices][3][2];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
+  const int vi = NBP == 1 ? 0 : NBP == 2 ? 1 : 2;
+  std::atomic<int>& slot = cache[dev][vi][ring ? 1 : 0];
+  int c = slot.load(std::memory_order_relaxed);
+  if (c == 0) {
+    int cus = 0, per = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+      cus = 256;
+    const void* fn = NBP == 1 ? (ring ? (const void*)k_gemv<1, true> : (const void*)k_gemv<1, false>)
+                     : NBP == 2 ? (const void*)k_gemv<2, false> : (const void*)k_gemv<4, false>;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fn, 256, 0) != hipSuccess || per < 1) per = 1;
+    c = cus * per;
+    slot.store(c, std::memory_order_relaxed);
+  }
+  return c;
+}
+
+// Rows per workgroup (4 m row groups). A workgroup builds the digit operand
+// of its range once and then streams m row groups. With one batch pair and
+// m > 1 the next round's weights are in flight during a round, so all
+// workgroups of a launch should be resident together: a second pass of a few
+// workgroups runs its m rounds with most of the device idle. Cost model:
+// passes x (m rounds + one for the digit build), ties to the smaller m (more
+// workgroups). With more batch pairs (one buffer, rounds not overlapped) the
+// rounds stay short: enough workgroups to fill the device a few times over.
+__host__ inline Plan make_plan(const int* outs, int nseg, int in, int batch) {
+  Plan P;
+  P.KG = col_groups(in);
+  P.S = (in + kChunk - 1) / kChunk;
+  P.NBP = nbp_for(batch);
+  const int pairs = (batch + 1) / 2;
+  const int groups = (pairs + P.NBP - 1) / P.NBP;
+  long best = -1;
+  P.m = 1;
+  if (P.NBP > 1) {
+    int quads = 0;
+    for (int s = 0; s < nseg; ++s) quads += (row_groups(outs[s]) + 3) / 4;
+    P.m = std::max(1, std::min(kMaxRounds, quads * P.S / 512));
+  }
+  for (int m = 1; m <= kMaxRounds && P.NBP == 1; ++m) {
+    long wgs = 0;
+    for (int s = 0; s < nseg; ++s) wgs += (row_groups(outs[s]) + 4 * m - 1) / (4 * m);
+    wgs *= (long)P.S * groups;
+    const long cap = resident_wgs(P.NBP, P.NBP == 1 && m > 1);
+    const long cost = (wgs + cap - 1) / cap * (m + 1);
+    if (best < 0 || cost < best) {
+      best = cost;
+      P.m = m;
+    }
+  }
+  for (int s = 0; s < nseg; ++s) P.RB[s] = (row_groups(outs[s]) + 4 * P.m - 1) / (4 * P.m);
+  return P;
 }
 
 hipError_t launch_main(const Plan& P, const Args& A, int batch, hipStream_t st) {

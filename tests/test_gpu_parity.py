@@ -336,6 +336,35 @@ def test_decode_llama7b_mlp_block(gpu_lib):
     assert ok
 
 
+@pytest.mark.parametrize("mlp_only", [True, False])
+def test_decode_batch1_inputs_from_partials_match_batch2(gpu_lib, mlp_only):
+    # every step of a decode step is per batch row (fixed-point scales per
+    # row and range, RMS statistics per row), and batch 1 and batch 2 run the
+    # same kernels with one or two live rows: row 0 must match bit for bit
+    say("decode batch 1 vs row 0 of batch 2, mlp_only", mlp_only)
+    cfg = gpu_lib.DecoderCfg(hidden=1024, ffn=2752, n_heads=8, n_kv_heads=2, head_dim=128, n_layers=2,
+                             mlp_only=mlp_only)
+    H, F, kv = cfg.hidden, cfg.ffn, cfg.n_kv_heads * cfg.head_dim
+    shapes = {"q": (H, H), "k": (kv, H), "v": (kv, H), "o": (H, H), "gate": (F, H), "up": (F, H), "down": (H, F)}
+    names = ["gate", "up", "down"] if mlp_only else list(shapes)
+    layers = [{n: pack_gpu(gpu_lib, weight_f32(*shapes[n], 900 + 10 * li + len(n))) for n in names}
+              for li in range(cfg.n_layers)]
+    x2 = act_bf16(2, H, 991).cuda()
+    y1 = gpu_lib.decode_step(cfg, layers, x2[:1].contiguous()).cpu()
+    y2 = gpu_lib.decode_step(cfg, layers, x2).cpu()
+    assert torch.equal(y1[0].view(torch.int16), y2[0].view(torch.int16))
+
+
+def test_decode_batch1_wide_hidden(gpu_lib):
+    # 9 input ranges per hidden row, 36 query heads over 4 key/value groups
+    say("decode batch 1, hidden 4608")
+    cfg = gpu_lib.DecoderCfg(hidden=4608, ffn=1024, n_heads=36, n_kv_heads=4, head_dim=128, n_layers=1)
+    y, ref = _decode_case(gpu_lib, cfg, False, 1, 800)
+    ok, nbad = bf16_close(y, ref)
+    say("  normwise err", oracle.normwise_rel_err(y, ref), "elements outside bound", nbad)
+    assert ok
+
+
 @pytest.mark.parametrize("batch", [1, 2, 4, 20])
 def test_decode_attention_block(gpu_lib, batch):
     say("decode attention block batch", batch)
