@@ -73,6 +73,7 @@ struct Args {
   const uint16_t* x;      // bf16 [batch][in]
   const double* stats;    // norm mode: [batch][kStatParts] partial sums of x^2
   int nseg, in, KG, S, m, batch, norm;
+  int items, ngrp;        // work items (row block, range); batch groups along x
   float eps;
 };
 
@@ -82,14 +83,9 @@ constexpr int kMaxRounds = 8;   // row groups per wave and launch
 constexpr int kMaxDevices = 64;
 
 struct Plan {
-  int KG, S, m, NBP;  // NBP: batch pairs per workgroup
+  int KG, S, m;
   int RB[kMaxSeg];    // row blocks per segment (4 m row groups each)
 };
-
-__host__ inline int nbp_for(int batch) {
-  const int pairs = (batch + 1) / 2;
-  return pairs <= 1 ? 1 : pairs <= 2 ? 2 : 4;
-}
 
 
 __host__ inline size_t part_bytes(int out, int S, int batch) {
@@ -136,14 +132,29 @@ __device__ __forceinline__ void deposit_digits(uint32_t (&dw)[kImgDw], const int
 }
 
 // Workgroup: 4 waves; segment/row block rbg, K range r (512 columns), batch
-// pairs [NBP*blockIdx.y, NBP*blockIdx.y + NBP). Round k: wave w takes row
+// pairs [NBP grp, NBP grp + NBP). Every launch uses NBP = 1: a workgroup that
+// carries several pairs shares one weight load among them, but needs more
+// registers (fewer resident waves) and was measured slower than one-pair
+// workgroups that share the weights through L2. Round k: wave w takes row
 // group 4 m rb + 4 k + w. Lane l = j + 16 g loads, per tile tau and path p,
 // the 16-byte unit (rg, 4 r + g, p, 16 tau + j): 128 columns of row
 // 16 tau + j, bit 4e + t of dword q being column 32 q + 4 e + t of the group.
 template <int NBP, bool RING>
 __global__ __launch_bounds__(256) void k_gemv(Args A) {
-  const int r = blockIdx.x % A.S;
-  const int rbg = blockIdx.x / A.S;
+  // Work item (row block, range) and batch group of this workgroup. With
+  // several batch groups, the groups of one item are adjacent in launch order
+  // and share blockIdx.x % 8 (workgroups are dealt to the 8 XCDs in launch
+  // order), so that the item's weights come from HBM once and from that XCD's
+  // L2 for the other groups.
+  int wid = blockIdx.x, grp = 0;
+  if (A.ngrp > 1) {
+    const int hi = blockIdx.x >> 3;
+    grp = hi % A.ngrp;
+    wid = (hi / A.ngrp) * 8 + (blockIdx.x & 7);
+    if (wid >= A.items) return;
+  }
+  const int r = wid % A.S;
+  const int rbg = wid / A.S;
   // segment of this row block (uniform selects, no indexing of the arguments)
   const int si = (A.nseg > 2 && rbg >= A.seg[2].rb0) ? 2 : (A.nseg > 1 && rbg >= A.seg[1].rb0) ? 1 : 0;
   const uint4* planes = si == 2 ? A.seg[2].planes : si == 1 ? A.seg[1].planes : A.seg[0].planes;
@@ -157,7 +168,7 @@ __global__ __launch_bounds__(256) void k_gemv(Args A) {
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
   const int j = l & 15, gl = l >> 4;
-  const int bp0 = blockIdx.y * NBP;
+  const int bp0 = grp * NBP;
   const int in = A.in, batch = A.batch, m = A.m;
   const int col0 = r * kChunk;
 
@@ -498,19 +509,17 @@ __global__ __launch_bounds__(256) void k_gemv_reduce(const double* __restrict__ 
 
 // Workgroups of one variant that fit on the device at once (occupancy from
 // the runtime, queried once per device and variant).
-int resident_wgs(int NBP, bool ring) {
-  static std::atomic<int> cache[kMaxDevices][3][2];
+int resident_wgs(bool ring) {
+  static std::atomic<int> cache[kMaxDevices][2];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
-  const int vi = NBP == 1 ? 0 : NBP == 2 ? 1 : 2;
-  std::atomic<int>& slot = cache[dev][vi][ring ? 1 : 0];
+  std::atomic<int>& slot = cache[dev][ring ? 1 : 0];
   int c = slot.load(std::memory_order_relaxed);
   if (c == 0) {
     int cus = 0, per = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
       cus = 256;
-    const void* fn = NBP == 1 ? (ring ? (const void*)k_gemv<1, true> : (const void*)k_gemv<1, false>)
-                     : NBP == 2 ? (const void*)k_gemv<2, false> : (const void*)k_gemv<4, false>;
+    const void* fn = ring ? (const void*)k_gemv<1, true> : (const void*)k_gemv<1, false>;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fn, 256, 0) != hipSuccess || per < 1) per = 1;
     c = cus * per;
     slot.store(c, std::memory_order_relaxed);
@@ -530,21 +539,14 @@ __host__ inline Plan make_plan(const int* outs, int nseg, int in, int batch) {
   Plan P;
   P.KG = col_groups(in);
   P.S = (in + kChunk - 1) / kChunk;
-  P.NBP = nbp_for(batch);
-  const int pairs = (batch + 1) / 2;
-  const int groups = (pairs + P.NBP - 1) / P.NBP;
+  const int groups = (batch + 1) / 2;  // one batch pair per workgroup
   long best = -1;
   P.m = 1;
-  if (P.NBP > 1) {
-    int quads = 0;
-    for (int s = 0; s < nseg; ++s) quads += (row_groups(outs[s]) + 3) / 4;
-    P.m = std::max(1, std::min(kMaxRounds, quads * P.S / 512));
-  }
-  for (int m = 1; m <= kMaxRounds && P.NBP == 1; ++m) {
+  for (int m = 1; m <= kMaxRounds; ++m) {
     long wgs = 0;
     for (int s = 0; s < nseg; ++s) wgs += (row_groups(outs[s]) + 4 * m - 1) / (4 * m);
     wgs *= (long)P.S * groups;
-    const long cap = resident_wgs(P.NBP, P.NBP == 1 && m > 1);
+    const long cap = resident_wgs(m > 1);
     const long cost = (wgs + cap - 1) / cap * (m + 1);
     if (best < 0 || cost < best) {
       best = cost;
@@ -558,18 +560,15 @@ __host__ inline Plan make_plan(const int* outs, int nseg, int in, int batch) {
 hipError_t launch_main(const Plan& P, const Args& A, int batch, hipStream_t st) {
   int nrb = 0;
   for (int s = 0; s < A.nseg; ++s) nrb += P.RB[s];
-  const int pairs = (batch + 1) / 2;
-  const dim3 grid(nrb * P.S, (pairs + P.NBP - 1) / P.NBP);
-  switch (P.NBP) {
-    case 1:
-      if (A.m > 1)
-        hipLaunchKernelGGL((k_gemv<1, true>), grid, dim3(256), 0, st, A);
-      else
-        hipLaunchKernelGGL((k_gemv<1, false>), grid, dim3(256), 0, st, A);
-      break;
-    case 2: hipLaunchKernelGGL((k_gemv<2, false>), grid, dim3(256), 0, st, A); break;
-    default: hipLaunchKernelGGL((k_gemv<4, false>), grid, dim3(256), 0, st, A); break;
-  }
+  const int groups = (batch + 1) / 2;
+  const dim3 grid(groups > 1 ? (nrb * P.S + 7) / 8 * 8 * groups : nrb * P.S);
+  Args B = A;
+  B.items = nrb * P.S;
+  B.ngrp = groups;
+  if (A.m > 1)
+    hipLaunchKernelGGL((k_gemv<1, true>), grid, dim3(256), 0, st, B);
+  else
+    hipLaunchKernelGGL((k_gemv<1, false>), grid, dim3(256), 0, st, B);
   return hipGetLastError();
 }
 
