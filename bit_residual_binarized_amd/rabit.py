@@ -27,7 +27,7 @@ RABIT_SCALES_MEANABS = 1
 RABIT_OUT_F32 = 0
 RABIT_OUT_BF16 = 1
 RABIT_LAYOUT_V1 = 1
-MAX_GEMV_BATCH = 16
+MAX_GEMV_BATCH = 32
 
 # every symbol include/rabit.h declares
 EXPORTS = [

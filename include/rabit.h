@@ -79,7 +79,7 @@ enum {
 
 /* Largest supported dimensions (out_features, in_features, batch, M). */
 #define RABIT_MAX_FEATURES (1 << 19)
-#define RABIT_MAX_GEMV_BATCH 16
+#define RABIT_MAX_GEMV_BATCH 32
 #define RABIT_MAX_GEMM_M (1 << 20)
 
 /*

@@ -45,7 +45,7 @@ def test_sizes(lib):
     assert lib.rabit_planes_bytes(1 << 20, 4, 2) == 0
     assert lib.rabit_pack_workspace_bytes(4096, 4096) > 0
     assert lib.rabit_gemv_workspace_bytes(4096, 4096, 1) > 0
-    assert lib.rabit_gemv_workspace_bytes(4096, 4096, 17) == 0
+    assert lib.rabit_gemv_workspace_bytes(4096, 4096, 33) == 0
     assert lib.rabit_gemm_workspace_bytes(4096, 4096, 512) > 0
     assert lib.rabit_layout_version() == 1
     for code in range(-6, 1):
@@ -78,7 +78,7 @@ def test_gemv_argument_errors(lib):
     assert gemv(lib, L, x=0) == rabit.RABIT_EINVAL
     assert gemv(lib, L, x=FAKE + 2 + (3 << 30)) == rabit.RABIT_EALIGN
     assert gemv(lib, L, batch=0) == rabit.RABIT_ESHAPE
-    assert gemv(lib, L, batch=17) == rabit.RABIT_ESHAPE
+    assert gemv(lib, L, batch=33) == rabit.RABIT_ESHAPE
     assert gemv(lib, L, dtype=7) == rabit.RABIT_EINVAL
     assert gemv(lib, L, y=FAKE + (3 << 30)) == rabit.RABIT_EINVAL     # y aliases x
     assert gemv(lib, L, ws=0) == rabit.RABIT_EWORKSPACE
@@ -98,7 +98,7 @@ def test_gemv_partial_multi_errors(lib):
     assert multi([a, b], n=4) == rabit.RABIT_ESHAPE
     assert multi([a, fake_layer(inp=256, planes=FAKE + (6 << 30), g=FAKE + (7 << 30), h=FAKE + (8 << 30))]) \
         == rabit.RABIT_ESHAPE                                             # in_features differ
-    assert multi([a, b], batch=17) == rabit.RABIT_ESHAPE
+    assert multi([a, b], batch=33) == rabit.RABIT_ESHAPE
     assert multi([a, b], x=0) == rabit.RABIT_EINVAL
     assert multi([a, fake_layer(version=3)]) == rabit.RABIT_EINVAL
     need = (lib.rabit_gemv_workspace_bytes(256, 512, 1) + lib.rabit_gemv_workspace_bytes(128, 512, 1))

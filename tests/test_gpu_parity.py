@@ -176,7 +176,7 @@ def test_gemv_batch1(gpu_lib, shape):
     assert np.array_equal(y.astype(np.float32), y2), "not repeatable"
 
 
-@pytest.mark.parametrize("batch", [2, 3, 4, 8, 16])
+@pytest.mark.parametrize("batch", [2, 3, 4, 8, 16, 25, 32])
 def test_gemv_batches(gpu_lib, batch):
     out, inp = 1024, 4096
     say("gemv batch", batch)
@@ -365,7 +365,7 @@ def test_decode_batch1_wide_hidden(gpu_lib):
     assert ok
 
 
-@pytest.mark.parametrize("batch", [1, 2, 4, 20])
+@pytest.mark.parametrize("batch", [1, 2, 4, 20, 40])
 def test_decode_attention_block(gpu_lib, batch):
     say("decode attention block batch", batch)
     cfg = gpu_lib.DecoderCfg(hidden=512, ffn=1376, n_heads=8, n_kv_heads=2, head_dim=64, n_layers=2)
