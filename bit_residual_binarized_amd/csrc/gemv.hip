@@ -139,15 +139,15 @@ __device__ __forceinline__ void deposit_digits(uint32_t (&dw)[kImgDw], const int
 // group 4 m rb + 4 k + w. Lane l = j + 16 g loads, per tile tau and path p,
 // the 16-byte unit (rg, 4 r + g, p, 16 tau + j): 128 columns of row
 // 16 tau + j, bit 4e + t of dword q being column 32 q + 4 e + t of the group.
-template <int NBP, bool RING>
+template <int NBP, bool RING, bool GROUPED>
 __global__ __launch_bounds__(256) void k_gemv(Args A) {
   // Work item (row block, range) and batch group of this workgroup. With
-  // several batch groups, the groups of one item are adjacent in launch order
-  // and share blockIdx.x % 8 (workgroups are dealt to the 8 XCDs in launch
-  // order), so that the item's weights come from HBM once and from that XCD's
-  // L2 for the other groups.
+  // several batch groups (GROUPED), the groups of one item are adjacent in
+  // launch order and share blockIdx.x % 8 (workgroups are dealt to the 8 XCDs
+  // in launch order), so that the item's weights come from HBM once and from
+  // that XCD's L2 for the other groups.
   int wid = blockIdx.x, grp = 0;
-  if (A.ngrp > 1) {
+  if (GROUPED) {
     const int hi = blockIdx.x >> 3;
     grp = hi % A.ngrp;
     wid = (hi / A.ngrp) * 8 + (blockIdx.x & 7);
@@ -500,7 +500,9 @@ __global__ __launch_bounds__(256) void k_gemv_reduce(const double* __restrict__ 
                                                      int RG, int S, void* y, int y_dtype) {
   const int row = blockIdx.x * 256 + threadIdx.x, b = blockIdx.y;
   if (row >= out) return;
-  const double v = sum_ranges(part, b, S, RG * 64, row);
+  // many ranges (wide layers): 32 loads in flight per round trip
+  const double* pp = part + (size_t)b * S * RG * 64 + row;
+  const double v = S <= 8 ? sum_ranges_by<8>(pp, S, RG * 64) : sum_ranges_by<32>(pp, S, RG * 64);
   if (y_dtype == RABIT_OUT_F32)
     ((float*)y)[(size_t)b * out + row] = (float)v;
   else
@@ -519,7 +521,7 @@ int resident_wgs(bool ring) {
     int cus = 0, per = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
       cus = 256;
-    const void* fn = ring ? (const void*)k_gemv<1, true> : (const void*)k_gemv<1, false>;
+    const void* fn = ring ? (const void*)k_gemv<1, true, false> : (const void*)k_gemv<1, false, false>;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fn, 256, 0) != hipSuccess || per < 1) per = 1;
     c = cus * per;
     slot.store(c, std::memory_order_relaxed);
@@ -565,10 +567,17 @@ hipError_t launch_main(const Plan& P, const Args& A, int batch, hipStream_t st) 
   Args B = A;
   B.items = nrb * P.S;
   B.ngrp = groups;
-  if (A.m > 1)
-    hipLaunchKernelGGL((k_gemv<1, true>), grid, dim3(256), 0, st, B);
-  else
-    hipLaunchKernelGGL((k_gemv<1, false>), grid, dim3(256), 0, st, B);
+  if (groups > 1) {
+    if (A.m > 1)
+      hipLaunchKernelGGL((k_gemv<1, true, true>), grid, dim3(256), 0, st, B);
+    else
+      hipLaunchKernelGGL((k_gemv<1, false, true>), grid, dim3(256), 0, st, B);
+  } else {
+    if (A.m > 1)
+      hipLaunchKernelGGL((k_gemv<1, true, false>), grid, dim3(256), 0, st, B);
+    else
+      hipLaunchKernelGGL((k_gemv<1, false, false>), grid, dim3(256), 0, st, B);
+  }
   return hipGetLastError();
 }
 

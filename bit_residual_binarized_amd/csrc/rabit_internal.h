@@ -192,9 +192,9 @@ struct LinSeg {
 #define RABIT_STAT_PARTS 32
 
 // Σ_r part[b][r][i] over the S ranges of a GEMV's float64 partials (row
-// stride `stride`), added in ascending r. The loads of up to 32 ranges are in
-// flight together (clamped index, masked), so that a consumer of a layer with
-// many ranges waits for memory once or twice, not once per 8 ranges.
+// stride `stride`), added in ascending r, with the loads of C ranges in flight
+// together (clamped index, masked). The decode consumers use C = 8: a wider
+// chunk makes these small kernels slower to start than the round trips it saves.
 template <int C>
 __device__ __forceinline__ double sum_ranges_by(const double* __restrict__ pp, int S, int stride) {
   double v = 0.0;
@@ -209,9 +209,7 @@ __device__ __forceinline__ double sum_ranges_by(const double* __restrict__ pp, i
 }
 __device__ __forceinline__ double sum_ranges(const double* __restrict__ part, int b, int S,
                                              int stride, int i) {
-  const double* pp = part + (size_t)b * S * stride + i;
-  return S <= 8 ? sum_ranges_by<8>(pp, S, stride)
-       : S <= 16 ? sum_ranges_by<16>(pp, S, stride) : sum_ranges_by<32>(pp, S, stride);
+  return sum_ranges_by<8>(part + (size_t)b * S * stride + i, S, stride);
 }
 size_t gemv_part_bytes(int out, int in, int batch);
 hipError_t launch_gemv_multi(const LinSeg* segs, int nseg, int in, const uint16_t* x, int batch,
