@@ -13,6 +13,7 @@
 // dword m of a fragment holds columns (m, m + 16): κ = 2m + hh <-> column
 // m + 16 hh. A and B use the same κ order, so the MFMA sums the same pairs.
 #include <algorithm>
+#include <type_traits>
 
 #include "rabit_internal.h"
 
@@ -110,108 +111,143 @@ __global__ void k_gemm_prep_h(const uint16_t* __restrict__ h, int in, int Kp, Ge
   ws.hpairs[idx] = lo | (hi << 16);
 }
 
-// 128 x 128 output tile per workgroup and K slice blockIdx.z, 4 waves in
-// 2 x 2 (64 x 64 per wave), 64 columns per step. The next step's operands are
+// 128 x 128 output tile per workgroup and K slice blockIdx.z, 64 columns per
+// step. Wave w owns output columns [32 w, 32 w + 32) for all 128 rows, and
+// builds its own ±h_p fragments in registers from the plane words (no LDS for
+// the weights): lane (fr, fg) of fragment (p, j, sub) holds rows κ = 8 fg ..
+// 8 fg + 7 of column n0 + 32 w + 16 j + fr, i.e. pairs (m, m + 16), m = 4 fg + c,
+// of the 32-column block. X goes through a double-buffered LDS tile (one
+// barrier per step). The next step's X rows, plane words and h pairs are
 // loaded into registers while the current step runs on the matrix cores.
-__global__ __launch_bounds__(256) void k_gemm(const uint4* __restrict__ planes,
+__global__ __launch_bounds__(256, 2) void k_gemm(const uint4* __restrict__ planes,
                                               const uint16_t* __restrict__ g, int out, int M,
                                               int Kp, int ksteps, GemmWs ws, void* Y, int y_dtype) {
   const int n0 = blockIdx.x * kBN, m0 = blockIdx.y * kBM;
-  const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63;
-  const int wm = (wv >> 1) * 64, wn = (wv & 1) * 64;
+  const int tid = threadIdx.x, l = tid & 63;
+  const int wn = __builtin_amdgcn_readfirstlane(tid >> 6) * 32;
   const int KG = Kp / 128;
+  const int nb = Kp / 32;
   const int out_pad = row_groups(out) * 64;
   const int ks0 = blockIdx.z * ksteps, ks1 = min(Kp / kBK, ks0 + ksteps);
-  // 16-row MFMA tiles of this wave that hold rows of X (uniform)
-  const int mtiles = __builtin_amdgcn_readfirstlane(min(4, max(0, (M - m0 - wm + 15) / 16)));
+  // 16-row MFMA tiles of the workgroup that hold rows of X (uniform)
+  const int mtiles = __builtin_amdgcn_readfirstlane(min(8, max(0, (M - m0 + 15) / 16)));
+  const int fr = l & 15, fg = l >> 4;
 
-  __shared__ __align__(16) uint32_t sA[kBM * kLdsStride];
-  __shared__ __align__(16) uint32_t sB[2][kBN * kLdsStride];
+  __shared__ __align__(16) uint32_t sA[2][kBM * kLdsStride];
+  __shared__ __align__(16) uint32_t sH[2][2][2][16];  // [buffer][p][sub]: the step's h pairs
 
-  v4f acc[2][4][4];
+  v4f acc[2][8][2];
 #pragma unroll
   for (int p = 0; p < 2; ++p)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[p][i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < 2; ++j) acc[p][i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-  // B loader: thread -> (row n0 + (tid & 127), path tid >> 7): two words
-  const int bn = min(n0 + (tid & 127), out_pad - 1), bp = tid >> 7;
-  const uint32_t* wsrc = (const uint32_t*)(planes + unit_index(bn >> 6, 0, bp, bn & 63, KG));
   // A loader: thread -> row m0 + (tid >> 1), half (tid & 1) of the 64 columns
   const int am = m0 + (tid >> 1), ah = tid & 1;
   const bool avalid = am < M;
   const uint4* asrc = (const uint4*)(ws.xh + (size_t)min(am, M - 1) * Kp) + ah * 4;
-  const uint4* hsrc = (const uint4*)(ws.hpairs + (size_t)bp * (Kp / 32) * 16);
+  // B: the words of rows n0 + wn + 16 j + fr (clamped into the padded rows)
+  const uint32_t* wsrc[2][2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int bn = min(n0 + wn + 16 * j + fr, out_pad - 1);
+      wsrc[p][j] = (const uint32_t*)(planes + unit_index(bn >> 6, 0, p, bn & 63, KG));
+    }
+  // h pairs of the step, staged through LDS by threads 0..63: (p, sub, pair)
+  const int hp = (tid >> 5) & 1, hs = (tid >> 4) & 1, hq = tid & 15;
+  const uint32_t* hsrc = ws.hpairs + (size_t)hp * nb * 16 + hs * 16 + hq;
 
   uint4 ra[4];
-  uint2 rw;
-  uint4 rh[8];
+  uint2 rw[2][2];   // [p][j]: words 2 ks, 2 ks + 1 of the row (the two 32-column blocks)
+  uint32_t rh = 0;
   auto load = [&](int ks) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) ra[q] = asrc[(size_t)ks * 8 + q];
-    // words 2 ks, 2 ks + 1 of the row: unit kg = ks / 2, dwords 2 (ks & 1) ..
-    rw = *(const uint2*)(wsrc + (size_t)(ks >> 1) * 128 * 4 + 2 * (ks & 1));
 #pragma unroll
-    for (int q = 0; q < 8; ++q) rh[q] = hsrc[(size_t)ks * 8 + q];  // 2 blocks x 16 pairs
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) rw[p][j] = *(const uint2*)(wsrc[p][j] + (size_t)(ks >> 1) * 128 * 4 + 2 * (ks & 1));
+    if (tid < 64) rh = hsrc[(size_t)ks * 32];
   };
-  if (ks0 < ks1) load(ks0);
-
-  for (int ks = ks0; ks < ks1; ++ks) {
-    __syncthreads();  // the previous step's LDS reads are done
-    uint32_t* da = sA + (tid >> 1) * kLdsStride + ah * 16;
+  auto store_a = [&](int buf) {
+    uint32_t* da = sA[buf] + (tid >> 1) * kLdsStride + ah * 16;
 #pragma unroll
     for (int q = 0; q < 4; ++q) *(uint4*)(da + 4 * q) = avalid ? ra[q] : make_uint4(0, 0, 0, 0);
-    uint32_t* db = sB[bp] + (tid & 127) * kLdsStride;
+    if (tid < 64) sH[buf][hp][hs][hq] = rh;
+  };
+  if (ks0 < ks1) {
+    load(ks0);
+    store_a(0);
+  }
+  __syncthreads();
+
+  // the main loop, in a copy without per-tile guards for full 128-row tiles
+  // (a guard per matrix op splits the loop into small blocks that the
+  // scheduler cannot overlap)
+  auto run = [&](auto full_tag) {
+  constexpr bool kFull = decltype(full_tag)::value;
+  for (int ks = ks0; ks < ks1; ++ks) {
+    const int buf = (ks - ks0) & 1;
+    uint2 cw[2][2];
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      const uint32_t w = blk ? rw.y : rw.x;
+    for (int p = 0; p < 2; ++p)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint4 hh = rh[blk * 4 + q];
-        uint4 e;
-        e.x = hh.x ^ ((w << (15 - (4 * q + 0))) & 0x80008000u);
-        e.y = hh.y ^ ((w << (15 - (4 * q + 1))) & 0x80008000u);
-        e.z = hh.z ^ ((w << (15 - (4 * q + 2))) & 0x80008000u);
-        e.w = hh.w ^ ((w << (15 - (4 * q + 3))) & 0x80008000u);
-        *(uint4*)(db + 16 * blk + 4 * q) = e;
-      }
-    }
-    __syncthreads();
+      for (int j = 0; j < 2; ++j) cw[p][j] = rw[p][j];
     if (ks + 1 < ks1) load(ks + 1);  // in flight during the matrix ops
 
-    const int fr = l & 15, fg = l >> 4;
+    const uint32_t* a0 = sA[buf] + fr * kLdsStride + 4 * fg;
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
-      v8h fa[4];
+      v8h fa[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) fa[i] = *(const v8h*)(sA + (wm + 16 * i + fr) * kLdsStride + 16 * sub + 4 * fg);
+      for (int i = 0; i < 8; ++i) fa[i] = *(const v8h*)(a0 + 16 * i * kLdsStride + 16 * sub);
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
+        const uint4 hh = *(const uint4*)(&sH[buf][p][sub][4 * fg]);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const v8h fb = *(const v8h*)(sB[p] + (wn + 16 * j + fr) * kLdsStride + 16 * sub + 4 * fg);
+        for (int j = 0; j < 2; ++j) {
+          const uint32_t w = sub ? cw[p][j].y : cw[p][j].x;
+          // dword c holds columns (m, m + 16), m = 4 fg + c: the sign bits are
+          // bits m and m + 16 of the word, moved to bits 15 and 31
+          const int sh = 15 - 4 * fg;
+          uint4 e;
+          e.x = hh.x ^ ((w << sh) & 0x80008000u);
+          e.y = hh.y ^ ((w << (sh - 1)) & 0x80008000u);
+          e.z = hh.z ^ ((w << (sh - 2)) & 0x80008000u);
+          e.w = hh.w ^ ((w << (sh - 3)) & 0x80008000u);
+          const v8h fb = __builtin_bit_cast(v8h, e);
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (i < mtiles) acc[p][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[i], fb, acc[p][i][j], 0, 0, 0);
+          for (int i = 0; i < 8; ++i)
+            if (kFull || i < mtiles)
+              acc[p][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[i], fb, acc[p][i][j], 0, 0, 0);
         }
       }
     }
+    if (ks + 1 < ks1) store_a(buf ^ 1);
+    __syncthreads();
   }
+  };
+  if (mtiles == 8)
+    run(std::true_type{});
+  else
+    run(std::false_type{});
 
   // epilogue: C[i][j] of a 16x16 tile: lane l, reg r -> row 4(l/16)+r, col l%16
   const bool split = gridDim.z > 1;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < 2; ++j) {
     const int n = n0 + wn + 16 * j + (l & 15);
     if (n >= out) continue;
     const float g0 = f16_bits_to_f32(g[n]), g1 = f16_bits_to_f32(g[out + n]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 8; ++i) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int m = m0 + wm + 16 * i + 4 * (l >> 4) + r;
+        const int m = m0 + 16 * i + 4 * (l >> 4) + r;
         if (m >= M) continue;
         const float v = g0 * acc[0][i][j][r] + g1 * acc[1][i][j][r];
         if (split) {
