@@ -16,10 +16,13 @@ statistics. Steps are replayed from a HIP graph.
 
 value = plane bytes per step / step time. The roofline object describes the
 dominant kernel, k_gemv<1> (the plane-streaming GEMV): the bench times its two
-launch shapes of the step (gate+up, down) back to back with HIP events on the
-launch stream, over all layers, and divides algorithmic bytes by the average
+launch shapes of the step (gate+up, down) back to back, over all layers,
+captured in a HIP graph and replayed between HIP events on the launch stream,
+and divides algorithmic bytes by the average
 launch duration. traffic comes from the committed rocprofv3 counter summary
-when it was taken on the current GEMV source, else null.
+when it was taken on the current GEMV source, else null. stream_ceiling is a
+practical ceiling measured in the same run: a plain read-only stream of the
+same number of plane bytes as each launch, and a large device copy.
 
 Printed: one JSON line (stdout). Diagnostics go to stderr.
 """
@@ -140,31 +143,68 @@ def cpu_baseline_mlp(shapes, budget_s):
     }
 
 
+def graph_ms(torch, fn, reps):
+    """fn() enqueues a sequence of launches on the current stream; it is
+    captured once into a HIP graph and replayed `reps` times between two
+    events, so that the launches run back to back on the GPU (Python-side
+    launch overhead would otherwise leave gaps). Returns ms per replay."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()  # eager warm-up
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    del g
+    return e0.elapsed_time(e1) / reps
+
+
+def stream_read_ms(rabit, torch, nbytes, reps=8):
+    """Practical ceiling: a plain read-only stream of nbytes (rabit_stream_read,
+    16-byte loads like the GEMV's plane loads) over rotating cold buffers
+    (>= 512 MiB in total), graph-replayed back to back; ms per call."""
+    n = max(16, nbytes // 16 * 16)
+    copies = max(2, -(-(512 << 20) // n))
+    bufs = [torch.ones(n, dtype=torch.uint8, device="cuda") for _ in range(copies)]
+    sink = torch.empty(4, dtype=torch.int32, device="cuda")
+
+    def run():
+        for b in bufs:
+            rabit.stream_read(b, sink)
+    ms = graph_ms(torch, run, reps) / copies
+    del bufs
+    return ms
+
+
 def time_gemv_launches(rabit, torch, layers, hidden, ffn, reps=5):
     """Average duration of the step's two k_gemv<1> launch shapes, each timed
-    as `len(layers)` back-to-back launches (one per layer, cold planes) between
-    two events on the launch stream; median over `reps`."""
-    stream = torch.cuda.current_stream()
+    as `len(layers)` back-to-back launches (one per layer, cold planes),
+    captured in a HIP graph and replayed `reps` times between two events on
+    the launch stream."""
     x_h = torch.randn(1, hidden, device="cuda").to(torch.bfloat16)
     x_f = torch.randn(1, ffn, device="cuda").to(torch.bfloat16)
     ws_gu = rabit.gemv_multi_workspace([layers[0]["gate"], layers[0]["up"]], 1)
     ws_d = rabit.gemv_workspace(layers[0]["down"], 1)
-    res = {"gate+up": [], "down": []}
-    for r in range(reps + 1):
-        for kind in ("gate+up", "down"):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            for L in layers:
-                if kind == "gate+up":
-                    rabit.gemv_partial_multi([L["gate"], L["up"]], x_h, ws_gu)
-                else:
-                    rabit.gemv_partial(L["down"], x_f, ws_d)
-            b.record(stream)
-            b.synchronize()
-            if r > 0:  # the first pass warms up
-                res[kind].append(a.elapsed_time(b) / len(layers))
-    med = {k: sorted(v)[len(v) // 2] for k, v in res.items()}
-    return med, res
+
+    def gate_up():
+        for L in layers:
+            rabit.gemv_partial_multi([L["gate"], L["up"]], x_h, ws_gu)
+
+    def down():
+        for L in layers:
+            rabit.gemv_partial(L["down"], x_f, ws_d)
+    med = {kind: graph_ms(torch, fn, reps) / len(layers) for kind, fn in (("gate+up", gate_up), ("down", down))}
+    return med, dict(med)
 
 
 def main():
@@ -278,6 +318,33 @@ def main():
     log(f"k_gemv<1>: gate+up {med['gate+up'] * 1e3:.2f} us, down {med['down'] * 1e3:.2f} us per launch "
         f"-> {achieved:.1f} GB/s algorithmic")
     traffic = committed_traffic()
+    # practical ceilings at the two launch sizes (planes only) and for a large copy
+    gu_planes = 2 * shapes["gate"][0] * shapes["gate"][1] // 4
+    d_planes = shapes["down"][0] * shapes["down"][1] // 4
+    st_gu, st_d = stream_read_ms(rabit, torch, gu_planes), stream_read_ms(rabit, torch, d_planes)
+    big_a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+    big_b = torch.empty_like(big_a)
+    big_b.copy_(big_a)
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(10):
+        big_b.copy_(big_a)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * (256 << 20) * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del big_a, big_b
+    stream = {
+        "read_only_us": {"gate+up planes": round(st_gu * 1e3, 2), "down planes": round(st_d * 1e3, 2)},
+        "read_only_gbs": {"gate+up planes": round(gu_planes / (st_gu * 1e-3) / 1e9, 1),
+                          "down planes": round(d_planes / (st_d * 1e-3) / 1e9, 1)},
+        "copy_256MiB_gbs_read_plus_write": round(copy_gbs, 1),
+        "gemv_launch_over_read_only": {"gate+up": round(med["gate+up"] / st_gu, 3),
+                                       "down": round(med["down"] / st_d, 3)},
+        "note": "rabit_stream_read (16-byte loads) over cold rotating buffers of the same byte size as each "
+                "launch's planes; copy is torch copy_ (read + write bytes)",
+    }
+    log(f"streaming ceiling: {stream}")
 
     pk = pack_ms[3:] or pack_ms
     pk_ms = sum(p[3] for p in pk) / len(pk)
@@ -329,6 +396,7 @@ def main():
                      "kernel": "k_gemv<1>", "avg_launch_us": round(kavg_ms * 1e3, 3),
                      "launch_us": {k: round(v * 1e3, 3) for k, v in med.items()},
                      "alg_bytes_per_launch": int(alg_bytes)},
+        "stream_ceiling": stream,
         "derive_pack": derive,
         "cpu_baseline": cpu,
     }

@@ -425,6 +425,12 @@ int rabit_decode_step(const rabit_decoder_cfg* cfg, const rabit_layer* layers, c
   return dev_status(e);
 }
 
+int rabit_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+  if (!src || !sink) return RABIT_EINVAL;
+  if (!aligned16(src) || !aligned16(sink) || bytes % 16) return RABIT_EALIGN;
+  return dev_status(launch_stream_read(src, bytes, sink, (hipStream_t)stream));
+}
+
 int rabit_test_f64_to_16(const double* in, uint16_t* out, int32_t n, int32_t bf16, void* stream) {
   if (!in || !out || n < 1) return RABIT_EINVAL;
   return dev_status(launch_test_f64_to_16(in, out, n, bf16, (hipStream_t)stream));

@@ -241,5 +241,6 @@ hipError_t launch_reduce_attn(const double* pq, const double* pk, const double* 
                               int in_of_part, float* qk, uint16_t* attn, int batch, int n_heads,
                               int n_kv_heads, int head_dim, hipStream_t st);
 hipError_t launch_test_f64_to_16(const double* in, uint16_t* out, int n, int bf16, hipStream_t st);
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t st);
 
 }  // namespace rabit

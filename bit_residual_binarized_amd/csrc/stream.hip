@@ -1,0 +1,40 @@
+// Measurement hook: a plain read-only stream of device memory, to measure the
+// practical HBM ceiling next to the plane-streaming GEMV at the same sizes.
+#include "rabit_internal.h"
+
+namespace rabit {
+
+namespace {
+
+constexpr int kPerThread = 8;  // 16-byte loads in flight per thread
+
+// Workgroup b reads the 16-byte units [b * 2048, (b + 1) * 2048) (the last one
+// fewer): unit b * 2048 + i * 256 + tid for i < 8, so that each load
+// instruction covers 4 KiB of consecutive memory.
+__global__ __launch_bounds__(256) void k_stream_read(const uint4* __restrict__ src, size_t n16,
+                                                     uint32_t* __restrict__ sink) {
+  const size_t base = (size_t)blockIdx.x * 256 * kPerThread + threadIdx.x;
+  uint4 v[kPerThread];
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i) {
+    const size_t u = base + (size_t)i * 256;
+    v[i] = src[u < n16 ? u : n16 - 1];
+  }
+  uint32_t acc = 0;
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i) acc ^= v[i].x ^ v[i].y ^ v[i].z ^ v[i].w;
+  // keeps the loads; the value written is unspecified
+  if (acc == 0x9e3779b9u) *sink = acc;
+}
+
+}  // namespace
+
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t st) {
+  const size_t n16 = bytes / 16;
+  if (n16 == 0) return hipSuccess;
+  const size_t blocks = (n16 + 256 * kPerThread - 1) / (256 * kPerThread);
+  hipLaunchKernelGGL(k_stream_read, dim3((unsigned)blocks), dim3(256), 0, st, (const uint4*)src, n16, sink);
+  return hipGetLastError();
+}
+
+}  // namespace rabit

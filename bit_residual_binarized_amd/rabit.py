@@ -35,7 +35,7 @@ EXPORTS = [
     "rabit_gemm_workspace_bytes", "rabit_pack", "rabit_unpack", "rabit_gemv", "rabit_gemm",
     "rabit_decode_workspace_bytes", "rabit_decode_step", "rabit_status_string",
     "rabit_layout_version", "rabit_test_f64_to_16", "rabit_gemv_partial", "rabit_gemv_reduce",
-    "rabit_gemv_partial_multi",
+    "rabit_gemv_partial_multi", "rabit_stream_read",
 ]
 
 
@@ -101,6 +101,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "rabit_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "rabit_layout_version": (i32, []),
         "rabit_test_f64_to_16": (ctypes.c_int, [vp, vp, i32, i32, vp]),
+        "rabit_stream_read": (ctypes.c_int, [vp, sz, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -327,6 +328,18 @@ def decode_step(cfg: DecoderCfg, layers, x: torch.Tensor, out: torch.Tensor | No
                                  _ptr(workspace), workspace.numel(), _stream(stream)),
            "rabit_decode_step")
     return out
+
+
+def stream_read(t: torch.Tensor, sink: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Measurement hook: read all bytes of the device tensor t once (see
+    rabit_stream_read); returns the sink buffer."""
+    lib = load()
+    assert t.is_cuda and t.is_contiguous()
+    if sink is None:
+        sink = torch.empty(4, dtype=torch.int32, device=t.device)
+    _check(lib.rabit_stream_read(_ptr(t), t.numel() * t.element_size(), _ptr(sink), _stream(stream)),
+           "rabit_stream_read")
+    return sink
 
 
 def test_f64_to_16(v: torch.Tensor, bf16: bool, stream=None) -> torch.Tensor:

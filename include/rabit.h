@@ -247,6 +247,19 @@ int32_t rabit_layout_version(void);
  */
 int rabit_test_f64_to_16(const double *in, uint16_t *out, int32_t n, int32_t bf16, void *stream);
 
+/*
+ * Measurement hook: reads `bytes` of device memory once with 16-byte loads
+ * (eight in flight per thread, each load instruction covering 4 KiB of
+ * consecutive memory) and keeps nothing. It gives the practical HBM ceiling
+ * for a read-only stream of a given size, next to the GEMV (which streams
+ * its planes the same way). Not part of the method.
+ * src   device, 16-byte aligned; bytes a multiple of 16 (0: nothing runs).
+ * sink  device uint32, 16-byte aligned; may be overwritten with an
+ *       unspecified value.
+ * Errors: RABIT_EINVAL (null pointer), RABIT_EALIGN (alignment or bytes).
+ */
+int rabit_stream_read(const void *src, size_t bytes, uint32_t *sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

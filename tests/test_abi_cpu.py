@@ -148,3 +148,13 @@ def test_decode_cfg_errors(lib):
     assert lib.rabit_decode_step(ctypes.byref(cc), arr, x, 1, out, ws, 1 << 40, None) == rabit.RABIT_ESHAPE
     mlp = rabit.DecoderCfg(hidden=64, ffn=96, mlp_only=True).c()
     assert lib.rabit_decode_step(ctypes.byref(mlp), arr, x, 1, out, ws, 1 << 40, None) == rabit.RABIT_ESHAPE
+
+
+def test_stream_read_errors(lib):
+    P, Q = ctypes.c_void_p(1 << 20), ctypes.c_void_p(2 << 20)
+    assert lib.rabit_stream_read(None, 64, Q, None) == rabit.RABIT_EINVAL
+    assert lib.rabit_stream_read(P, 64, None, None) == rabit.RABIT_EINVAL
+    assert lib.rabit_stream_read(ctypes.c_void_p((1 << 20) + 8), 64, Q, None) == rabit.RABIT_EALIGN
+    assert lib.rabit_stream_read(P, 64, ctypes.c_void_p((2 << 20) + 4), None) == rabit.RABIT_EALIGN
+    assert lib.rabit_stream_read(P, 72, Q, None) == rabit.RABIT_EALIGN
+    assert lib.rabit_stream_read(P, 0, Q, None) == rabit.RABIT_OK  # nothing runs

@@ -374,3 +374,12 @@ def test_decode_attention_block(gpu_lib, batch):
     ok, nbad = bf16_close(y, ref)
     say("  normwise err", err, "elements outside bound", nbad)
     assert ok
+
+
+def test_stream_read_runs(gpu_lib):
+    # the measurement hook reads a buffer (whole tiles and a ragged tail)
+    say("stream read hook")
+    t = torch.ones(3001 * 4 + (64 << 18), dtype=torch.int32, device="cuda")
+    sink = gpu_lib.stream_read(t)
+    torch.cuda.synchronize()
+    assert sink.numel() == 4
