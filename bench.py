@@ -217,7 +217,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of graph replay")
     ap.add_argument("--workload", default="mlp7b",
-                    choices=["mlp7b", "layer4096", "llama3-8b", "gemm", "llama70b"],
+                    choices=["mlp7b", "layer4096", "llama3-8b", "gemm", "llama70b", "table7"],
                     help="mlp7b (default): the headline decode workload; the others measure the "
                          "remaining configurations (one JSON line each)")
     args = ap.parse_args()
@@ -235,7 +235,7 @@ def main():
     torch.cuda.set_device(0)
     if args.workload != "mlp7b":
         extra = {"layer4096": bench_layer4096, "llama3-8b": bench_llama3_8b, "gemm": bench_gemm,
-                 "llama70b": bench_llama70b}[args.workload]
+                 "llama70b": bench_llama70b, "table7": bench_table7}[args.workload]
         print(json.dumps(extra(args, rabit, torch)), flush=True)
         return
     hidden, ffn = 4096, 11008
@@ -422,14 +422,13 @@ def _pack_layer(rabit, torch, out, inp, seed, ws_holder):
     return pl, e0.elapsed_time(e1)
 
 
-def _events_ms(torch, fn, n):
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for i in range(n):
-        fn(i)
-    b.record()
-    b.synchronize()
-    return a.elapsed_time(b) / n
+def _events_ms(torch, fn, n, reps=3):
+    """ms per call of fn(i), i = 0..n-1, captured in a HIP graph and replayed
+    back to back (Python launch overhead excluded)."""
+    def run():
+        for i in range(n):
+            fn(i)
+    return graph_ms(torch, run, reps) / n
 
 
 def _line(metric, value, unit, config, higher=True, **kw):
@@ -467,6 +466,59 @@ def bench_layer4096(args, rabit, torch):
                            "frac": round(alg / (part * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                            "kernel": "k_gemv<1>"},
                  derive_pack={"ms": round(pk, 4), "gbs": round(8.25 * 4096 * 4096 / (pk * 1e-3) / 1e9, 1)})
+
+
+def bench_table7(args, rabit, torch):
+    """The shapes of the pages' kernel-latency table (Llama-2 7B and 13B
+    projections) at batch 1: the residual-binary GEMV (rabit_gemv, both
+    launches) against a dense bf16 GEMV (torch.mm on a contiguous [in][out]
+    bf16 weight, hipBLASLt), each cold (rotating copies over >= 512 MiB) and
+    warm (one copy, as the pages measured). Context only: the pages' figures
+    are from another GPU."""
+    from synth.inputs import act_bf16, seed_w, seed_x
+    shapes = [(4096, 4096, "q_proj 7B"), (11008, 4096, "gate_proj 7B"), (5120, 5120, "q_proj 13B"),
+              (13824, 5120, "gate_proj 13B")]
+    runs, wsh, speed = {}, [None], []
+    for si, (out, inp, name) in enumerate(shapes):
+        pl, _ = _pack_layer(rabit, torch, out, inp, seed_w(6, si, "q"), wsh)
+        pb = rabit.planes_bytes(out, inp)
+        n = max(2, -(-(512 << 20) // pb))
+        layers = [pl]
+        for _ in range(n - 1):
+            c = rabit.PackedLayer.empty(out, inp)
+            c.planes.copy_(pl.planes)
+            c.g.copy_(pl.g)
+            c.h.copy_(pl.h)
+            layers.append(c)
+        x = act_bf16(1, inp, seed_x(6, 1)).cuda()
+        ws = rabit.gemv_workspace(pl, 1)
+        y = torch.empty(1, out, device="cuda")
+        ours_cold = _events_ms(torch, lambda i: rabit.gemv(layers[i % n], x, y=y, workspace=ws), n)
+        ours_warm = _events_ms(torch, lambda i: rabit.gemv(layers[0], x, y=y, workspace=ws), 64)
+        del layers
+        wb = out * inp * 2
+        nd = max(2, -(-(512 << 20) // wb))
+        dense = [torch.randn(inp, out, device="cuda").mul_(0.02).to(torch.bfloat16) for _ in range(nd)]
+        yd = torch.empty(1, out, device="cuda", dtype=torch.bfloat16)
+        dense_cold = _events_ms(torch, lambda i: torch.mm(x, dense[i % nd], out=yd), nd)
+        dense_warm = _events_ms(torch, lambda i: torch.mm(x, dense[0], out=yd), 64)
+        del dense
+        sp = dense_cold / ours_cold
+        speed.append(sp)
+        runs[f"{out}x{inp} {name}"] = {
+            "rabit_us_cold": round(ours_cold * 1e3, 2), "rabit_us_warm": round(ours_warm * 1e3, 2),
+            "dense_bf16_us_cold": round(dense_cold * 1e3, 2), "dense_bf16_us_warm": round(dense_warm * 1e3, 2),
+            "speedup_cold": round(sp, 2), "speedup_warm": round(dense_warm / ours_warm, 2),
+            "rabit_plane_gbs_cold": round(pb / (ours_cold * 1e-3) / 1e9, 1),
+            "dense_gbs_cold": round(wb / (dense_cold * 1e-3) / 1e9, 1)}
+        log(f"{name} {out}x{inp}: {runs[f'{out}x{inp} {name}']}")
+    gm = 1.0
+    for v in speed:
+        gm *= v
+    gm **= 1.0 / len(speed)
+    return _line("Residual-binary GEMV speed-up over dense bf16 GEMV, batch 1, cold (geometric mean over the "
+                 "pages' 7B/13B shapes)", round(gm, 3), "x", {"workload": "table7-shapes-b1"},
+                 dtype="fp4xfp6 vs bf16", runs=runs)
 
 
 def _decoder_layers(rabit, torch, cfg_id, H, F, kv, n_layers):
