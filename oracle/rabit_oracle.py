@@ -1,4 +1,4 @@
-"""Plain float64 CPU oracle for the RaBiT 2-path residual-binary hot path.
+"""Plain float64 CPU oracle for the RaBiT residual-binary hot path (2 paths, and 3 for the 3-bit variant).
 
 TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``). Slow and obvious by
 design; numpy float64 (plus ``fractions.Fraction`` for tiny exact cases).
@@ -10,6 +10,9 @@ Accurate and Efficient LLMs", arXiv 2602.05367):
 * paper §4.1 "Multi-bit Approximation via Stacking" eq.  W_hat^(k) = Σ_i g_i ⊙ B_i ⊙ h_i
 * paper §4.2 "The Coupled Forward Pass", steps 1-3: B_1 = sign(W_FP),
   R_1 = W_FP − W_hat_1, B_2 = sign(R_1)
+* paper §1 and abstract: each successive path is derived from the residual
+  error of its predecessor; App. E.1 "Weight Packing" packs 2-bit (two
+  binary weights) and 3-bit (three) models
 * paper §4.3 (text under eq. for preconditioning) maps g to the output side
   and h to the input side
 * paper App. E.1 "Weight Packing": 32 columns per uint32, +1 -> 0, -1 -> 1
@@ -27,6 +30,9 @@ Readings where the pages are silent (each is listed in the design doc):
   single direct round-to-nearest-even.
 * R_1 is float32 with one rounding: R = fl32(W − B_1·g_1·h_1); the product
   g_1·h_1 of two fp16 values is exact in float32.
+* Three paths (the 3-bit variant): the recursion continues one step,
+  R_2 = fl32(R_1 − B_2·g_2·h_2), B_3 = sign(R_2), with g_3, h_3 the mean |R_2|
+  (or given); the device buffer holds the third plane as path p = 2.
 * GEMV/GEMM outputs are float64 here; the GPU returns float32.
 
 Pins (tests/test_oracle_*.py): brute-force argmin on 4x8 with Fraction (B_1,
@@ -198,28 +204,48 @@ def meanabs_scales(m_abs: np.ndarray):
 
 
 class Derived:
-    """Frozen artefact of one layer: sign bits and fp16 scales of both paths."""
+    """Frozen artefact of one layer: sign bits and fp16 scales of each path
+    (two, or three for the 3-bit variant)."""
 
-    def __init__(self, s1, s2, g1, h1, g2, h2, r=None):
+    def __init__(self, s1, s2, g1, h1, g2, h2, r=None, s3=None, g3=None, h3=None, r2=None):
         self.s1, self.s2 = s1, s2          # bool [out][in], True = -1
         self.g1, self.h1 = g1, h1          # float16 [out], [in]
         self.g2, self.h2 = g2, h2
         self.r = r                         # float32 residual R_1 (for pins)
+        self.s3, self.g3, self.h3 = s3, g3, h3   # third path, or None
+        self.r2 = r2                       # float32 residual R_2 (three paths)
 
     @property
     def shape(self):
         return self.s1.shape
 
+    @property
+    def n_paths(self):
+        return 2 if self.s3 is None else 3
 
-def derive(w, mode: str = "meanabs", g1=None, h1=None, g2=None, h2=None) -> Derived:
-    """Coupled derivation of both binary cores from one shared weight.
+    @property
+    def paths(self):
+        """[(s_p, g_p, h_p)] in path order."""
+        ps = [(self.s1, self.g1, self.h1), (self.s2, self.g2, self.h2)]
+        if self.s3 is not None:
+            ps.append((self.s3, self.g3, self.h3))
+        return ps
+
+
+def derive(w, mode: str = "meanabs", g1=None, h1=None, g2=None, h2=None, n_paths: int = 2,
+           g3=None, h3=None) -> Derived:
+    """Coupled derivation of the binary cores from one shared weight.
 
     paper §4.2 step 1: B_1 = sign(W_FP), with path-1 scales g_1, h_1;
     step 2: R_1 = W_FP − g_1 ⊙ B_1 ⊙ h_1; step 3: B_2 = sign(R_1).
+    With n_paths = 3 the same step once more (each path corrects the residual
+    of its predecessor, paper §1): R_2 = R_1 − g_2 ⊙ B_2 ⊙ h_2, B_3 = sign(R_2).
     mode "meanabs": g_p, h_p are the mean |.| of the matrix being binarised
-    (W for path 1, R_1 for path 2). mode "given": g_1, h_1 (and g_2, h_2,
-    which do not affect the bits) are supplied by the caller.
+    (W for path 1, R_1 for path 2, R_2 for path 3). mode "given": the scales
+    are supplied by the caller (the last path's scales do not affect the bits).
     """
+    if n_paths not in (2, 3):
+        raise ValueError(n_paths)
     w = np.asarray(w, dtype=np.float32)
     out, inp = w.shape
     s1 = w < 0
@@ -242,7 +268,19 @@ def derive(w, mode: str = "meanabs", g1=None, h1=None, g2=None, h2=None) -> Deri
     else:
         g2 = np.asarray(g2 if g2 is not None else np.zeros(out), dtype=np.float16)
         h2 = np.asarray(h2 if h2 is not None else np.zeros(inp), dtype=np.float16)
-    return Derived(s1, s2, g1, h1, g2, h2, r)
+    if n_paths == 2:
+        return Derived(s1, s2, g1, h1, g2, h2, r)
+    # third path: the residual of path 2, with the same single float32 rounding
+    e2 = g2.astype(np.float32)[:, None] * h2.astype(np.float32)[None, :]
+    b2e2 = np.where(s2, -e2, e2).astype(np.float32)
+    r2 = (r - b2e2).astype(np.float32)
+    s3 = r2 < 0
+    if mode == "meanabs":
+        g3, h3 = meanabs_scales(np.abs(r2).astype(np.float64))
+    else:
+        g3 = np.asarray(g3 if g3 is not None else np.zeros(out), dtype=np.float16)
+        h3 = np.asarray(h3 if h3 is not None else np.zeros(inp), dtype=np.float16)
+    return Derived(s1, s2, g1, h1, g2, h2, r, s3, g3, h3, r2)
 
 
 # ---------------------------------------------------------------------------
@@ -274,20 +312,22 @@ def planes_bytes(out: int, inp: int, n_paths: int = 2) -> int:
     return rg * kg * n_paths * 64 * 16
 
 
-def device_planes(words1: np.ndarray, words2: np.ndarray, out: int, inp: int) -> np.ndarray:
-    """Device layout of the two planes, written from the header's description.
+def device_planes(words1: np.ndarray, words2: np.ndarray, out: int, inp: int,
+                  words3: np.ndarray | None = None) -> np.ndarray:
+    """Device layout of the planes, written from the header's description.
 
     The buffer is a sequence of 16-byte units indexed (rg, kg, p, r) in
     row-major order with rg = row group of 64 rows, kg = group of 128 columns,
-    p = path (0, 1) and r = row inside the group (0..63). The unit holds, as
-    four little-endian uint32, the canonical words 4*kg + 0..3 of row
+    p = path (0 .. n_paths − 1) and r = row inside the group (0..63). The unit
+    holds, as four little-endian uint32, the canonical words 4*kg + 0..3 of row
     64*rg + r of path p. Rows >= out and words beyond the last are zero.
     Returns a flat uint32 array.
     """
     rg = (out + 63) // 64
     kg = (inp + 127) // 128
-    buf = np.zeros((rg, kg, 2, 64, 4), dtype=np.uint32)
-    for p, words in enumerate((words1, words2)):
+    planes = (words1, words2) if words3 is None else (words1, words2, words3)
+    buf = np.zeros((rg, kg, len(planes), 64, 4), dtype=np.uint32)
+    for p, words in enumerate(planes):
         rows, nw = words.shape
         for i in range(rows):
             g, r = divmod(i, 64)
@@ -296,17 +336,17 @@ def device_planes(words1: np.ndarray, words2: np.ndarray, out: int, inp: int) ->
     return buf.reshape(-1)
 
 
-def device_planes_to_words(buf: np.ndarray, out: int, inp: int):
-    """Inverse of ``device_planes`` (returns canonical words of both planes)."""
+def device_planes_to_words(buf: np.ndarray, out: int, inp: int, n_paths: int = 2):
+    """Inverse of ``device_planes`` (returns canonical words of every plane)."""
     rg = (out + 63) // 64
     kg = (inp + 127) // 128
     nw = (inp + 31) // 32
-    b = np.asarray(buf, dtype=np.uint32).reshape(rg, kg, 2, 64, 4)
+    b = np.asarray(buf, dtype=np.uint32).reshape(rg, kg, n_paths, 64, 4)
     res = []
-    for p in range(2):
+    for p in range(n_paths):
         t = b[:, :, p].transpose(0, 2, 1, 3).reshape(rg * 64, kg * 4)
         res.append(t[:out, :nw].copy())
-    return res[0], res[1]
+    return tuple(res)
 
 
 # ---------------------------------------------------------------------------
@@ -314,14 +354,12 @@ def device_planes_to_words(buf: np.ndarray, out: int, inp: int):
 # scaling"; App. E.1 "per-path parallelizable")
 # ---------------------------------------------------------------------------
 def weff(d: Derived) -> np.ndarray:
-    """W_eff = Σ_p g_p ⊙ B_p ⊙ h_p in float64 (each term exact)."""
-    b1 = np.where(d.s1, -1.0, 1.0)
-    b2 = np.where(d.s2, -1.0, 1.0)
-    g1 = d.g1.astype(np.float64)[:, None]
-    h1 = d.h1.astype(np.float64)[None, :]
-    g2 = d.g2.astype(np.float64)[:, None]
-    h2 = d.h2.astype(np.float64)[None, :]
-    return g1 * b1 * h1 + g2 * b2 * h2
+    """W_eff = Σ_p g_p ⊙ B_p ⊙ h_p in float64 (each term exact; paths added
+    in order)."""
+    res = np.zeros(d.s1.shape, dtype=np.float64)
+    for s, g, h in d.paths:
+        res = res + g.astype(np.float64)[:, None] * np.where(s, -1.0, 1.0) * h.astype(np.float64)[None, :]
+    return res
 
 
 def gemv(d: Derived, x: np.ndarray) -> np.ndarray:
@@ -335,7 +373,7 @@ def gemv_additions(d: Derived, x: np.ndarray) -> np.ndarray:
     subtract those whose bit is −1, then scale by g (paper §5.4, App. E.1)."""
     x = np.atleast_2d(np.asarray(x, dtype=np.float64))
     y = np.zeros((x.shape[0], d.s1.shape[0]), dtype=np.float64)
-    for s, g, h in ((d.s1, d.g1, d.h1), (d.s2, d.g2, d.h2)):
+    for s, g, h in d.paths:
         u = x * h.astype(np.float64)[None, :]
         plus = u @ (~s).astype(np.float64).T
         minus = u @ s.astype(np.float64).T
@@ -354,7 +392,7 @@ def gemm(d: Derived, xm: np.ndarray, rows=None) -> np.ndarray:
 def frac_weff(d: Derived):
     out, inp = d.s1.shape
     res = [[Fraction(0)] * inp for _ in range(out)]
-    for s, g, h in ((d.s1, d.g1, d.h1), (d.s2, d.g2, d.h2)):
+    for s, g, h in d.paths:
         for i in range(out):
             gi = Fraction(float(g[i]))
             for j in range(inp):
@@ -378,7 +416,7 @@ def frac_gemv_additions(d: Derived, x) -> list:
         row = []
         for i in range(out):
             acc = Fraction(0)
-            for s, g, h in ((d.s1, d.g1, d.h1), (d.s2, d.g2, d.h2)):
+            for s, g, h in d.paths:
                 plus = sum((Fraction(float(h[j])) * xf[j] for j in range(inp) if not s[i, j]), Fraction(0))
                 minus = sum((Fraction(float(h[j])) * xf[j] for j in range(inp) if s[i, j]), Fraction(0))
                 acc += Fraction(float(g[i])) * (plus - minus)
