@@ -1,14 +1,20 @@
-// Derive and pack both binary paths of a layer from one shared fp32 weight.
+// Derive and pack the binary paths of a layer from one shared fp32 weight.
 //
 // RaBiT paper §4.2 ("The Coupled Forward Pass"): B_1 = sign(W);
-// R_1 = W − g_1 ⊙ B_1 ⊙ h_1; B_2 = sign(R_1). Paper App. E.1 ("Weight
-// Packing"): 32 columns per uint32, +1 -> 0, -1 -> 1.
+// R_1 = W − g_1 ⊙ B_1 ⊙ h_1; B_2 = sign(R_1). For the 3-bit variant (three
+// paths) the same step once more, each path correcting the residual of its
+// predecessor (paper §1): R_2 = R_1 − g_2 ⊙ B_2 ⊙ h_2, B_3 = sign(R_2).
+// Paper App. E.1 ("Weight Packing"): 32 columns per uint32, +1 -> 0, -1 -> 1.
 //
 // Passes (each reads W once, HBM-bound at 4 B per weight):
 //   S1  |W| partial sums per (column tile, row) and (row tile, column)
 //   F   finalize: ordered sums of the partials, IEEE f64 divide, f64->fp16 RNE
 //   D   B_1, R_1 (fp32, one rounding), B_2, |R_1| partial sums, packed planes
 //   F   finalize g_2, h_2
+//   and with three paths:
+//   E   R_1 again, R_2 (fp32, one rounding), B_3, |R_2| partial sums, plane 3
+//   F   finalize g_3, h_3
+// With given scales one pass (D) writes every plane.
 // The partial-sum structure is the canonical scale-sum order of rabit.h, so
 // the fp16 scales and hence B_2 are bit-exact and independent of the launch.
 #include "rabit_internal.h"
@@ -21,27 +27,36 @@ constexpr int kTileRows = 64;   // rows per tile (4 waves x 16-row segments)
 constexpr int kTileCols = 256;  // columns per tile (lane l: l + 64c, c = 0..3)
 
 // One workgroup = one 64 x 256 tile, 4 waves; wave w owns rows 16w..16w+15.
-template <bool PASS_D, bool SUMS>
+// STAGE 0: |W| sums. STAGE 1: B_1, B_2 (and B_3 with three paths and given
+// scales), |R_1| sums. STAGE 2 (three paths): B_3, |R_2| sums. P: paths of the
+// layer (the plane stride of the device layout). g, h: the scales of every
+// path ([P][out], [P][in]), as far as they are known at this stage.
+template <int STAGE, bool SUMS, int P>
 __global__ __launch_bounds__(256) void k_derive_tile(
     const float* __restrict__ W, int out, int in,
-    const uint16_t* __restrict__ g1h, const uint16_t* __restrict__ h1h,
+    const uint16_t* __restrict__ gh, const uint16_t* __restrict__ hh,
     double* __restrict__ rowpart, double* __restrict__ colpart,
     uint4* __restrict__ planes, int KG) {
+  // paths written by this stage: [pb, pb + NP)
+  constexpr bool kB3 = P == 3 && (STAGE == 2 || (STAGE == 1 && !SUMS));
+  constexpr int pb = STAGE == 2 ? 2 : 0;
+  constexpr int NP = STAGE == 0 ? 0 : STAGE == 2 ? 1 : (kB3 ? 3 : 2);
   const int ct = blockIdx.x, rt = blockIdx.y;
   const int wv = threadIdx.x >> 6, l = threadIdx.x & 63;
   const int col0 = ct * kTileCols;
 
   __shared__ double scol[4][kTileCols];
-  __shared__ uint32_t swords[2][2][64][4];  // [kg local][path][row][word]
+  __shared__ uint32_t swords[2][NP > 0 ? NP : 1][64][4];  // [kg local][path - pb][row][word]
 
   int cols[4];
   bool cval[4];
-  float h1f[4];
+  float h1f[4], h2f[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     cols[c] = col0 + l + 64 * c;
     cval[c] = cols[c] < in;
-    h1f[c] = (PASS_D && cval[c]) ? f16_bits_to_f32(h1h[cols[c]]) : 0.0f;
+    h1f[c] = (STAGE > 0 && cval[c]) ? f16_bits_to_f32(hh[cols[c]]) : 0.0f;
+    h2f[c] = (kB3 && cval[c]) ? f16_bits_to_f32(hh[in + cols[c]]) : 0.0f;
   }
   double cp[4] = {0.0, 0.0, 0.0, 0.0};
 
@@ -51,18 +66,26 @@ __global__ __launch_bounds__(256) void k_derive_tile(
     const int row = rt * kTileRows + rloc;
     const bool rv = row < out;
     const float* wrow = W + (size_t)(rv ? row : 0) * in;
-    const float g1f = (PASS_D && rv) ? f16_bits_to_f32(g1h[row]) : 0.0f;
+    const float g1f = (STAGE > 0 && rv) ? f16_bits_to_f32(gh[row]) : 0.0f;
+    const float g2f = (kB3 && rv) ? f16_bits_to_f32(gh[out + row]) : 0.0f;
     float a[4];
-    bool b1[4], b2[4];
+    bool b1[4], b2[4], b3[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const float v = (rv && cval[c]) ? __builtin_nontemporal_load(wrow + cols[c]) : 0.0f;
-      if (PASS_D) {
+      b3[c] = false;
+      if (STAGE > 0) {
         const float e = g1f * h1f[c];           // exact: fp16 x fp16 fits fp32
         b1[c] = v < 0.0f;
         const float r = v - (b1[c] ? -e : e);   // one rounding
         b2[c] = r < 0.0f;
         a[c] = fabsf(r);
+        if (kB3) {
+          const float e2 = g2f * h2f[c];
+          const float r2 = r - (b2[c] ? -e2 : e2);  // one rounding
+          b3[c] = r2 < 0.0f;
+          if (STAGE == 2) a[c] = fabsf(r2);
+        }
       } else {
         a[c] = fabsf(v);
       }
@@ -80,22 +103,24 @@ __global__ __launch_bounds__(256) void k_derive_tile(
 #pragma unroll
       for (int c = 0; c < 4; ++c) cp[c] += (double)a[c];
     }
-    if (PASS_D) {
+    if (NP > 0) {
       // ballot(c) bit l <-> column col0 + 64c + l: low half = word 2c,
-      // high half = word 2c + 1 of the tile (8 words = 2 column groups)
+      // high half = word 2c + 1 of the tile (8 words = 2 column groups);
+      // lane 8 q + k keeps word k of written path pb + q
       uint32_t myword = 0;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const uint64_t m1 = __ballot(b1[c]);
-        const uint64_t m2 = __ballot(b2[c]);
-        if (l == 2 * c) myword = (uint32_t)m1;
-        if (l == 2 * c + 1) myword = (uint32_t)(m1 >> 32);
-        if (l == 8 + 2 * c) myword = (uint32_t)m2;
-        if (l == 8 + 2 * c + 1) myword = (uint32_t)(m2 >> 32);
+#pragma unroll
+        for (int q = 0; q < NP; ++q) {
+          const int path = pb + q;
+          const uint64_t m = __ballot(path == 0 ? b1[c] : path == 1 ? b2[c] : b3[c]);
+          if (l == 8 * q + 2 * c) myword = (uint32_t)m;
+          if (l == 8 * q + 2 * c + 1) myword = (uint32_t)(m >> 32);
+        }
       }
-      if (l < 16) {
-        const int p = l >> 3, k = l & 7;
-        swords[k >> 2][p][rloc][k & 3] = myword;
+      if (l < 8 * NP) {
+        const int q = l >> 3, k = l & 7;
+        swords[k >> 2][q][rloc][k & 3] = myword;
       }
     }
   }
@@ -116,13 +141,14 @@ __global__ __launch_bounds__(256) void k_derive_tile(
       colpart[(size_t)rt * in + col] = t;
     }
   }
-  if (PASS_D) {
-    const int t = threadIdx.x;
-    const int kgl = t >> 7, p = (t >> 6) & 1, r = t & 63;
+  // units (kg local, written path, row): 2 * NP * 64 of them
+#pragma unroll
+  for (int u = threadIdx.x; u < 2 * NP * 64; u += 256) {
+    const int kgl = u / (NP * 64), q = (u / 64) % NP, r = u & 63;
     const int kg = 2 * ct + kgl;
     if (kg < KG) {
-      const uint32_t* s = swords[kgl][p][r];
-      planes[unit_index(rt, kg, p, r, KG)] = make_uint4(s[0], s[1], s[2], s[3]);
+      const uint32_t* s = swords[kgl][q][r];
+      planes[unit_index(rt, kg, pb + q, r, KG, P)] = make_uint4(s[0], s[1], s[2], s[3]);
     }
   }
 }
@@ -157,16 +183,16 @@ __global__ __launch_bounds__(256) void k_finalize(const double* __restrict__ row
 
 // Device layout -> canonical words (test hook).
 __global__ __launch_bounds__(256) void k_unpack(const uint4* __restrict__ planes, int out, int in,
-                                                uint32_t* __restrict__ words) {
+                                                int P, uint32_t* __restrict__ words) {
   const int KG = col_groups(in);
   const int nw = (in + 31) / 32;
-  const size_t total = (size_t)2 * out * nw;
+  const size_t total = (size_t)P * out * nw;
   for (size_t idx = blockIdx.x * (size_t)blockDim.x + threadIdx.x; idx < total;
        idx += (size_t)gridDim.x * blockDim.x) {
     const int k = (int)(idx % nw);
     const int row = (int)((idx / nw) % out);
     const int p = (int)(idx / ((size_t)nw * out));
-    const uint4 u = planes[unit_index(row >> 6, k >> 2, p, row & 63, KG)];
+    const uint4 u = planes[unit_index(row >> 6, k >> 2, p, row & 63, KG, P)];
     const int q = k & 3;
     words[idx] = q == 0 ? u.x : (q == 1 ? u.y : (q == 2 ? u.z : u.w));
   }
@@ -186,8 +212,9 @@ size_t pack_workspace_bytes(int out, int in) {
   return (nct * out + nrt * in) * sizeof(double);
 }
 
-hipError_t launch_pack(const float* W, int out, int in, bool meanabs, uint16_t* g, uint16_t* h,
-                       uint4* planes, void* ws, hipStream_t st) {
+hipError_t launch_pack(const float* W, int out, int in, int P, bool meanabs, uint16_t* g,
+                       uint16_t* h, uint4* planes, void* ws, hipStream_t st) {
+  if (P != 2 && P != 3) return hipErrorInvalidValue;
   const int nct = (in + kTileCols - 1) / kTileCols;
   const int nrt = (out + kTileRows - 1) / kTileRows;
   const int KG = col_groups(in);
@@ -195,26 +222,40 @@ hipError_t launch_pack(const float* W, int out, int in, bool meanabs, uint16_t* 
   double* colpart = rowpart + (size_t)nct * out;
   const dim3 grid(nct, nrt), block(256);
   const int fin_blocks = (out + in + 255) / 256;
+  auto finalize = [&](int p) {
+    hipLaunchKernelGGL(k_finalize, dim3(fin_blocks), block, 0, st, rowpart, colpart, out, in, nct,
+                       nrt, g + (size_t)p * out, h + (size_t)p * in);
+  };
   if (meanabs) {
-    hipLaunchKernelGGL((k_derive_tile<false, true>), grid, block, 0, st, W, out, in, nullptr,
+    hipLaunchKernelGGL((k_derive_tile<0, true, 2>), grid, block, 0, st, W, out, in, nullptr,
                        nullptr, rowpart, colpart, nullptr, KG);
-    hipLaunchKernelGGL(k_finalize, dim3(fin_blocks), block, 0, st, rowpart, colpart, out, in, nct,
-                       nrt, g, h);
-    hipLaunchKernelGGL((k_derive_tile<true, true>), grid, block, 0, st, W, out, in, g, h, rowpart,
-                       colpart, planes, KG);
-    hipLaunchKernelGGL(k_finalize, dim3(fin_blocks), block, 0, st, rowpart, colpart, out, in, nct,
-                       nrt, g + out, h + in);
+    finalize(0);
+    if (P == 2) {
+      hipLaunchKernelGGL((k_derive_tile<1, true, 2>), grid, block, 0, st, W, out, in, g, h, rowpart,
+                         colpart, planes, KG);
+      finalize(1);
+    } else {
+      hipLaunchKernelGGL((k_derive_tile<1, true, 3>), grid, block, 0, st, W, out, in, g, h, rowpart,
+                         colpart, planes, KG);
+      finalize(1);
+      hipLaunchKernelGGL((k_derive_tile<2, true, 3>), grid, block, 0, st, W, out, in, g, h, rowpart,
+                         colpart, planes, KG);
+      finalize(2);
+    }
+  } else if (P == 2) {
+    hipLaunchKernelGGL((k_derive_tile<1, false, 2>), grid, block, 0, st, W, out, in, g, h,
+                       nullptr, nullptr, planes, KG);
   } else {
-    hipLaunchKernelGGL((k_derive_tile<true, false>), grid, block, 0, st, W, out, in, g, h,
+    hipLaunchKernelGGL((k_derive_tile<1, false, 3>), grid, block, 0, st, W, out, in, g, h,
                        nullptr, nullptr, planes, KG);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_unpack(const uint4* planes, int out, int in, uint32_t* words, hipStream_t st) {
-  const size_t total = (size_t)2 * out * ((in + 31) / 32);
+hipError_t launch_unpack(const uint4* planes, int out, int in, int P, uint32_t* words, hipStream_t st) {
+  const size_t total = (size_t)P * out * ((in + 31) / 32);
   const int blocks = (int)std::min<size_t>((total + 255) / 256, 65535);
-  hipLaunchKernelGGL(k_unpack, dim3(blocks), dim3(256), 0, st, planes, out, in, words);
+  hipLaunchKernelGGL(k_unpack, dim3(blocks), dim3(256), 0, st, planes, out, in, P, words);
   return hipGetLastError();
 }
 

@@ -27,17 +27,25 @@ int check_dims(int64_t out, int64_t in) {
 int check_layer(const rabit_layer* L) {
   if (!L) return RABIT_EINVAL;
   if (L->layout_version != RABIT_LAYOUT_V1) return RABIT_EINVAL;
-  if (L->n_paths != 2) return RABIT_EUNSUPPORTED;
+  if (L->n_paths != 2 && L->n_paths != 3) return RABIT_EUNSUPPORTED;
   int s = check_dims(L->out_features, L->in_features);
   if (s) return s;
   if (!L->planes || !L->g || !L->h) return RABIT_EINVAL;
   if (!aligned16(L->planes) || !aligned16(L->g) || !aligned16(L->h)) return RABIT_EALIGN;
-  const size_t pb = rabit_planes_bytes(L->out_features, L->in_features, 2);
-  const size_t gb = (size_t)2 * L->out_features * 2, hb = (size_t)2 * L->in_features * 2;
+  const int P = L->n_paths;
+  const size_t pb = rabit_planes_bytes(L->out_features, L->in_features, P);
+  const size_t gb = (size_t)P * L->out_features * 2, hb = (size_t)P * L->in_features * 2;
   if (overlap(L->planes, pb, L->g, gb) || overlap(L->planes, pb, L->h, hb) ||
       overlap(L->g, gb, L->h, hb))
     return RABIT_EINVAL;
   return RABIT_OK;
+}
+
+// layers read by the GEMV, GEMM and decode kernels (two paths)
+int check_compute_layer(const rabit_layer* L) {
+  int s = check_layer(L);
+  if (s) return s;
+  return L->n_paths == 2 ? RABIT_OK : RABIT_EUNSUPPORTED;
 }
 
 }  // namespace
@@ -60,7 +68,7 @@ const char* rabit_status_string(int status) {
 }
 
 size_t rabit_planes_bytes(int32_t out, int32_t in, int32_t n_paths) {
-  if (check_dims(out, in) || n_paths != 2) return 0;
+  if (check_dims(out, in) || (n_paths != 2 && n_paths != 3)) return 0;
   return (size_t)n_paths * row_groups(out) * 64 * col_groups(in) * 16;
 }
 
@@ -86,10 +94,10 @@ int rabit_pack(const float* W, uint32_t scale_mode, const rabit_layer* L, void* 
   int s = check_layer(L);
   if (s) return s;
   if (!aligned16(W)) return RABIT_EALIGN;
-  const int out = L->out_features, in = L->in_features;
+  const int out = L->out_features, in = L->in_features, P = L->n_paths;
   const size_t wb = (size_t)out * in * 4;
-  if (overlap(W, wb, L->planes, rabit_planes_bytes(out, in, 2)) ||
-      overlap(W, wb, L->g, (size_t)4 * out) || overlap(W, wb, L->h, (size_t)4 * in))
+  if (overlap(W, wb, L->planes, rabit_planes_bytes(out, in, P)) ||
+      overlap(W, wb, L->g, (size_t)2 * P * out) || overlap(W, wb, L->h, (size_t)2 * P * in))
     return RABIT_EINVAL;
   const bool meanabs = scale_mode == RABIT_SCALES_MEANABS;
   if (meanabs) {
@@ -97,7 +105,7 @@ int rabit_pack(const float* W, uint32_t scale_mode, const rabit_layer* L, void* 
     if (workspace_bytes < pack_workspace_bytes(out, in)) return RABIT_EWORKSPACE;
     if (!aligned16(workspace)) return RABIT_EALIGN;
   }
-  return dev_status(launch_pack(W, out, in, meanabs, L->g, L->h, (uint4*)L->planes, workspace,
+  return dev_status(launch_pack(W, out, in, P, meanabs, L->g, L->h, (uint4*)L->planes, workspace,
                                 (hipStream_t)stream));
 }
 
@@ -106,13 +114,13 @@ int rabit_unpack(const rabit_layer* L, uint32_t* words, void* stream) {
   if (s) return s;
   if (!words) return RABIT_EINVAL;
   if (!aligned16(words)) return RABIT_EALIGN;
-  return dev_status(launch_unpack((const uint4*)L->planes, L->out_features, L->in_features, words,
-                                  (hipStream_t)stream));
+  return dev_status(launch_unpack((const uint4*)L->planes, L->out_features, L->in_features,
+                                  L->n_paths, words, (hipStream_t)stream));
 }
 
 namespace {
 int check_gemv_common(const rabit_layer* L, int32_t batch, void* workspace, size_t workspace_bytes) {
-  int s = check_layer(L);
+  int s = check_compute_layer(L);
   if (s) return s;
   if (batch < 1 || batch > RABIT_MAX_GEMV_BATCH) return RABIT_ESHAPE;
   if (!workspace || workspace_bytes < gemv_workspace_bytes(L->out_features, L->in_features, batch))
@@ -141,7 +149,7 @@ int check_gemv_y(const rabit_layer* L, int32_t batch, void* y, int32_t y_dtype, 
 
 int rabit_gemv(const rabit_layer* L, const uint16_t* x, int32_t batch, void* y, int32_t y_dtype,
                void* workspace, size_t workspace_bytes, void* stream) {
-  int s = check_layer(L);
+  int s = check_compute_layer(L);
   if (s) return s;
   if (!x || !y) return RABIT_EINVAL;
   if (y_dtype != RABIT_OUT_F32 && y_dtype != RABIT_OUT_BF16) return RABIT_EINVAL;
@@ -180,7 +188,7 @@ int rabit_gemv_partial_multi(const rabit_layer* Ls, int32_t n, const uint16_t* x
   LinSeg segs[3];
   size_t off = 0;
   for (int i = 0; i < n; ++i) {
-    if ((s = check_layer(&Ls[i]))) return s;
+    if ((s = check_compute_layer(&Ls[i]))) return s;
     if (Ls[i].in_features != in) return RABIT_ESHAPE;
     segs[i] = LinSeg{(const uint4*)Ls[i].planes, Ls[i].g, Ls[i].h, Ls[i].out_features,
                      (double*)((char*)workspace + off)};
@@ -211,7 +219,7 @@ int rabit_gemv_reduce(const rabit_layer* L, int32_t batch, void* y, int32_t y_dt
 
 int rabit_gemm(const rabit_layer* L, const uint16_t* X, int32_t m, void* Y, int32_t y_dtype,
                void* workspace, size_t workspace_bytes, void* stream) {
-  int s = check_layer(L);
+  int s = check_compute_layer(L);
   if (s) return s;
   if (!X || !Y) return RABIT_EINVAL;
   if (y_dtype != RABIT_OUT_F32 && y_dtype != RABIT_OUT_BF16) return RABIT_EINVAL;
@@ -382,7 +390,7 @@ int rabit_decode_step(const rabit_decoder_cfg* cfg, const rabit_layer* layers, c
   for (int l = 0; l < cfg->n_layers; ++l) {
     for (int m = cfg->mlp_only ? 4 : 0; m < 7; ++m) {
       const rabit_layer& L = layers[l * 7 + m];
-      if ((s = check_layer(&L))) return s;
+      if ((s = check_compute_layer(&L))) return s;
       static const int kOut[7] = {0, 1, 1, 0, 2, 2, 0}, kIn[7] = {0, 0, 0, 0, 0, 0, 2};
       const int want_out = kOut[m] == 0 ? H : (kOut[m] == 1 ? kv : F);
       const int want_in = kIn[m] == 0 ? H : F;

@@ -158,17 +158,18 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 // ---------------------------------------------------------------------------
 __host__ __device__ __forceinline__ int row_groups(int out) { return (out + 63) / 64; }
 __host__ __device__ __forceinline__ int col_groups(int in) { return (in + 127) / 128; }
-__host__ __device__ __forceinline__ size_t unit_index(int rg, int kg, int p, int r, int KG) {
-  return (((size_t)rg * KG + kg) * 2 + p) * 64 + r;
+// 16-byte unit (rg, kg, p, r) of a layer with P paths (layout V1)
+__host__ __device__ __forceinline__ size_t unit_index(int rg, int kg, int p, int r, int KG, int P = 2) {
+  return (((size_t)rg * KG + kg) * P + p) * 64 + r;
 }
 
 // ---------------------------------------------------------------------------
 // Host-side launchers (each returns hipSuccess or the launch error)
 // ---------------------------------------------------------------------------
 size_t pack_workspace_bytes(int out, int in);
-hipError_t launch_pack(const float* W, int out, int in, bool meanabs, uint16_t* g, uint16_t* h,
-                       uint4* planes, void* ws, hipStream_t st);
-hipError_t launch_unpack(const uint4* planes, int out, int in, uint32_t* words, hipStream_t st);
+hipError_t launch_pack(const float* W, int out, int in, int P, bool meanabs, uint16_t* g,
+                       uint16_t* h, uint4* planes, void* ws, hipStream_t st);
+hipError_t launch_unpack(const uint4* planes, int out, int in, int P, uint32_t* words, hipStream_t st);
 
 size_t gemv_workspace_bytes(int out, int in, int batch);
 hipError_t launch_gemv(const uint4* planes, const uint16_t* g, const uint16_t* h, int out, int in,

@@ -130,31 +130,34 @@ def _ptr(t: torch.Tensor | None):
     return ctypes.c_void_p(0 if t is None else t.data_ptr())
 
 
-def planes_bytes(out: int, inp: int) -> int:
-    return int(load().rabit_planes_bytes(out, inp, 2))
+def planes_bytes(out: int, inp: int, n_paths: int = 2) -> int:
+    return int(load().rabit_planes_bytes(out, inp, n_paths))
 
 
 @dataclass
 class PackedLayer:
-    """Device buffers of one frozen 2-path layer (see rabit_layer in rabit.h)."""
+    """Device buffers of one frozen layer of n_paths (2 or 3) binary paths
+    (see rabit_layer in rabit.h)."""
     out_features: int
     in_features: int
     planes: torch.Tensor  # uint8 [planes_bytes]
-    g: torch.Tensor       # int16 fp16 bits [2, out]
-    h: torch.Tensor       # int16 fp16 bits [2, in]
+    g: torch.Tensor       # int16 fp16 bits [n_paths, out]
+    h: torch.Tensor       # int16 fp16 bits [n_paths, in]
+    n_paths: int = 2
 
     @staticmethod
-    def empty(out: int, inp: int, device="cuda") -> "PackedLayer":
-        pb = planes_bytes(out, inp)
+    def empty(out: int, inp: int, device="cuda", n_paths: int = 2) -> "PackedLayer":
+        pb = planes_bytes(out, inp, n_paths)
         if pb == 0:
             raise RabitError(RABIT_ESHAPE, "planes_bytes")
         return PackedLayer(out, inp,
                            torch.empty(pb, dtype=torch.uint8, device=device),
-                           torch.empty(2, out, dtype=torch.int16, device=device),
-                           torch.empty(2, inp, dtype=torch.int16, device=device))
+                           torch.empty(n_paths, out, dtype=torch.int16, device=device),
+                           torch.empty(n_paths, inp, dtype=torch.int16, device=device),
+                           n_paths)
 
     def c(self) -> RabitLayerC:
-        return RabitLayerC(RABIT_LAYOUT_V1, self.out_features, self.in_features, 2,
+        return RabitLayerC(RABIT_LAYOUT_V1, self.out_features, self.in_features, self.n_paths,
                            self.planes.data_ptr(), self.g.data_ptr(), self.h.data_ptr())
 
     def scales_f16(self):
@@ -167,7 +170,7 @@ def _ws(nbytes: int, device) -> torch.Tensor:
 
 def pack(w: torch.Tensor, layer: PackedLayer, mode: int = RABIT_SCALES_MEANABS,
          workspace: torch.Tensor | None = None, stream=None) -> PackedLayer:
-    """Derive and pack both paths of `w` (float32 [out, in], cuda) into `layer`."""
+    """Derive and pack every path of `w` (float32 [out, in], cuda) into `layer`."""
     lib = load()
     assert w.dtype == torch.float32 and w.is_contiguous()
     nb = lib.rabit_pack_workspace_bytes(layer.out_features, layer.in_features)
@@ -183,7 +186,7 @@ def pack(w: torch.Tensor, layer: PackedLayer, mode: int = RABIT_SCALES_MEANABS,
 def unpack(layer: PackedLayer, stream=None) -> torch.Tensor:
     lib = load()
     nw = (layer.in_features + 31) // 32
-    words = torch.empty(2, layer.out_features, nw, dtype=torch.int32, device=layer.planes.device)
+    words = torch.empty(layer.n_paths, layer.out_features, nw, dtype=torch.int32, device=layer.planes.device)
     lc = layer.c()
     _check(lib.rabit_unpack(ctypes.byref(lc), _ptr(words), _stream(stream)), "rabit_unpack")
     return words

@@ -83,31 +83,38 @@ enum {
 #define RABIT_MAX_GEMM_M (1 << 20)
 
 /*
- * One frozen 2-path layer (paper §4.2: cores derived once, W discarded).
+ * One frozen layer of n_paths binary paths (paper §4.2: cores derived once,
+ * W discarded). n_paths is 2 (the 2-bit model) or 3 (the 3-bit variant: a
+ * third path from the residual of the second, paper §1 and App. E.1).
  *
- * planes  device, rabit_planes_bytes(out, in, 2) bytes. Device layout V1: a
- *         sequence of 16-byte units indexed (rg, kg, p, r) in row-major order,
- *         rg in [0, ceil(out/64)) = group of 64 output rows,
+ * planes  device, rabit_planes_bytes(out, in, n_paths) bytes. Device layout
+ *         V1: a sequence of 16-byte units indexed (rg, kg, p, r) in row-major
+ *         order, rg in [0, ceil(out/64)) = group of 64 output rows,
  *         kg in [0, ceil(in/128)) = group of 128 input columns,
- *         p in {0, 1} = path, r in [0, 64) = row inside the group.
+ *         p in [0, n_paths) = path, r in [0, 64) = row inside the group.
  *         Unit (rg, kg, p, r) holds, as 4 little-endian uint32, the canonical
  *         words 4*kg + 0, +1, +2, +3 of row 64*rg + r of path p. Rows >= out
  *         and words past ceil(in/32) are zero. (A wave of 64 lanes loads one
  *         (rg, kg, p) slab of 1 KiB with one 16-byte load per lane.)
- * g       device, fp16 bit patterns [2][out]: g_1 then g_2 (per output row)
- * h       device, fp16 bit patterns [2][in]:  h_1 then h_2 (per input column)
+ * g       device, fp16 bit patterns [n_paths][out]: g_1, g_2(, g_3) (per
+ *         output row)
+ * h       device, fp16 bit patterns [n_paths][in]: h_1, h_2(, h_3) (per input
+ *         column)
+ * The GEMV, GEMM and decode calls take 2-path layers (RABIT_EUNSUPPORTED
+ * otherwise); rabit_pack and rabit_unpack take both.
  */
 typedef struct {
   int32_t layout_version;   /* RABIT_LAYOUT_V1 */
   int32_t out_features;     /* rows of W (outputs) */
   int32_t in_features;      /* columns of W (inputs) */
-  int32_t n_paths;          /* 2 */
+  int32_t n_paths;          /* 2 or 3 */
   void *planes;
   uint16_t *g;
   uint16_t *h;
 } rabit_layer;
 
-/* Bytes of the plane buffer: n_paths * ceil(out/64)*64 * ceil(in/128) * 16. */
+/* Bytes of the plane buffer: n_paths * ceil(out/64)*64 * ceil(in/128) * 16
+   (0 for n_paths other than 2 and 3, or unsupported dimensions). */
 size_t rabit_planes_bytes(int32_t out_features, int32_t in_features, int32_t n_paths);
 
 /* Workspace needed by rabit_pack / rabit_gemv / rabit_gemm for these sizes. */
@@ -116,13 +123,17 @@ size_t rabit_gemv_workspace_bytes(int32_t out_features, int32_t in_features, int
 size_t rabit_gemm_workspace_bytes(int32_t out_features, int32_t in_features, int32_t m);
 
 /*
- * Derive and pack both paths of one layer (paper §4.2 steps 1-3, App. E.1).
+ * Derive and pack every path of one layer (paper §4.2 steps 1-3, App. E.1;
+ * with three paths one more step: R_2 = fl32(R_1 − g_2 B_2 h_2),
+ * B_3 = sign(R_2)).
  *
  * W           device float32 [out][in], row-major, contiguous (read only).
  * scale_mode  RABIT_SCALES_MEANABS: writes g_1, h_1 = mean |W| per row/column,
- *             then g_2, h_2 = mean |R_1|, and the planes.
- *             RABIT_SCALES_GIVEN: reads g_1 = layer->g[0..out), h_1 =
- *             layer->h[0..in); writes only the planes.
+ *             then g_2, h_2 = mean |R_1| (and g_3, h_3 = mean |R_2|), and the
+ *             planes. W is read 2 times (3 with three paths).
+ *             RABIT_SCALES_GIVEN: reads g_1, h_1 (and with three paths g_2,
+ *             h_2) from layer->g, layer->h; writes only the planes (one read
+ *             of W).
  * layer       host pointer; its device buffers are written as described.
  * Errors: RABIT_EINVAL (null, bad mode, W aliasing an output),
  * RABIT_ESHAPE, RABIT_EALIGN, RABIT_EUNSUPPORTED, RABIT_EWORKSPACE,
@@ -132,8 +143,8 @@ int rabit_pack(const float *W, uint32_t scale_mode, const rabit_layer *layer,
                void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * Test hook: write the canonical words of both planes.
- * words  device uint32 [2][out][ceil(in/32)] (path 1 first).
+ * Test hook: write the canonical words of every plane.
+ * words  device uint32 [n_paths][out][ceil(in/32)] (path 1 first).
  */
 int rabit_unpack(const rabit_layer *layer, uint32_t *words, void *stream);
 

@@ -41,7 +41,10 @@ def test_sizes(lib):
     assert lib.rabit_planes_bytes(1, 1, 2) == 2048
     assert lib.rabit_planes_bytes(65, 129, 2) == 2 * 2 * 64 * 2 * 16
     assert lib.rabit_planes_bytes(0, 4, 2) == 0
-    assert lib.rabit_planes_bytes(4, 4, 3) == 0
+    assert lib.rabit_planes_bytes(4, 4, 3) == 3 * 64 * 16          # the 3-bit variant
+    assert lib.rabit_planes_bytes(65, 129, 3) == 3 * 2 * 64 * 2 * 16
+    assert lib.rabit_planes_bytes(4, 4, 1) == 0
+    assert lib.rabit_planes_bytes(4, 4, 4) == 0
     assert lib.rabit_planes_bytes(1 << 20, 4, 2) == 0
     assert lib.rabit_pack_workspace_bytes(4096, 4096) > 0
     assert lib.rabit_gemv_workspace_bytes(4096, 4096, 1) > 0
