@@ -50,7 +50,9 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 constexpr int kChunk = 512;                    // columns per K range
 constexpr int kImgDw = 6;                      // dwords per lane of one fp6 image (32 x 6 bits)
 constexpr int kImgDwords = 64 * kImgDw;        // one (path, slice) image
-constexpr int kPairDwords = 8 * kImgDwords;    // 2 paths x 4 slices, one batch pair (12 KiB)
+// P paths x 4 slices, one batch pair (12 KiB with two paths)
+template <int P>
+constexpr int kPairDwords = P * 4 * kImgDwords;
 constexpr int kFxTop = 18;                     // max |v| of a range in [2^18, 2^19]
 constexpr int kOff = 1 << 20;                  // v + kOff in [0, 2^21): 7 digits of base 8
 constexpr int kNoExp = -100000;                // exponent of an all-zero range
@@ -83,7 +85,7 @@ constexpr int kMaxRounds = 8;   // row groups per wave and launch
 constexpr int kMaxDevices = 64;
 
 struct Plan {
-  int KG, S, m;
+  int KG, S, m, paths;
   int RB[kMaxSeg];    // row blocks per segment (4 m row groups each)
 };
 
@@ -139,7 +141,7 @@ __device__ __forceinline__ void deposit_digits(uint32_t (&dw)[kImgDw], const int
 // group 4 m rb + 4 k + w. Lane l = j + 16 g loads, per tile tau and path p,
 // the 16-byte unit (rg, 4 r + g, p, 16 tau + j): 128 columns of row
 // 16 tau + j, bit 4e + t of dword q being column 32 q + 4 e + t of the group.
-template <int NBP, bool RING, bool GROUPED>
+template <int NBP, bool RING, bool GROUPED, int P>
 __global__ __launch_bounds__(256) void k_gemv(Args A) {
   // Work item (row block, range) and batch group of this workgroup. With
   // several batch groups (GROUPED), the groups of one item are adjacent in
@@ -174,37 +176,37 @@ __global__ __launch_bounds__(256) void k_gemv(Args A) {
 
   // weights of round k (clamped row group: loads stay in bounds, results unused)
   // and the row scales g_p of this lane's 4 output rows
-  auto load_round = [&](uint4 (&wt)[8], uint16_t (&gt)[8], int k) {
+  auto load_round = [&](uint4 (&wt)[4 * P], uint16_t (&gt)[4 * P], int k) {
     const int rg = min(RG - 1, 4 * m * rb + 4 * k + w);
     const int kg = min(A.KG - 1, 4 * r + gl);
 #pragma unroll
     for (int tau = 0; tau < 4; ++tau)
 #pragma unroll
-      for (int p = 0; p < 2; ++p) wt[tau * 2 + p] = load_nt(planes + unit_index(rg, kg, p, 16 * tau + j, A.KG));
+      for (int p = 0; p < P; ++p) wt[tau * P + p] = load_nt(planes + unit_index(rg, kg, p, 16 * tau + j, A.KG, P));
 #pragma unroll
     for (int tau = 0; tau < 4; ++tau)
 #pragma unroll
-      for (int p = 0; p < 2; ++p) gt[tau * 2 + p] = gsc[(size_t)p * out + min(rg * 64 + 16 * tau + j, out - 1)];
+      for (int p = 0; p < P; ++p) gt[tau * P + p] = gsc[(size_t)p * out + min(rg * 64 + 16 * tau + j, out - 1)];
   };
 
-  __shared__ __align__(16) uint32_t s_img[NBP * kPairDwords];
-  __shared__ __align__(16) int s_v[2][2][kChunk];     // [hb][p][t*128 + g*32 + x] = v + kOff
-  __shared__ int s_ex[4][2][2];         // per wave [hb][p]
-  __shared__ int s_sum[4][2][2];
-  __shared__ int s_sh[NBP][2][2];
-  __shared__ int s_U[NBP][2][2];
+  __shared__ __align__(16) uint32_t s_img[NBP * kPairDwords<P>];
+  __shared__ __align__(16) int s_v[2][P][kChunk];     // [hb][p][t*128 + g*32 + x] = v + kOff
+  __shared__ int s_ex[4][2][P];         // per wave [hb][p]
+  __shared__ int s_sum[4][2][P];
+  __shared__ int s_sh[NBP][2][P];
+  __shared__ int s_U[NBP][2][P];
 
   // ---- digit operand of this range, pair by pair ---------------------------
   // element e = tid + 256 k (k = 0, 1) of the range: column col0 + e
   // loads are unconditional (clamped indices) and masked afterwards, so that
   // no branch separates them and they are all in flight together
-  uint16_t hv[2][2], xv[NBP][2][2];
+  uint16_t hv[P][2], xv[NBP][2][2];
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const int col = col0 + tid + 256 * k;
     const int cc = min(col, in - 1);
 #pragma unroll
-    for (int p = 0; p < 2; ++p) hv[p][k] = hsc[(size_t)p * in + cc];
+    for (int p = 0; p < P; ++p) hv[p][k] = hsc[(size_t)p * in + cc];
 #pragma unroll
     for (int q = 0; q < NBP; ++q)
 #pragma unroll
@@ -225,8 +227,8 @@ __global__ __launch_bounds__(256) void k_gemv(Args A) {
   }
   // the first round's weights are issued after x and h: waiting for those
   // (loads complete in order) then does not wait for the weights
-  uint4 w0[8], w1[8];
-  uint16_t g0[8], g1[8];
+  uint4 w0[4 * P], w1[4 * P];
+  uint16_t g0[4 * P], g1[4 * P];
   __builtin_amdgcn_sched_barrier(0);
   load_round(w0, g0, 0);
   __builtin_amdgcn_sched_barrier(0);  // keep every load above the first use of x and h
@@ -246,7 +248,7 @@ __global__ __launch_bounds__(256) void k_gemv(Args A) {
   for (int k = 0; k < 2; ++k) {
     const bool ok = col0 + tid + 256 * k < in;
 #pragma unroll
-    for (int p = 0; p < 2; ++p) hv[p][k] = ok ? hv[p][k] : (uint16_t)0;
+    for (int p = 0; p < P; ++p) hv[p][k] = ok ? hv[p][k] : (uint16_t)0;
 #pragma unroll
     for (int q = 0; q < NBP; ++q)
 #pragma unroll
@@ -260,12 +262,12 @@ __global__ __launch_bounds__(256) void k_gemv(Args A) {
     const bool live0 = 2 * (bp0 + q) < batch, live1 = 2 * (bp0 + q) + 1 < batch;
     // range exponent: the largest binary exponent of a nonzero |u| (frexp:
     // |u| = f 2^e, f in [1/2, 1)), so that max |u| 2^sh lies in [2^18, 2^19)
-    double u[2][2][2];
-    int ex[2][2];
+    double u[2][P][2];
+    int ex[2][P];
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
+      for (int p = 0; p < P; ++p) {
         ex[hb][p] = kNoExp;
         if (hb == 1 && !live1) continue;
 #pragma unroll
@@ -281,13 +283,13 @@ __global__ __launch_bounds__(256) void k_gemv(Args A) {
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-        for (int p = 0; p < 2; ++p) s_ex[w][hb][p] = ex[hb][p];
+        for (int p = 0; p < P; ++p) s_ex[w][hb][p] = ex[hb][p];
     __syncthreads();
-    int sh[2][2];
+    int sh[2][P];
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
+      for (int p = 0; p < P; ++p) {
         const int E = max(max(s_ex[0][hb][p], s_ex[1][hb][p]), max(s_ex[2][hb][p], s_ex[3][hb][p]));
         sh[hb][p] = E == kNoExp ? 0 : kFxTop + 1 - E;
         if (hb == 1 && !live1) continue;
@@ -304,23 +306,32 @@ __global__ __launch_bounds__(256) void k_gemv(Args A) {
         if (l == 0) s_sum[w][hb][p] = su;
       }
     __syncthreads();
-    if (tid < 4) {
-      const int hb = tid >> 1, p = tid & 1;
+    if (tid < 2 * P) {
+      const int hb = tid / P, p = tid % P;
       // same value as sh[hb][p], selected without indexing a register array
-      const int shs = (hb ? (p ? sh[1][1] : sh[1][0]) : (p ? sh[0][1] : sh[0][0]));
+      int shs = 0;
+#pragma unroll
+      for (int hb2 = 0; hb2 < 2; ++hb2)
+#pragma unroll
+        for (int p2 = 0; p2 < P; ++p2) shs = (hb2 == hb && p2 == p) ? sh[hb2][p2] : shs;
       const bool lv = hb ? live1 : live0;
       s_sh[q][hb][p] = shs;
       s_U[q][hb][p] = lv ? ((s_sum[0][hb][p] + s_sum[1][hb][p]) + s_sum[2][hb][p]) + s_sum[3][hb][p] : 0;
     }
-    // image rows: wave w builds slice t = w, lane (p, g, dr) the row
-    // L = 8 hb + dr + 16 g of image (p, t) for each batch row hb of the pair
-    {
-      const int t = w, p = l >> 5, g = (l >> 3) & 3, dr = l & 7;
+    // image rows: wave w builds slice t = w, row unit u = (p, g, dr) the row
+    // L = 8 hb + dr + 16 g of image (p, t) for each batch row hb of the pair;
+    // the 32 P units of a slice take the wave's 64 lanes once (two paths) or
+    // twice (three)
+#pragma unroll
+    for (int u0 = 0; u0 < 32 * P; u0 += 64) {
+      const int uu = u0 + l;
+      if (uu >= 32 * P) break;
+      const int t = w, p = uu >> 5, g = (uu >> 3) & 3, dr = uu & 7;
       const bool dbl = t == 0;  // slice of value 0.5: code 2d
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) {
         const bool lv = hb ? live1 : live0;
-        uint32_t* dst = s_img + q * kPairDwords + (p * 4 + t) * kImgDwords + (8 * hb + dr + 16 * g) * kImgDw;
+        uint32_t* dst = s_img + q * kPairDwords<P> + (p * 4 + t) * kImgDwords + (8 * hb + dr + 16 * g) * kImgDw;
         if (!lv) {
 #pragma unroll
           for (int d = 0; d < kImgDw; d += 2) *(uint2*)(dst + d) = make_uint2(0u, 0u);
@@ -366,39 +377,39 @@ __global__ __launch_bounds__(256) void k_gemv(Args A) {
   const float kc3 = (gl & 1) ? -8.f * kOff : 1.f;
   // this lane's row of image (pair q, path/slice ps)
   auto image_row = [&](int q, int ps) -> v8i {
-    const uint32_t* s = s_img + q * kPairDwords + ps * kImgDwords + l * kImgDw;
+    const uint32_t* s = s_img + q * kPairDwords<P> + ps * kImgDwords + l * kImgDw;
     const uint2 a0 = *(const uint2*)(s), a1 = *(const uint2*)(s + 2), a2 = *(const uint2*)(s + 4);
     return (v8i){(int)a0.x, (int)a0.y, (int)a1.x, (int)a1.y, (int)a2.x, (int)a2.y, 0, 0};
   };
-  // with one batch pair the 8 operand rows of this lane stay in registers
-  // (with the ring, NBP == 1); without it they are read from LDS per use,
+  // with one batch pair and two paths the 8 operand rows of this lane stay in
+  // registers (with the ring); without it they are read from LDS per use,
   // which frees 48 registers for more resident waves
-  constexpr bool kAreg = NBP == 1 && RING;
-  v8i areg[8];
+  constexpr bool kAreg = NBP == 1 && RING && P == 2;
+  v8i areg[kAreg ? 8 : 1];
 #pragma unroll
-  for (int ps = 0; ps < 8; ++ps) areg[ps] = kAreg ? image_row(0, ps) : (v8i){};
+  for (int ps = 0; ps < (kAreg ? 8 : 1); ++ps) areg[ps] = kAreg ? image_row(0, ps) : (v8i){};
 
   // Slice 3 is read as (0.5 - bit) against digits coded -d/8, which adds a
   // constant -(1/16) Σ d per operand row over the chunk's slice-3 columns; the
   // accumulators start from that constant's negation, computed exactly by one
   // matrix op against an all -0.5 operand (fp4 code 0b1001).
-  v4f ainit[NBP][2];
+  v4f ainit[NBP][P];
 #pragma unroll
   for (int q = 0; q < NBP; ++q)
 #pragma unroll
-    for (int p = 0; p < 2; ++p)
+    for (int p = 0; p < P; ++p)
       ainit[q][p] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-          kAreg ? areg[p * 4 + 3] : image_row(q, p * 4 + 3),
+          kAreg ? areg[(p * 4 + 3) % (kAreg ? 8 : 1)] : image_row(q, p * 4 + 3),
           (v8i){(int)0x99999999u, (int)0x99999999u, (int)0x99999999u, (int)0x99999999u, 0, 0, 0, 0},
           (v4f){0.f, 0.f, 0.f, 0.f}, 2, 4, 0, ascale, 0, 127);
 
   // one round: row group 4 m rb + 4 k + w from the weights in wt
-  auto round = [&](const uint4 (&wt)[8], const uint16_t (&gt)[8], int k) {
+  auto round = [&](const uint4 (&wt)[4 * P], const uint16_t (&gt)[4 * P], int k) {
     const int rg = 4 * m * rb + 4 * k + w;
     // per lane and path: this lane's exact share of Σ bit·v (see above)
-    int mv[NBP][2][4];
+    int mv[NBP][P][4];
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
+    for (int p = 0; p < P; ++p) {
       v4f acc[NBP][4];
 #pragma unroll
       for (int q = 0; q < NBP; ++q)
@@ -414,10 +425,10 @@ __global__ __launch_bounds__(256) void k_gemv(Args A) {
         const int sc = T == 2 ? ascale - 1 : ascale;
         v8i a[NBP];
 #pragma unroll
-        for (int q = 0; q < NBP; ++q) a[q] = kAreg ? areg[p * 4 + T] : image_row(q, p * 4 + T);
+        for (int q = 0; q < NBP; ++q) a[q] = kAreg ? areg[(p * 4 + T) % (kAreg ? 8 : 1)] : image_row(q, p * 4 + T);
 #pragma unroll
         for (int tau = 0; tau < 4; ++tau) {
-          const uint4 wv = wt[tau * 2 + p];
+          const uint4 wv = wt[tau * P + p];
           const v8i bv = (v8i){(int)((wv.x & mT) | oT), (int)((wv.y & mT) | oT),
                                (int)((wv.z & mT) | oT), (int)((wv.w & mT) | oT), 0, 0, 0, 0};
 #pragma unroll
@@ -441,19 +452,27 @@ __global__ __launch_bounds__(256) void k_gemv(Args A) {
     }
 
     // lanes of rows 0 and 2 (gl even) add the share of the lane 16 above
-    // (a VALU row swap) and form g_1 S_1 + g_2 S_2 in float64
+    // (a VALU row swap) and form Σ_p g_p S_p in float64 (each product exact,
+    // paths added in order)
     double res[NBP][4];
 #pragma unroll
     for (int q = 0; q < NBP; ++q) {
-      const int sh0 = s_sh[q][hbl][0], sh1 = s_sh[q][hbl][1];
-      const int U0 = s_U[q][hbl][0], U1 = s_U[q][hbl][1];
+      int shp[P], Up[P];
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        shp[p] = s_sh[q][hbl][p];
+        Up[p] = s_U[q][hbl][p];
+      }
 #pragma unroll
       for (int tau = 0; tau < 4; ++tau) {
-        const int m0 = mv[q][0][tau] + (int)__builtin_amdgcn_permlane16_swap(mv[q][0][tau], mv[q][0][tau], false, false)[1];
-        const int m1 = mv[q][1][tau] + (int)__builtin_amdgcn_permlane16_swap(mv[q][1][tau], mv[q][1][tau], false, false)[1];
-        const double g0 = ldexp((double)f16_bits_to_f32(gt[tau * 2 + 0]), -sh0);
-        const double g1 = ldexp((double)f16_bits_to_f32(gt[tau * 2 + 1]), -sh1);
-        res[q][tau] = g0 * (double)(U0 - 2 * m0) + g1 * (double)(U1 - 2 * m1);
+        double acc = 0.0;
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+          const int mp = mv[q][p][tau] + (int)__builtin_amdgcn_permlane16_swap(mv[q][p][tau], mv[q][p][tau], false, false)[1];
+          const double gp = ldexp((double)f16_bits_to_f32(gt[tau * P + p]), -shp[p]);
+          acc = p == 0 ? gp * (double)(Up[p] - 2 * mp) : acc + gp * (double)(Up[p] - 2 * mp);
+        }
+        res[q][tau] = acc;
       }
     }
 
@@ -511,17 +530,19 @@ __global__ __launch_bounds__(256) void k_gemv_reduce(const double* __restrict__ 
 
 // Workgroups of one variant that fit on the device at once (occupancy from
 // the runtime, queried once per device and variant).
-int resident_wgs(bool ring) {
-  static std::atomic<int> cache[kMaxDevices][2];
+int resident_wgs(bool ring, int paths) {
+  static std::atomic<int> cache[kMaxDevices][2][2];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
-  std::atomic<int>& slot = cache[dev][ring ? 1 : 0];
+  std::atomic<int>& slot = cache[dev][ring ? 1 : 0][paths == 3 ? 1 : 0];
   int c = slot.load(std::memory_order_relaxed);
   if (c == 0) {
     int cus = 0, per = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
       cus = 256;
-    const void* fn = ring ? (const void*)k_gemv<1, true, false> : (const void*)k_gemv<1, false, false>;
+    const void* fn = paths == 3
+        ? (ring ? (const void*)k_gemv<1, true, false, 3> : (const void*)k_gemv<1, false, false, 3>)
+        : (ring ? (const void*)k_gemv<1, true, false, 2> : (const void*)k_gemv<1, false, false, 2>);
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fn, 256, 0) != hipSuccess || per < 1) per = 1;
     c = cus * per;
     slot.store(c, std::memory_order_relaxed);
@@ -537,8 +558,9 @@ int resident_wgs(bool ring) {
 // passes x (m rounds + one for the digit build), ties to the smaller m (more
 // workgroups). With more batch pairs (one buffer, rounds not overlapped) the
 // rounds stay short: enough workgroups to fill the device a few times over.
-__host__ inline Plan make_plan(const int* outs, int nseg, int in, int batch) {
+__host__ inline Plan make_plan(const int* outs, int nseg, int in, int batch, int paths) {
   Plan P;
+  P.paths = paths;
   P.KG = col_groups(in);
   P.S = (in + kChunk - 1) / kChunk;
   const int groups = (batch + 1) / 2;  // one batch pair per workgroup
@@ -548,7 +570,7 @@ __host__ inline Plan make_plan(const int* outs, int nseg, int in, int batch) {
     long wgs = 0;
     for (int s = 0; s < nseg; ++s) wgs += (row_groups(outs[s]) + 4 * m - 1) / (4 * m);
     wgs *= (long)P.S * groups;
-    const long cap = resident_wgs(m > 1);
+    const long cap = resident_wgs(m > 1, paths);
     const long cost = (wgs + cap - 1) / cap * (m + 1);
     if (best < 0 || cost < best) {
       best = cost;
@@ -567,17 +589,24 @@ hipError_t launch_main(const Plan& P, const Args& A, int batch, hipStream_t st) 
   Args B = A;
   B.items = nrb * P.S;
   B.ngrp = groups;
-  if (groups > 1) {
-    if (A.m > 1)
-      hipLaunchKernelGGL((k_gemv<1, true, true>), grid, dim3(256), 0, st, B);
-    else
-      hipLaunchKernelGGL((k_gemv<1, false, true>), grid, dim3(256), 0, st, B);
-  } else {
-    if (A.m > 1)
-      hipLaunchKernelGGL((k_gemv<1, true, false>), grid, dim3(256), 0, st, B);
-    else
-      hipLaunchKernelGGL((k_gemv<1, false, false>), grid, dim3(256), 0, st, B);
-  }
+  auto go = [&](auto paths_tag) {
+    constexpr int NP = decltype(paths_tag)::value;
+    if (groups > 1) {
+      if (A.m > 1)
+        hipLaunchKernelGGL((k_gemv<1, true, true, NP>), grid, dim3(256), 0, st, B);
+      else
+        hipLaunchKernelGGL((k_gemv<1, false, true, NP>), grid, dim3(256), 0, st, B);
+    } else {
+      if (A.m > 1)
+        hipLaunchKernelGGL((k_gemv<1, true, false, NP>), grid, dim3(256), 0, st, B);
+      else
+        hipLaunchKernelGGL((k_gemv<1, false, false, NP>), grid, dim3(256), 0, st, B);
+    }
+  };
+  if (P.paths == 3)
+    go(std::integral_constant<int, 3>());
+  else
+    go(std::integral_constant<int, 2>());
   return hipGetLastError();
 }
 
@@ -612,8 +641,10 @@ size_t gemv_workspace_bytes(int out, int in, int batch) {
 }
 
 hipError_t launch_gemv_partial(const uint4* planes, const uint16_t* g, const uint16_t* h, int out,
-                               int in, const uint16_t* x, int batch, void* ws, hipStream_t st) {
-  const Plan P = make_plan(&out, 1, in, batch);
+                               int in, const uint16_t* x, int batch, void* ws, hipStream_t st,
+                               int paths) {
+  if (paths != 2 && paths != 3) return hipErrorInvalidValue;
+  const Plan P = make_plan(&out, 1, in, batch, paths);
   const Args A = make_args(P, planes, g, h, out, in, x, batch, ws);
   return launch_main(P, A, batch, st);
 }
@@ -634,8 +665,12 @@ hipError_t launch_gemv_multi(const LinSeg* segs, int nseg, int in, const uint16_
                              const double* stats, float eps, hipStream_t st) {
   if (nseg < 1 || nseg > kMaxSeg) return hipErrorInvalidValue;
   int outs[kMaxSeg];
-  for (int s = 0; s < nseg; ++s) outs[s] = segs[s].out;
-  const Plan P = make_plan(outs, nseg, in, batch);
+  for (int s = 0; s < nseg; ++s) {
+    outs[s] = segs[s].out;
+    if (segs[s].paths != segs[0].paths) return hipErrorInvalidValue;
+  }
+  if (segs[0].paths != 2 && segs[0].paths != 3) return hipErrorInvalidValue;
+  const Plan P = make_plan(outs, nseg, in, batch, segs[0].paths);
   Args A = {};
   int rb0 = 0;
   for (int s = 0; s < nseg; ++s) {
@@ -663,8 +698,8 @@ hipError_t launch_gemv_multi(const LinSeg* segs, int nseg, int in, const uint16_
 
 hipError_t launch_gemv(const uint4* planes, const uint16_t* g, const uint16_t* h, int out, int in,
                        const uint16_t* x, int batch, void* y, int y_dtype, void* ws,
-                       hipStream_t st) {
-  hipError_t e = launch_gemv_partial(planes, g, h, out, in, x, batch, ws, st);
+                       hipStream_t st, int paths) {
+  hipError_t e = launch_gemv_partial(planes, g, h, out, in, x, batch, ws, st, paths);
   if (e != hipSuccess) return e;
   return launch_gemv_reduce(out, in, batch, y, y_dtype, ws, st);
 }

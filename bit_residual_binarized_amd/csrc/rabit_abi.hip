@@ -41,8 +41,8 @@ int check_layer(const rabit_layer* L) {
   return RABIT_OK;
 }
 
-// layers read by the GEMV, GEMM and decode kernels (two paths)
-int check_compute_layer(const rabit_layer* L) {
+// layers read by the GEMM (two paths; the GEMV takes two or three)
+int check_gemm_layer(const rabit_layer* L) {
   int s = check_layer(L);
   if (s) return s;
   return L->n_paths == 2 ? RABIT_OK : RABIT_EUNSUPPORTED;
@@ -120,7 +120,7 @@ int rabit_unpack(const rabit_layer* L, uint32_t* words, void* stream) {
 
 namespace {
 int check_gemv_common(const rabit_layer* L, int32_t batch, void* workspace, size_t workspace_bytes) {
-  int s = check_compute_layer(L);
+  int s = check_layer(L);
   if (s) return s;
   if (batch < 1 || batch > RABIT_MAX_GEMV_BATCH) return RABIT_ESHAPE;
   if (!workspace || workspace_bytes < gemv_workspace_bytes(L->out_features, L->in_features, batch))
@@ -149,7 +149,7 @@ int check_gemv_y(const rabit_layer* L, int32_t batch, void* y, int32_t y_dtype, 
 
 int rabit_gemv(const rabit_layer* L, const uint16_t* x, int32_t batch, void* y, int32_t y_dtype,
                void* workspace, size_t workspace_bytes, void* stream) {
-  int s = check_compute_layer(L);
+  int s = check_layer(L);
   if (s) return s;
   if (!x || !y) return RABIT_EINVAL;
   if (y_dtype != RABIT_OUT_F32 && y_dtype != RABIT_OUT_BF16) return RABIT_EINVAL;
@@ -163,7 +163,7 @@ int rabit_gemv(const rabit_layer* L, const uint16_t* x, int32_t batch, void* y, 
     return RABIT_EINVAL;
   return dev_status(launch_gemv((const uint4*)L->planes, L->g, L->h, L->out_features,
                                 L->in_features, x, batch, y, y_dtype, workspace,
-                                (hipStream_t)stream));
+                                (hipStream_t)stream, L->n_paths));
 }
 
 int rabit_gemv_partial(const rabit_layer* L, const uint16_t* x, int32_t batch, void* workspace,
@@ -174,7 +174,8 @@ int rabit_gemv_partial(const rabit_layer* L, const uint16_t* x, int32_t batch, v
   const size_t wsb = gemv_workspace_bytes(L->out_features, L->in_features, batch);
   if (overlap(workspace, wsb, x, (size_t)batch * L->in_features * 2)) return RABIT_EINVAL;
   return dev_status(launch_gemv_partial((const uint4*)L->planes, L->g, L->h, L->out_features,
-                                        L->in_features, x, batch, workspace, (hipStream_t)stream));
+                                        L->in_features, x, batch, workspace, (hipStream_t)stream,
+                                        L->n_paths));
 }
 
 int rabit_gemv_partial_multi(const rabit_layer* Ls, int32_t n, const uint16_t* x, int32_t batch,
@@ -188,10 +189,11 @@ int rabit_gemv_partial_multi(const rabit_layer* Ls, int32_t n, const uint16_t* x
   LinSeg segs[3];
   size_t off = 0;
   for (int i = 0; i < n; ++i) {
-    if ((s = check_compute_layer(&Ls[i]))) return s;
+    if ((s = check_layer(&Ls[i]))) return s;
     if (Ls[i].in_features != in) return RABIT_ESHAPE;
+    if (Ls[i].n_paths != Ls[0].n_paths) return RABIT_EUNSUPPORTED;
     segs[i] = LinSeg{(const uint4*)Ls[i].planes, Ls[i].g, Ls[i].h, Ls[i].out_features,
-                     (double*)((char*)workspace + off)};
+                     (double*)((char*)workspace + off), Ls[i].n_paths};
     off += gemv_workspace_bytes(Ls[i].out_features, in, batch);
   }
   if (!workspace || workspace_bytes < off) return RABIT_EWORKSPACE;
@@ -219,7 +221,7 @@ int rabit_gemv_reduce(const rabit_layer* L, int32_t batch, void* y, int32_t y_dt
 
 int rabit_gemm(const rabit_layer* L, const uint16_t* X, int32_t m, void* Y, int32_t y_dtype,
                void* workspace, size_t workspace_bytes, void* stream) {
-  int s = check_compute_layer(L);
+  int s = check_gemm_layer(L);
   if (s) return s;
   if (!X || !Y) return RABIT_EINVAL;
   if (y_dtype != RABIT_OUT_F32 && y_dtype != RABIT_OUT_BF16) return RABIT_EINVAL;
@@ -321,7 +323,7 @@ size_t decode_ws(const rabit_decoder_cfg* c, int batch, DecodeWs* w, void* base)
 }
 
 LinSeg seg_of(const rabit_layer& L, double* part) {
-  return LinSeg{(const uint4*)L.planes, L.g, L.h, L.out_features, part};
+  return LinSeg{(const uint4*)L.planes, L.g, L.h, L.out_features, part, L.n_paths};
 }
 
 // One decode step at batch <= RABIT_MAX_GEMV_BATCH. Per layer: [q,k,v] GEMV
@@ -390,7 +392,10 @@ int rabit_decode_step(const rabit_decoder_cfg* cfg, const rabit_layer* layers, c
   for (int l = 0; l < cfg->n_layers; ++l) {
     for (int m = cfg->mlp_only ? 4 : 0; m < 7; ++m) {
       const rabit_layer& L = layers[l * 7 + m];
-      if ((s = check_compute_layer(&L))) return s;
+      // the GEMV path (batch <= RABIT_MAX_GEMV_BATCH) takes 2 or 3 paths, with
+      // the same number in every layer; the GEMM path takes 2
+      if ((s = batch <= RABIT_MAX_GEMV_BATCH ? check_layer(&L) : check_gemm_layer(&L))) return s;
+      if (L.n_paths != layers[(cfg->mlp_only ? 4 : 0)].n_paths) return RABIT_EUNSUPPORTED;
       static const int kOut[7] = {0, 1, 1, 0, 2, 2, 0}, kIn[7] = {0, 0, 0, 0, 0, 0, 2};
       const int want_out = kOut[m] == 0 ? H : (kOut[m] == 1 ? kv : F);
       const int want_in = kIn[m] == 0 ? H : F;

@@ -172,10 +172,13 @@ hipError_t launch_pack(const float* W, int out, int in, int P, bool meanabs, uin
 hipError_t launch_unpack(const uint4* planes, int out, int in, int P, uint32_t* words, hipStream_t st);
 
 size_t gemv_workspace_bytes(int out, int in, int batch);
+// paths: 2, or 3 for the 3-bit variant
 hipError_t launch_gemv(const uint4* planes, const uint16_t* g, const uint16_t* h, int out, int in,
-                       const uint16_t* x, int batch, void* y, int y_dtype, void* ws, hipStream_t st);
+                       const uint16_t* x, int batch, void* y, int y_dtype, void* ws, hipStream_t st,
+                       int paths = 2);
 hipError_t launch_gemv_partial(const uint4* planes, const uint16_t* g, const uint16_t* h, int out,
-                               int in, const uint16_t* x, int batch, void* ws, hipStream_t st);
+                               int in, const uint16_t* x, int batch, void* ws, hipStream_t st,
+                               int paths = 2);
 hipError_t launch_gemv_reduce(int out, int in, int batch, void* y, int y_dtype, const void* ws,
                               hipStream_t st);
 
@@ -189,6 +192,7 @@ struct LinSeg {
   const uint16_t* h;
   int out;
   double* part;
+  int paths = 2;  // every segment of a launch has the same number of paths
 };
 #define RABIT_STAT_PARTS 32
 

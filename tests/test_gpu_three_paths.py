@@ -100,3 +100,125 @@ def test_pack3_first_two_paths_match_two_path_pack(gpu_lib):
     u3, u2 = gpu_lib.unpack(l3), gpu_lib.unpack(l2)
     assert torch.equal(u3[:2], u2)
     assert torch.equal(l3.g[:2], l2.g) and torch.equal(l3.h[:2], l2.h)
+
+
+# ---- GEMV and decode with three paths -----------------------------------
+from synth.inputs import act_bf16, bf16_values  # noqa: E402
+
+TOL = 2e-3
+
+
+def fx_bound(d, xv):
+    """Elementwise bound of the GEMV arithmetic (rabit.h): per (batch row, path,
+    512-column range) h_p*x on a grid of step 2^(ilogb(max |h_p*x|) - 18),
+    exact signed sums, g_p in float64; summed over the paths."""
+    xb = np.atleast_2d(xv)
+    B, K = xb.shape
+    bound = np.zeros((B, d.g1.shape[0]))
+    for _, g, h in d.paths:
+        u = np.abs(h.astype(np.float64)[None, :] * xb)
+        tot = np.zeros(B)
+        for c0 in range(0, K, 512):
+            mr = u[:, c0:c0 + 512].max(axis=1)
+            _, e = np.frexp(mr)
+            tot += np.where(mr > 0, min(512, K - c0) * np.exp2(e - 1.0 - 19.0), 0.0)
+        bound += np.abs(g.astype(np.float64))[None, :] * tot[:, None]
+    return bound
+
+
+def check_gemv3(y, ref, d, xv):
+    bound = fx_bound(d, xv) + 2.0 ** -23 * np.abs(ref) + 1e-300
+    bad = np.argwhere(np.abs(y - ref) > bound)
+    assert bad.size == 0, f"{len(bad)} outputs outside the fixed-point bound, first {bad[:3].tolist()}"
+    assert oracle.normwise_rel_err(y, ref) < TOL
+
+
+@pytest.mark.parametrize("shape", [(64, 512), (100, 300), (130, 1000), (1, 1), (1024, 4096),
+                                   (4096, 4096), (11008, 4096)])
+def test_gemv3_batch1(gpu_lib, shape):
+    out, inp = shape
+    say("gemv 3 paths b=1", shape)
+    w = weight_f32(out, inp, 3100 + out + inp).numpy()
+    layer = pack3(gpu_lib, w)
+    d = oracle.derive(w, n_paths=3)
+    x = act_bf16(1, inp, 3101)
+    y = gpu_lib.gemv(layer, x.cuda()).cpu().numpy().astype(np.float64)
+    xv = bf16_values(x)
+    check_gemv3(y, oracle.gemv(d, xv), d, xv)
+    # repeatable bit for bit
+    y2 = gpu_lib.gemv(layer, x.cuda()).cpu().numpy().astype(np.float64)
+    assert np.array_equal(y, y2)
+
+
+@pytest.mark.parametrize("batch", [2, 3, 17, 32])
+def test_gemv3_batches(gpu_lib, batch):
+    out, inp = 1024, 4096
+    say("gemv 3 paths batch", batch)
+    w = weight_f32(out, inp, 3200 + batch).numpy()
+    layer = pack3(gpu_lib, w)
+    d = oracle.derive(w, n_paths=3)
+    x = act_bf16(batch, inp, 3201 + batch)
+    y = gpu_lib.gemv(layer, x.cuda()).cpu().numpy().astype(np.float64)
+    xv = bf16_values(x)
+    check_gemv3(y, oracle.gemv(d, xv), d, xv)
+    # every batch row equals the batch-1 result of that row
+    for r in (0, batch - 1):
+        y1 = gpu_lib.gemv(layer, x[r:r + 1].contiguous().cuda()).cpu().numpy().astype(np.float64)
+        assert np.array_equal(y1[0], y[r])
+
+
+def test_gemv3_partial_multi_equals_gemv(gpu_lib):
+    inp = 2048
+    say("gemv 3 paths multi")
+    ws_ = [weight_f32(o, inp, 3300 + o).numpy() for o in (512, 300)]
+    layers = [pack3(gpu_lib, w) for w in ws_]
+    x = act_bf16(2, inp, 3301).cuda()
+    parts = gpu_lib.gemv_partial_multi(layers, x, gpu_lib.gemv_multi_workspace(layers, 2))
+    for L, part in zip(layers, parts):
+        ref = gpu_lib.gemv(L, x)
+        y = gpu_lib.gemv_reduce(L, 2, torch.empty(2, L.out_features, device="cuda"), part)
+        assert torch.equal(y, ref)
+
+
+def test_decode3_mlp_and_attention(gpu_lib):
+    for mlp_only in (True, False):
+        say("decode 3 paths, mlp_only", mlp_only)
+        cfg = gpu_lib.DecoderCfg(hidden=1024, ffn=2752, n_heads=8, n_kv_heads=2, head_dim=128, n_layers=2,
+                                 mlp_only=mlp_only)
+        H, F, kv = cfg.hidden, cfg.ffn, cfg.n_kv_heads * cfg.head_dim
+        shapes = {"q": (H, H), "k": (kv, H), "v": (kv, H), "o": (H, H), "gate": (F, H), "up": (F, H),
+                  "down": (H, F)}
+        names = ["gate", "up", "down"] if mlp_only else list(shapes)
+        layers, dmats = [], []
+        for li in range(cfg.n_layers):
+            ld, dd = {}, {}
+            for n in names:
+                w = weight_f32(*shapes[n], 3400 + 10 * li + len(n)).numpy()
+                ld[n] = pack3(gpu_lib, w)
+                dd[n] = oracle.derive(w, n_paths=3)
+            layers.append(ld)
+            dmats.append(dd)
+        x = act_bf16(1, H, 3499)
+        y = gpu_lib.decode_step(cfg, layers, x.cuda()).cpu().to(torch.float32).numpy().astype(np.float64)
+        ref = bf16_values(x)
+        ocfg = {"n_heads": cfg.n_heads, "n_kv_heads": cfg.n_kv_heads, "head_dim": cfg.head_dim,
+                "rms_eps": cfg.rms_eps}
+        for dd in dmats:
+            ref = oracle.decode_layer(ref, dd, ocfg)
+        a = np.abs(ref)
+        ulp = np.exp2(np.floor(np.log2(np.where(a > 0, a, 1.0))) - 7)
+        allow = TOL * a.max(axis=1, keepdims=True) + ulp
+        assert not (np.abs(y - ref) > allow).any()
+
+
+def test_mixed_path_counts_are_rejected(gpu_lib):
+    say("mixed path counts")
+    inp = 512
+    l2 = gpu_lib.PackedLayer.empty(256, inp)
+    gpu_lib.pack(weight_f32(256, inp, 3501).cuda(), l2)
+    l3 = pack3(gpu_lib, weight_f32(256, inp, 3502).numpy())
+    x = act_bf16(1, inp, 3503).cuda()
+    with pytest.raises(gpu_lib.RabitError):
+        gpu_lib.gemv_partial_multi([l2, l3], x, gpu_lib.gemv_multi_workspace([l2, l3], 1))
+    with pytest.raises(gpu_lib.RabitError):
+        gpu_lib.gemm(l3, act_bf16(64, inp, 3504).cuda())
