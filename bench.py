@@ -471,7 +471,8 @@ def bench_layer4096(args, rabit, torch):
 def bench_table7(args, rabit, torch):
     """The shapes of the pages' kernel-latency table (Llama-2 7B and 13B
     projections) at batch 1: the residual-binary GEMV (rabit_gemv, both
-    launches) against a dense bf16 GEMV (torch.mm on a contiguous [in][out]
+    launches; 2-bit, and the 3-bit variant with three planes) against a dense
+    bf16 GEMV (torch.mm on a contiguous [in][out]
     bf16 weight, hipBLASLt), each cold (rotating copies over >= 512 MiB) and
     warm (one copy, as the pages measured). Context only: the pages' figures
     are from another GPU."""
@@ -496,6 +497,24 @@ def bench_table7(args, rabit, torch):
         ours_cold = _events_ms(torch, lambda i: rabit.gemv(layers[i % n], x, y=y, workspace=ws), n)
         ours_warm = _events_ms(torch, lambda i: rabit.gemv(layers[0], x, y=y, workspace=ws), 64)
         del layers
+        # the 3-bit variant (three planes) on the same shape
+        from synth.inputs import weight_f32
+        l3 = rabit.PackedLayer.empty(out, inp, n_paths=3)
+        w = weight_f32(out, inp, seed_w(6, si, "q"), device="cuda")
+        rabit.pack(w, l3, workspace=wsh[0])
+        del w
+        pb3 = rabit.planes_bytes(out, inp, 3)
+        n3 = max(2, -(-(512 << 20) // pb3))
+        layers3 = [l3]
+        for _ in range(n3 - 1):
+            c = rabit.PackedLayer.empty(out, inp, n_paths=3)
+            c.planes.copy_(l3.planes)
+            c.g.copy_(l3.g)
+            c.h.copy_(l3.h)
+            layers3.append(c)
+        ours3_cold = _events_ms(torch, lambda i: rabit.gemv(layers3[i % n3], x, y=y, workspace=ws), n3)
+        ours3_warm = _events_ms(torch, lambda i: rabit.gemv(layers3[0], x, y=y, workspace=ws), 64)
+        del layers3
         wb = out * inp * 2
         nd = max(2, -(-(512 << 20) // wb))
         dense = [torch.randn(inp, out, device="cuda").mul_(0.02).to(torch.bfloat16) for _ in range(nd)]
@@ -510,6 +529,8 @@ def bench_table7(args, rabit, torch):
             "dense_bf16_us_cold": round(dense_cold * 1e3, 2), "dense_bf16_us_warm": round(dense_warm * 1e3, 2),
             "speedup_cold": round(sp, 2), "speedup_warm": round(dense_warm / ours_warm, 2),
             "rabit_plane_gbs_cold": round(pb / (ours_cold * 1e-3) / 1e9, 1),
+            "rabit3_us_cold": round(ours3_cold * 1e3, 2), "rabit3_us_warm": round(ours3_warm * 1e3, 2),
+            "rabit3_speedup_cold": round(dense_cold / ours3_cold, 2),
             "dense_gbs_cold": round(wb / (dense_cold * 1e-3) / 1e9, 1)}
         log(f"{name} {out}x{inp}: {runs[f'{out}x{inp} {name}']}")
     gm = 1.0
