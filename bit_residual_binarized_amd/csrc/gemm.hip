@@ -24,29 +24,32 @@ namespace {
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-constexpr int kBM = 128, kBN = 128, kBK = 64;
+constexpr int kBN = 128, kBK = 64;
+// token rows per workgroup: 128 with two paths; 64 with three (the third
+// accumulator set would not fit the registers of two waves per SIMD)
+__host__ __device__ constexpr int bm_of(int P) { return P == 2 ? 128 : 64; }
 constexpr int kLdsStride = 36;  // dwords per 64-column row in LDS (32 + 4 padding)
 
 struct GemmWs {
   uint16_t* xh;      // fp16 [m][Kp], κ-permuted inside 32-column blocks
   int* rowexp;       // [m] power-of-two exponent applied to row m
-  uint32_t* hpairs;  // [2][Kp/32][16] fp16 pairs (h[32b+m], h[32b+m+16])
-  float* part;       // split K: [Z][m][out] partial g_1 acc_1 + g_2 acc_2
+  uint32_t* hpairs;  // [P][Kp/32][16] fp16 pairs (h[32b+m], h[32b+m+16])
+  float* part;       // split K: [Z][m][out] partial Σ_p g_p acc_p
 };
 
 __host__ inline size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // split of K over grid.z: enough workgroups to fill the chip, at least four
 // 64-column steps per slice
-__host__ inline int split_k(int out, int in, int m) {
+__host__ inline int split_k(int out, int in, int m, int P) {
   const int Kp = col_groups(in) * 128;
-  const int tiles = ((out + kBN - 1) / kBN) * ((m + kBM - 1) / kBM);
+  const int tiles = ((out + kBN - 1) / kBN) * ((m + bm_of(P) - 1) / bm_of(P));
   int z = std::max(1, (512 + tiles - 1) / tiles);
   z = std::min(z, std::max(1, Kp / (4 * kBK)));
   return std::min(z, 16);
 }
 
-__host__ inline GemmWs carve(void* ws, int out, int in, int m) {
+__host__ inline GemmWs carve(void* ws, int out, int in, int m, int P) {
   const size_t Kp = (size_t)col_groups(in) * 128;
   char* p = (char*)ws;
   GemmWs w;
@@ -55,16 +58,21 @@ __host__ inline GemmWs carve(void* ws, int out, int in, int m) {
   w.rowexp = (int*)p;
   p += a256((size_t)m * 4);
   w.hpairs = (uint32_t*)p;
-  p += a256(2 * (Kp / 32) * 16 * 4);
+  p += a256((size_t)P * (Kp / 32) * 16 * 4);
   w.part = (float*)p;
   return w;
 }
 
-__host__ inline size_t ws_bytes(int out, int in, int m) {
+__host__ inline size_t ws_bytes_p(int out, int in, int m, int P) {
   const size_t Kp = (size_t)col_groups(in) * 128;
-  const int z = split_k(out, in, m);
-  return a256((size_t)m * Kp * 2) + a256((size_t)m * 4) + a256(2 * (Kp / 32) * 16 * 4) +
+  const int z = split_k(out, in, m, P);
+  return a256((size_t)m * Kp * 2) + a256((size_t)m * 4) + a256((size_t)P * (Kp / 32) * 16 * 4) +
          (z > 1 ? a256((size_t)z * m * out * 4) : 0);
+}
+
+// enough for a layer of two or of three paths
+__host__ inline size_t ws_bytes(int out, int in, int m) {
+  return std::max(ws_bytes_p(out, in, m, 2), ws_bytes_p(out, in, m, 3));
 }
 
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
@@ -100,10 +108,10 @@ __global__ __launch_bounds__(256) void k_gemm_prep_x(const uint16_t* __restrict_
   if (threadIdx.x == 0) ws.rowexp[m] = e;
 }
 
-__global__ void k_gemm_prep_h(const uint16_t* __restrict__ h, int in, int Kp, GemmWs ws) {
+__global__ void k_gemm_prep_h(const uint16_t* __restrict__ h, int in, int Kp, int P, GemmWs ws) {
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;  // (p, blk, pair)
   const int nb = Kp / 32;
-  if (idx >= 2 * nb * 16) return;
+  if (idx >= P * nb * 16) return;
   const int pr = idx & 15, blk = (idx >> 4) % nb, p = idx / (16 * nb);
   const int c0 = blk * 32 + pr, c1 = c0 + 16;
   const uint32_t lo = c0 < in ? h[(size_t)p * in + c0] : 0;
@@ -119,9 +127,11 @@ __global__ void k_gemm_prep_h(const uint16_t* __restrict__ h, int in, int Kp, Ge
 // of the 32-column block. X goes through a double-buffered LDS tile (one
 // barrier per step). The next step's X rows, plane words and h pairs are
 // loaded into registers while the current step runs on the matrix cores.
+template <int P>
 __global__ __launch_bounds__(256, 2) void k_gemm(const uint4* __restrict__ planes,
                                               const uint16_t* __restrict__ g, int out, int M,
                                               int Kp, int ksteps, GemmWs ws, void* Y, int y_dtype) {
+  constexpr int kBM = bm_of(P), MT = kBM / 16;  // 16-row matrix tiles per wave
   const int n0 = blockIdx.x * kBN, m0 = blockIdx.y * kBM;
   const int tid = threadIdx.x, l = tid & 63;
   const int wn = __builtin_amdgcn_readfirstlane(tid >> 6) * 32;
@@ -130,54 +140,60 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint4* __restrict__ plane
   const int out_pad = row_groups(out) * 64;
   const int ks0 = blockIdx.z * ksteps, ks1 = min(Kp / kBK, ks0 + ksteps);
   // 16-row MFMA tiles of the workgroup that hold rows of X (uniform)
-  const int mtiles = __builtin_amdgcn_readfirstlane(min(8, max(0, (M - m0 + 15) / 16)));
+  const int mtiles = __builtin_amdgcn_readfirstlane(min(MT, max(0, (M - m0 + 15) / 16)));
   const int fr = l & 15, fg = l >> 4;
 
   __shared__ __align__(16) uint32_t sA[2][kBM * kLdsStride];
-  __shared__ __align__(16) uint32_t sH[2][2][2][16];  // [buffer][p][sub]: the step's h pairs
+  __shared__ __align__(16) uint32_t sH[2][P][2][16];  // [buffer][p][sub]: the step's h pairs
 
-  v4f acc[2][8][2];
+  v4f acc[P][MT][2];
 #pragma unroll
-  for (int p = 0; p < 2; ++p)
+  for (int p = 0; p < P; ++p)
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < MT; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) acc[p][i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
 
   // A loader: thread -> row m0 + (tid >> 1), half (tid & 1) of the 64 columns
   const int am = m0 + (tid >> 1), ah = tid & 1;
-  const bool avalid = am < M;
+  const bool aload = (tid >> 1) < kBM;  // all threads with 128 rows, half with 64
+  const bool avalid = aload && am < M;
   const uint4* asrc = (const uint4*)(ws.xh + (size_t)min(am, M - 1) * Kp) + ah * 4;
   // B: the words of rows n0 + wn + 16 j + fr (clamped into the padded rows)
-  const uint32_t* wsrc[2][2];
+  const uint32_t* wsrc[P][2];
 #pragma unroll
-  for (int p = 0; p < 2; ++p)
+  for (int p = 0; p < P; ++p)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int bn = min(n0 + wn + 16 * j + fr, out_pad - 1);
-      wsrc[p][j] = (const uint32_t*)(planes + unit_index(bn >> 6, 0, p, bn & 63, KG));
+      wsrc[p][j] = (const uint32_t*)(planes + unit_index(bn >> 6, 0, p, bn & 63, KG, P));
     }
-  // h pairs of the step, staged through LDS by threads 0..63: (p, sub, pair)
-  const int hp = (tid >> 5) & 1, hs = (tid >> 4) & 1, hq = tid & 15;
+  // h pairs of the step, staged through LDS by threads 0 .. 32 P - 1: (p, sub, pair)
+  const bool hload = tid < 32 * P;
+  const int hp = hload ? tid >> 5 : 0, hs = (tid >> 4) & 1, hq = tid & 15;
   const uint32_t* hsrc = ws.hpairs + (size_t)hp * nb * 16 + hs * 16 + hq;
 
   uint4 ra[4];
-  uint2 rw[2][2];   // [p][j]: words 2 ks, 2 ks + 1 of the row (the two 32-column blocks)
+  uint2 rw[P][2];   // [p][j]: words 2 ks, 2 ks + 1 of the row (the two 32-column blocks)
   uint32_t rh = 0;
   auto load = [&](int ks) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) ra[q] = asrc[(size_t)ks * 8 + q];
 #pragma unroll
-    for (int p = 0; p < 2; ++p)
+    for (int p = 0; p < P; ++p)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) rw[p][j] = *(const uint2*)(wsrc[p][j] + (size_t)(ks >> 1) * 128 * 4 + 2 * (ks & 1));
-    if (tid < 64) rh = hsrc[(size_t)ks * 32];
+      for (int j = 0; j < 2; ++j)
+        // column group ks / 2 is P x 64 units (4 dwords each) after group 0
+        rw[p][j] = *(const uint2*)(wsrc[p][j] + (size_t)(ks >> 1) * (P * 64 * 4) + 2 * (ks & 1));
+    if (hload) rh = hsrc[(size_t)ks * 32];
   };
   auto store_a = [&](int buf) {
-    uint32_t* da = sA[buf] + (tid >> 1) * kLdsStride + ah * 16;
+    if (aload) {
+      uint32_t* da = sA[buf] + (tid >> 1) * kLdsStride + ah * 16;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) *(uint4*)(da + 4 * q) = avalid ? ra[q] : make_uint4(0, 0, 0, 0);
-    if (tid < 64) sH[buf][hp][hs][hq] = rh;
+      for (int q = 0; q < 4; ++q) *(uint4*)(da + 4 * q) = avalid ? ra[q] : make_uint4(0, 0, 0, 0);
+    }
+    if (hload) sH[buf][hp][hs][hq] = rh;
   };
   if (ks0 < ks1) {
     load(ks0);
@@ -192,9 +208,9 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint4* __restrict__ plane
   constexpr bool kFull = decltype(full_tag)::value;
   for (int ks = ks0; ks < ks1; ++ks) {
     const int buf = (ks - ks0) & 1;
-    uint2 cw[2][2];
+    uint2 cw[P][2];
 #pragma unroll
-    for (int p = 0; p < 2; ++p)
+    for (int p = 0; p < P; ++p)
 #pragma unroll
       for (int j = 0; j < 2; ++j) cw[p][j] = rw[p][j];
     if (ks + 1 < ks1) load(ks + 1);  // in flight during the matrix ops
@@ -202,11 +218,11 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint4* __restrict__ plane
     const uint32_t* a0 = sA[buf] + fr * kLdsStride + 4 * fg;
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
-      v8h fa[8];
+      v8h fa[MT];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) fa[i] = *(const v8h*)(a0 + 16 * i * kLdsStride + 16 * sub);
+      for (int i = 0; i < MT; ++i) fa[i] = *(const v8h*)(a0 + 16 * i * kLdsStride + 16 * sub);
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
+      for (int p = 0; p < P; ++p) {
         const uint4 hh = *(const uint4*)(&sH[buf][p][sub][4 * fg]);
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -221,7 +237,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint4* __restrict__ plane
           e.w = hh.w ^ ((w << (sh - 3)) & 0x80008000u);
           const v8h fb = __builtin_bit_cast(v8h, e);
 #pragma unroll
-          for (int i = 0; i < 8; ++i)
+          for (int i = 0; i < MT; ++i)
             if (kFull || i < mtiles)
               acc[p][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[i], fb, acc[p][i][j], 0, 0, 0);
         }
@@ -231,7 +247,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint4* __restrict__ plane
     __syncthreads();
   }
   };
-  if (mtiles == 8)
+  if (mtiles == MT)
     run(std::true_type{});
   else
     run(std::false_type{});
@@ -243,13 +259,15 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint4* __restrict__ plane
     const int n = n0 + wn + 16 * j + (l & 15);
     if (n >= out) continue;
     const float g0 = f16_bits_to_f32(g[n]), g1 = f16_bits_to_f32(g[out + n]);
+    const float g2 = P == 3 ? f16_bits_to_f32(g[2 * out + n]) : 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < MT; ++i) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = m0 + 16 * i + 4 * (l >> 4) + r;
         if (m >= M) continue;
-        const float v = g0 * acc[0][i][j][r] + g1 * acc[1][i][j][r];
+        float v = g0 * acc[0][i][j][r] + g1 * acc[1][i][j][r];
+        if (P == 3) v += g2 * acc[P - 1][i][j][r];
         if (split) {
           ws.part[((size_t)blockIdx.z * M + m) * out + n] = v;
         } else {
@@ -284,17 +302,22 @@ __global__ __launch_bounds__(256) void k_gemm_reduce(GemmWs ws, int out, int M, 
 size_t gemm_workspace_bytes(int out, int in, int m) { return ws_bytes(out, in, m); }
 
 hipError_t launch_gemm(const uint4* planes, const uint16_t* g, const uint16_t* h, int out, int in,
-                       const uint16_t* X, int m, void* Y, int y_dtype, void* ws, hipStream_t st) {
+                       const uint16_t* X, int m, void* Y, int y_dtype, void* ws, hipStream_t st,
+                       int paths) {
+  if (paths != 2 && paths != 3) return hipErrorInvalidValue;
   const int Kp = col_groups(in) * 128;
-  GemmWs w = carve(ws, out, in, m);
+  GemmWs w = carve(ws, out, in, m, paths);
   hipLaunchKernelGGL(k_gemm_prep_x, dim3(m), dim3(256), 0, st, X, in, Kp, w);
-  const int nh = 2 * (Kp / 32) * 16;
-  hipLaunchKernelGGL(k_gemm_prep_h, dim3((nh + 255) / 256), dim3(256), 0, st, h, in, Kp, w);
-  const int Z = split_k(out, in, m);
+  const int nh = paths * (Kp / 32) * 16;
+  hipLaunchKernelGGL(k_gemm_prep_h, dim3((nh + 255) / 256), dim3(256), 0, st, h, in, Kp, paths, w);
+  const int Z = split_k(out, in, m, paths);
   const int steps = Kp / kBK;
   const int per = (steps + Z - 1) / Z;
-  const dim3 grid((out + kBN - 1) / kBN, (m + kBM - 1) / kBM, Z);
-  hipLaunchKernelGGL(k_gemm, grid, dim3(256), 0, st, planes, g, out, m, Kp, per, w, Y, y_dtype);
+  const dim3 grid((out + kBN - 1) / kBN, (m + bm_of(paths) - 1) / bm_of(paths), Z);
+  if (paths == 3)
+    hipLaunchKernelGGL(k_gemm<3>, grid, dim3(256), 0, st, planes, g, out, m, Kp, per, w, Y, y_dtype);
+  else
+    hipLaunchKernelGGL(k_gemm<2>, grid, dim3(256), 0, st, planes, g, out, m, Kp, per, w, Y, y_dtype);
   if (Z > 1) {
     const size_t n = (size_t)m * out;
     hipLaunchKernelGGL(k_gemm_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, w, out,

@@ -41,13 +41,6 @@ int check_layer(const rabit_layer* L) {
   return RABIT_OK;
 }
 
-// layers read by the GEMM (two paths; the GEMV takes two or three)
-int check_gemm_layer(const rabit_layer* L) {
-  int s = check_layer(L);
-  if (s) return s;
-  return L->n_paths == 2 ? RABIT_OK : RABIT_EUNSUPPORTED;
-}
-
 }  // namespace
 
 extern "C" {
@@ -221,7 +214,7 @@ int rabit_gemv_reduce(const rabit_layer* L, int32_t batch, void* y, int32_t y_dt
 
 int rabit_gemm(const rabit_layer* L, const uint16_t* X, int32_t m, void* Y, int32_t y_dtype,
                void* workspace, size_t workspace_bytes, void* stream) {
-  int s = check_gemm_layer(L);
+  int s = check_layer(L);
   if (s) return s;
   if (!X || !Y) return RABIT_EINVAL;
   if (y_dtype != RABIT_OUT_F32 && y_dtype != RABIT_OUT_BF16) return RABIT_EINVAL;
@@ -235,7 +228,7 @@ int rabit_gemm(const rabit_layer* L, const uint16_t* X, int32_t m, void* Y, int3
   if (!workspace || workspace_bytes < gemm_workspace_bytes(out, in, m)) return RABIT_EWORKSPACE;
   if (!aligned16(workspace)) return RABIT_EALIGN;
   return dev_status(launch_gemm((const uint4*)L->planes, L->g, L->h, out, in, X, m, Y, y_dtype,
-                                workspace, (hipStream_t)stream));
+                                workspace, (hipStream_t)stream, L->n_paths));
 }
 
 // --------------------------------------------------------------------------
@@ -366,9 +359,9 @@ hipError_t linear(const rabit_layer& L, const uint16_t* x, int batch, float* y, 
                   hipStream_t st) {
   if (batch <= RABIT_MAX_GEMV_BATCH)
     return launch_gemv((const uint4*)L.planes, L.g, L.h, L.out_features, L.in_features, x, batch,
-                       y, RABIT_OUT_F32, w.lin, st);
+                       y, RABIT_OUT_F32, w.lin, st, L.n_paths);
   return launch_gemm((const uint4*)L.planes, L.g, L.h, L.out_features, L.in_features, x, batch, y,
-                     RABIT_OUT_F32, w.lin, st);
+                     RABIT_OUT_F32, w.lin, st, L.n_paths);
 }
 
 }  // namespace
@@ -392,9 +385,8 @@ int rabit_decode_step(const rabit_decoder_cfg* cfg, const rabit_layer* layers, c
   for (int l = 0; l < cfg->n_layers; ++l) {
     for (int m = cfg->mlp_only ? 4 : 0; m < 7; ++m) {
       const rabit_layer& L = layers[l * 7 + m];
-      // the GEMV path (batch <= RABIT_MAX_GEMV_BATCH) takes 2 or 3 paths, with
-      // the same number in every layer; the GEMM path takes 2
-      if ((s = batch <= RABIT_MAX_GEMV_BATCH ? check_layer(&L) : check_gemm_layer(&L))) return s;
+      // 2 or 3 paths, the same number in every layer
+      if ((s = check_layer(&L))) return s;
       if (L.n_paths != layers[(cfg->mlp_only ? 4 : 0)].n_paths) return RABIT_EUNSUPPORTED;
       static const int kOut[7] = {0, 1, 1, 0, 2, 2, 0}, kIn[7] = {0, 0, 0, 0, 0, 0, 2};
       const int want_out = kOut[m] == 0 ? H : (kOut[m] == 1 ? kv : F);

@@ -222,7 +222,8 @@ hipError_t launch_gemv_multi(const LinSeg* segs, int nseg, int in, const uint16_
 
 size_t gemm_workspace_bytes(int out, int in, int m);
 hipError_t launch_gemm(const uint4* planes, const uint16_t* g, const uint16_t* h, int out, int in,
-                       const uint16_t* X, int m, void* Y, int y_dtype, void* ws, hipStream_t st);
+                       const uint16_t* X, int m, void* Y, int y_dtype, void* ws, hipStream_t st,
+                       int paths = 2);
 
 // decode glue (plain bf16 stand-ins around the binary linear layers)
 hipError_t launch_rmsnorm(const uint16_t* x, uint16_t* y, int batch, int n, float eps, hipStream_t st);

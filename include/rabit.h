@@ -100,10 +100,8 @@ enum {
  *         output row)
  * h       device, fp16 bit patterns [n_paths][in]: h_1, h_2(, h_3) (per input
  *         column)
- * rabit_pack, rabit_unpack, the GEMV calls and rabit_decode_step at batch
- * <= RABIT_MAX_GEMV_BATCH take both (one call's layers all with the same
- * n_paths); rabit_gemm and the decode step above that batch take 2-path
- * layers (RABIT_EUNSUPPORTED otherwise).
+ * Every call takes both (the layers of one call all with the same n_paths;
+ * RABIT_EUNSUPPORTED otherwise).
  */
 typedef struct {
   int32_t layout_version;   /* RABIT_LAYOUT_V1 */

@@ -134,8 +134,11 @@ def test_gemm_and_unpack_errors(lib):
     assert lib.rabit_gemm(ctypes.byref(L), X, 0, Y, 0, ws, 1 << 30, None) == rabit.RABIT_ESHAPE
     assert lib.rabit_gemm(ctypes.byref(L), X, 8, X, 0, ws, 1 << 30, None) == rabit.RABIT_EINVAL
     assert lib.rabit_gemm(ctypes.byref(L), X, 8, Y, 0, ws, 16, None) == rabit.RABIT_EWORKSPACE
-    L3 = fake_layer(paths=3)     # the GEMM takes 2-path layers only
-    assert lib.rabit_gemm(ctypes.byref(L3), X, 8, Y, 0, ws, 1 << 30, None) == rabit.RABIT_EUNSUPPORTED
+    # a 3-path layer passes the path check and fails later on its workspace
+    L3 = fake_layer(paths=3)
+    assert lib.rabit_gemm(ctypes.byref(L3), X, 8, Y, 0, ws, 16, None) == rabit.RABIT_EWORKSPACE
+    assert lib.rabit_gemm(ctypes.byref(fake_layer(paths=4)), X, 8, Y, 0, ws, 1 << 30, None) == \
+        rabit.RABIT_EUNSUPPORTED
     assert lib.rabit_unpack(ctypes.byref(L), 0, None) == rabit.RABIT_EINVAL
     assert lib.rabit_unpack(ctypes.byref(fake_layer(version=0)), Y, None) == rabit.RABIT_EINVAL
 

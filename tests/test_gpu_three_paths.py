@@ -180,9 +180,11 @@ def test_gemv3_partial_multi_equals_gemv(gpu_lib):
         assert torch.equal(y, ref)
 
 
-def test_decode3_mlp_and_attention(gpu_lib):
+@pytest.mark.parametrize("batch", [1, 40])
+def test_decode3_mlp_and_attention(gpu_lib, batch):
+    # batch 40 runs the prefill GEMM path
     for mlp_only in (True, False):
-        say("decode 3 paths, mlp_only", mlp_only)
+        say("decode 3 paths, mlp_only", mlp_only, "batch", batch)
         cfg = gpu_lib.DecoderCfg(hidden=1024, ffn=2752, n_heads=8, n_kv_heads=2, head_dim=128, n_layers=2,
                                  mlp_only=mlp_only)
         H, F, kv = cfg.hidden, cfg.ffn, cfg.n_kv_heads * cfg.head_dim
@@ -198,7 +200,7 @@ def test_decode3_mlp_and_attention(gpu_lib):
                 dd[n] = oracle.derive(w, n_paths=3)
             layers.append(ld)
             dmats.append(dd)
-        x = act_bf16(1, H, 3499)
+        x = act_bf16(batch, H, 3499)
         y = gpu_lib.decode_step(cfg, layers, x.cuda()).cpu().to(torch.float32).numpy().astype(np.float64)
         ref = bf16_values(x)
         ocfg = {"n_heads": cfg.n_heads, "n_kv_heads": cfg.n_kv_heads, "head_dim": cfg.head_dim,
@@ -220,5 +222,29 @@ def test_mixed_path_counts_are_rejected(gpu_lib):
     x = act_bf16(1, inp, 3503).cuda()
     with pytest.raises(gpu_lib.RabitError):
         gpu_lib.gemv_partial_multi([l2, l3], x, gpu_lib.gemv_multi_workspace([l2, l3], 1))
-    with pytest.raises(gpu_lib.RabitError):
-        gpu_lib.gemm(l3, act_bf16(64, inp, 3504).cuda())
+
+
+
+@pytest.mark.parametrize("case", [(256, 512, 64), (300, 1000, 100), (1024, 4096, 200), (4096, 4096, 512),
+                                  (100, 300, 1)])
+def test_gemm3(gpu_lib, case):
+    out, inp, m = case
+    say("gemm 3 paths", case)
+    w = weight_f32(out, inp, 3600 + m).numpy()
+    layer = pack3(gpu_lib, w)
+    d = oracle.derive(w, n_paths=3)
+    xm = act_bf16(m, inp, 3700 + m)
+    y = gpu_lib.gemm(layer, xm.cuda()).cpu().numpy().astype(np.float64)
+    ref = oracle.gemm(d, bf16_values(xm))
+    assert oracle.normwise_rel_err(y, ref) < TOL
+
+
+def test_gemm3_rows_match_gemv3(gpu_lib):
+    out, inp, m = 512, 2048, 70
+    say("gemm 3 vs gemv 3 rows")
+    layer = pack3(gpu_lib, weight_f32(out, inp, 3800).numpy())
+    xm = act_bf16(m, inp, 3801).cuda()
+    ym = gpu_lib.gemm(layer, xm).cpu().numpy().astype(np.float64)
+    for r in (0, 33, 69):
+        yv = gpu_lib.gemv(layer, xm[r:r + 1].contiguous()).cpu().numpy().astype(np.float64)
+        assert oracle.normwise_rel_err(ym[r:r + 1], yv) < 1e-5
