@@ -614,7 +614,7 @@ def bench_llama3_8b(args, rabit, torch):
 def bench_gemm(args, rabit, torch):
     """Prefill GEMM with the Llama-3-8B MLP shapes at M = 512, 2048, 8192."""
     from synth.inputs import act_bf16, seed_w, seed_x
-    wsh, res = [None], {}
+    wsh, res, res3 = [None], {}, {}
     for (N, K) in ((14336, 4096), (4096, 14336)):
         pl, _ = _pack_layer(rabit, torch, N, K, seed_w(4, 0, "gate" if N > K else "down"), wsh)
         for M in (512, 2048, 8192):
@@ -628,10 +628,27 @@ def bench_gemm(args, rabit, torch):
                                     "mfma_frac_fp16": round(tf / 2500.0, 4)}
             log(f"gemm {N}x{K} M={M}: {ms:.3f} ms {tf:.1f} TFLOP/s")
             del X, ws, Y
+        # the 3-bit variant (three planes): 6 M N K flops
+        from synth.inputs import weight_f32
+        l3 = rabit.PackedLayer.empty(N, K, n_paths=3)
+        w = weight_f32(N, K, seed_w(4, 1, "gate" if N > K else "down"), device="cuda")
+        rabit.pack(w, l3, workspace=wsh[0])
+        del w
+        for M in (2048, 8192):
+            X = act_bf16(M, K, seed_x(4, M)).cuda()
+            ws = rabit.gemm_workspace(l3, M)
+            Y = torch.empty(M, N, device="cuda")
+            rabit.gemm(l3, X, y=Y, workspace=ws)
+            ms = _events_ms(torch, lambda i: rabit.gemm(l3, X, y=Y, workspace=ws), 10)
+            tf = 6.0 * M * N * K / (ms * 1e-3) / 1e12
+            res3[f"{N}x{K}_M{M}"] = {"ms": round(ms, 4), "tflops": round(tf, 1),
+                                     "mfma_frac_fp16": round(tf / 2500.0, 4)}
+            log(f"gemm 3-bit {N}x{K} M={M}: {ms:.3f} ms {tf:.1f} TFLOP/s")
+            del X, ws, Y
     best = max(v["tflops"] for v in res.values())
     return _line("Residual-binary prefill GEMM TFLOP/s (4 M N K, fp16 MFMA)", best, "TFLOP/s",
                  {"workload": "llama3-8b-mlp-gemm", "M": [512, 2048, 8192]}, dtype="fp16",
-                 runs=res, roofline={"bound": "mfma", "peak": 2500.0, "unit": "TFLOP/s",
+                 runs=res, runs_3bit=res3, roofline={"bound": "mfma", "peak": 2500.0, "unit": "TFLOP/s",
                                      "achieved": best, "frac": round(best / 2500.0, 4)})
 
 
