@@ -559,7 +559,9 @@ def _decoder_layers(rabit, torch, cfg_id, H, F, kv, n_layers):
     return layers, planes, pack
 
 
-def _time_decode(rabit, torch, cfg, layers, batch, steps, graph=True):
+def _time_decode(rabit, torch, cfg, layers, batch, steps):
+    """ms per decode step: `steps` steps ping-ponging between two activation
+    buffers, captured in one HIP graph and replayed back to back."""
     from synth.inputs import act_bf16, seed_x
     arr = rabit.layer_array(cfg, layers)
     x0 = act_bf16(batch, cfg.hidden, seed_x(3, batch)).cuda()
@@ -572,24 +574,7 @@ def _time_decode(rabit, torch, cfg, layers, batch, steps, graph=True):
     step(0)
     step(1)
     torch.cuda.synchronize()
-    if graph:
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            step(0)
-        torch.cuda.current_stream().wait_stream(s)
-        gs = []
-        for par in (0, 1):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                step(par)
-            gs.append(g)
-        run = lambda i: gs[i % 2].replay()
-    else:
-        run = step
-    for i in range(2):
-        run(i)
-    ms = _events_ms(torch, run, steps)
+    ms = _events_ms(torch, step, steps)
     del ws
     return ms
 
@@ -662,7 +647,7 @@ def bench_llama70b(args, rabit, torch):
     pack_ms = sum(ms for _, ms in pack)
     cfg = rabit.DecoderCfg(hidden=H, ffn=F, n_heads=64, n_kv_heads=8, head_dim=128, n_layers=L)
     ms1 = _time_decode(rabit, torch, cfg, layers, 1, 5)
-    ms32 = _time_decode(rabit, torch, cfg, layers, 32, 3, graph=False)
+    ms32 = _time_decode(rabit, torch, cfg, layers, 32, 3)
     return _line("Llama-2-70B decode step, packed-weight GB/s at batch 1", round(planes / (ms1 * 1e-3) / 1e9, 1),
                  "GB/s", {"workload": "llama2-70b-80-layers", "plane_bytes_per_step": planes},
                  dtype="fp4xfp6", ms_per_step_b1=round(ms1, 3), tokens_per_s_b1=round(1e3 / ms1, 1),
