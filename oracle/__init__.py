@@ -11,3 +11,4 @@ rationals, independent library routines, invariants). See the module docstring
 of ``oracle.rabit_oracle`` for which pin covers which function.
 """
 from .rabit_oracle import *  # noqa: F401,F403
+from .rabit_train import *  # noqa: F401,F403

@@ -81,3 +81,17 @@ def random_f16_scales(n: int, seed: int, lo: float = 0.005, hi: float = 0.03) ->
     """Positive float16 scale vector (for SCALES_GIVEN tests)."""
     rng = np.random.default_rng(seed)
     return rng.uniform(lo, hi, size=n).astype(np.float16)
+
+
+def seed_dy(cfg: int, batch: int) -> int:
+    return 53 + 1000 * cfg + batch
+
+
+def grad_bf16(batch: int, out: int, seed: int, std: float = 0.01,
+              device: str = "cpu") -> torch.Tensor:
+    """Loss gradient at a layer output, dY ~ std * N(0,1) rounded to bfloat16,
+    shape [batch][out] (training-side tests and bench)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    y = torch.randn(batch, out, generator=g, dtype=torch.float32, device=device)
+    return y.mul_(std).to(torch.bfloat16)
