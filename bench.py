@@ -217,7 +217,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of graph replay")
     ap.add_argument("--workload", default="mlp7b",
-                    choices=["mlp7b", "layer4096", "llama3-8b", "gemm", "llama70b", "table7"],
+                    choices=["mlp7b", "layer4096", "llama3-8b", "gemm", "llama70b", "table7", "train"],
                     help="mlp7b (default): the headline decode workload; the others measure the "
                          "remaining configurations (one JSON line each)")
     args = ap.parse_args()
@@ -235,7 +235,8 @@ def main():
     torch.cuda.set_device(0)
     if args.workload != "mlp7b":
         extra = {"layer4096": bench_layer4096, "llama3-8b": bench_llama3_8b, "gemm": bench_gemm,
-                 "llama70b": bench_llama70b, "table7": bench_table7}[args.workload]
+                 "llama70b": bench_llama70b, "table7": bench_table7,
+                 "train": bench_train}[args.workload]
         print(json.dumps(extra(args, rabit, torch)), flush=True)
         return
     hidden, ffn = 4096, 11008
@@ -635,6 +636,78 @@ def bench_gemm(args, rabit, torch):
                  {"workload": "llama3-8b-mlp-gemm", "M": [512, 2048, 8192]}, dtype="fp16",
                  runs=res, runs_3bit=res3, roofline={"bound": "mfma", "peak": 2500.0, "unit": "TFLOP/s",
                                      "achieved": best, "frac": round(best / 2500.0, 4)})
+
+
+def bench_train(args, rabit, torch):
+    """Training step of one layer (the coupled forward: derive with the current
+    scales + GEMM; the backward: dX, and dW with dg, dh) on the Llama-2-7B
+    layer shapes at M = 2048 and 8192 tokens, next to a dense bf16 layer's
+    three matrix products (torch.mm: forward, dX, dW in bf16)."""
+    import numpy as np
+    from synth.inputs import act_bf16, grad_bf16, random_f16_scales, seed_w, seed_x, seed_dy, weight_f32
+    res = {}
+    best_gw = 0.0
+    gw_launch = None
+    for (N, K, name) in ((4096, 4096, "q"), (11008, 4096, "gate"), (4096, 11008, "down")):
+        w = weight_f32(N, K, seed_w(6, 0, name), device="cuda")
+        pl = rabit.PackedLayer.empty(N, K)
+        g = torch.from_numpy(np.stack([random_f16_scales(N, 61), random_f16_scales(N, 62, 0.002, 0.01)]))
+        h = torch.from_numpy(np.stack([random_f16_scales(K, 63), random_f16_scales(K, 64, 0.002, 0.01)]))
+        pl.g.copy_(g.view(torch.int16))
+        pl.h.copy_(h.view(torch.int16))
+        wd = w.to(torch.bfloat16)
+        for M in (2048, 8192):
+            X = act_bf16(M, K, seed_x(6, M)).cuda()
+            dY = grad_bf16(M, N, seed_dy(6, M)).cuda()
+            Y = torch.empty(M, N, device="cuda", dtype=torch.bfloat16)
+            dX = torch.empty(M, K, device="cuda", dtype=torch.bfloat16)
+            dW = torch.empty(N, K, device="cuda")
+            dg = torch.empty(2, N, device="cuda")
+            dh = torch.empty(2, K, device="cuda")
+            wsf = rabit.gemm_workspace(pl, M)
+            wsx = rabit.grad_input_workspace(pl, M)
+            wsw = rabit.grad_weight_workspace(pl)
+            derive = lambda i: rabit.pack(w, pl, rabit.RABIT_SCALES_GIVEN)
+            fwd = lambda i: rabit.gemm(pl, X, rabit.RABIT_OUT_BF16, y=Y, workspace=wsf)
+            gx = lambda i: rabit.grad_input(pl, dY, rabit.RABIT_OUT_BF16, dx=dX, workspace=wsx)
+            gw = lambda i: rabit.grad_weight(pl, X, dY, dw=dW, dg=dg, dh=dh, workspace=wsw)
+            for f in (derive, fwd, gx, gw):
+                f(0)
+            t = {k: _events_ms(torch, f, 5) for k, f in
+                 (("derive", derive), ("forward", fwd), ("grad_input", gx), ("grad_weight", gw))}
+            dense = {
+                "forward": _events_ms(torch, lambda i: torch.mm(X, wd.t()), 5),
+                "grad_input": _events_ms(torch, lambda i: torch.mm(dY, wd), 5),
+                "grad_weight": _events_ms(torch, lambda i: torch.mm(dY.t(), X), 5),
+            }
+            flop = 2.0 * M * N * K
+            ours = sum(t.values())
+            dn = sum(dense.values())
+            tf_gw = flop / (t["grad_weight"] * 1e-3) / 1e12
+            if tf_gw > best_gw and M == 8192:
+                best_gw = tf_gw
+            if name == "gate" and M == 8192:
+                gw_launch = t["grad_weight"]
+            res[f"{N}x{K}_M{M}"] = {
+                "ms": {k: round(v, 4) for k, v in t.items()}, "ms_step": round(ours, 4),
+                "dense_bf16_ms": {k: round(v, 4) for k, v in dense.items()},
+                "dense_bf16_ms_step": round(dn, 4),
+                "grad_weight_tflops": round(tf_gw, 1),
+                "step_tflops_dense_equiv": round(3 * flop / (ours * 1e-3) / 1e12, 1),
+                "speedup_vs_dense": round(dn / ours, 3)}
+            log(f"train {N}x{K} M={M}: derive {t['derive']:.3f} fwd {t['forward']:.3f} "
+                f"dX {t['grad_input']:.3f} dW {t['grad_weight']:.3f} ms (dW {tf_gw:.0f} TFLOP/s); "
+                f"step {ours:.3f} ms vs dense bf16 {dn:.3f} ms")
+            del X, dY, Y, dX, dW, wsf, wsx, wsw
+        del w, wd, pl
+    gate = res["11008x4096_M8192"]
+    return _line("Coupled training step of one layer, dense-equivalent TFLOP/s (6 M N K), "
+                 "Llama-2-7B gate shape at M = 8192", gate["step_tflops_dense_equiv"], "TFLOP/s",
+                 {"workload": "llama2-7b-layer-train-step", "M": [2048, 8192]}, dtype="bf16",
+                 runs=res, roofline={"bound": "mfma", "kernel": "k_grad_w<2>", "peak": 2500.0,
+                                     "unit": "TFLOP/s", "achieved": round(best_gw, 1),
+                                     "frac": round(best_gw / 2500.0, 4),
+                                     "launch_ms_gate_M8192": round(gw_launch, 4)})
 
 
 def bench_llama70b(args, rabit, torch):

@@ -144,7 +144,8 @@ __global__ __launch_bounds__(256) void k_derive_tile(
   // units (kg local, written path, row): 2 * NP * 64 of them
 #pragma unroll
   for (int u = threadIdx.x; u < 2 * NP * 64; u += 256) {
-    const int kgl = u / (NP * 64), q = (u / 64) % NP, r = u & 63;
+    constexpr int NPs = NP > 0 ? NP : 1;  // (no units when a stage writes no path)
+    const int kgl = u / (NPs * 64), q = (u / 64) % NPs, r = u & 63;
     const int kg = 2 * ct + kgl;
     if (kg < KG) {
       const uint32_t* s = swords[kgl][q][r];

@@ -223,12 +223,93 @@ int rabit_gemm(const rabit_layer* L, const uint16_t* X, int32_t m, void* Y, int3
   const int out = L->out_features, in = L->in_features;
   const size_t yb = (size_t)m * out * (y_dtype == RABIT_OUT_F32 ? 4 : 2);
   if (overlap(Y, yb, X, (size_t)m * in * 2) ||
-      overlap(Y, yb, L->planes, rabit_planes_bytes(out, in, 2)))
+      overlap(Y, yb, L->planes, rabit_planes_bytes(out, in, L->n_paths)))
     return RABIT_EINVAL;
   if (!workspace || workspace_bytes < gemm_workspace_bytes(out, in, m)) return RABIT_EWORKSPACE;
   if (!aligned16(workspace)) return RABIT_EALIGN;
   return dev_status(launch_gemm((const uint4*)L->planes, L->g, L->h, out, in, X, m, Y, y_dtype,
                                 workspace, (hipStream_t)stream, L->n_paths));
+}
+
+// --------------------------------------------------------------------------
+// training side
+// --------------------------------------------------------------------------
+namespace {
+// does [p, p + n) overlap any buffer of the layer?
+bool overlaps_layer(const void* p, size_t n, const rabit_layer* L) {
+  const int P = L->n_paths, out = L->out_features, in = L->in_features;
+  return overlap(p, n, L->planes, rabit_planes_bytes(out, in, P)) ||
+         overlap(p, n, L->g, (size_t)2 * P * out) || overlap(p, n, L->h, (size_t)2 * P * in);
+}
+}  // namespace
+
+size_t rabit_grad_input_workspace_bytes(int32_t out, int32_t in, int32_t m) {
+  if (check_dims(out, in) || m < 1 || m > RABIT_MAX_GEMM_M) return 0;
+  return std::max(grad_input_workspace_bytes(out, in, m, 2), grad_input_workspace_bytes(out, in, m, 3));
+}
+
+size_t rabit_grad_weight_workspace_bytes(int32_t out, int32_t in) {
+  if (check_dims(out, in)) return 0;
+  return std::max(grad_weight_workspace_bytes(out, in, 2), grad_weight_workspace_bytes(out, in, 3));
+}
+
+int rabit_transpose_planes(const rabit_layer* L, void* planes_t, void* stream) {
+  int s = check_layer(L);
+  if (s) return s;
+  if (!planes_t) return RABIT_EINVAL;
+  if (!aligned16(planes_t)) return RABIT_EALIGN;
+  const int out = L->out_features, in = L->in_features, P = L->n_paths;
+  if (overlaps_layer(planes_t, rabit_planes_bytes(in, out, P), L)) return RABIT_EINVAL;
+  return dev_status(launch_transpose_planes((const uint4*)L->planes, out, in, P, (uint4*)planes_t,
+                                            (hipStream_t)stream));
+}
+
+int rabit_grad_input(const rabit_layer* L, const uint16_t* dY, int32_t m, void* dX,
+                     int32_t dx_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  int s = check_layer(L);
+  if (s) return s;
+  if (!dY || !dX) return RABIT_EINVAL;
+  if (dx_dtype != RABIT_OUT_F32 && dx_dtype != RABIT_OUT_BF16) return RABIT_EINVAL;
+  if (m < 1 || m > RABIT_MAX_GEMM_M) return RABIT_ESHAPE;
+  if (!aligned16(dY) || !aligned16(dX)) return RABIT_EALIGN;
+  const int out = L->out_features, in = L->in_features, P = L->n_paths;
+  const size_t xb = (size_t)m * in * (dx_dtype == RABIT_OUT_F32 ? 4 : 2);
+  if (overlap(dX, xb, dY, (size_t)m * out * 2) || overlaps_layer(dX, xb, L)) return RABIT_EINVAL;
+  if (!workspace || workspace_bytes < grad_input_workspace_bytes(out, in, m, P))
+    return RABIT_EWORKSPACE;
+  if (!aligned16(workspace)) return RABIT_EALIGN;
+  return dev_status(launch_grad_input((const uint4*)L->planes, L->g, L->h, out, in, P, dY, m, dX,
+                                      dx_dtype, workspace, (hipStream_t)stream));
+}
+
+int rabit_grad_weight(const rabit_layer* L, const uint16_t* X, const uint16_t* dY, int32_t m,
+                      float* dW, float* dg, float* dh, uint32_t flags, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  int s = check_layer(L);
+  if (s) return s;
+  if (!X || !dY || !dW || !dg || !dh) return RABIT_EINVAL;
+  if (flags & ~RABIT_GRAD_ACCUMULATE) return RABIT_EINVAL;
+  if (m < 1 || m > RABIT_MAX_GEMM_M) return RABIT_ESHAPE;
+  if (!aligned16(X) || !aligned16(dY) || !aligned16(dW) || !aligned16(dg) || !aligned16(dh))
+    return RABIT_EALIGN;
+  const int out = L->out_features, in = L->in_features, P = L->n_paths;
+  const size_t wb = (size_t)out * in * 4, gb = (size_t)P * out * 4, hb = (size_t)P * in * 4;
+  const size_t xb = (size_t)m * in * 2, yb = (size_t)m * out * 2;
+  const void* outs[3] = {dW, dg, dh};
+  const size_t ob[3] = {wb, gb, hb};
+  for (int a = 0; a < 3; ++a) {
+    if (overlap(outs[a], ob[a], X, xb) || overlap(outs[a], ob[a], dY, yb) ||
+        overlaps_layer(outs[a], ob[a], L))
+      return RABIT_EINVAL;
+    for (int b = a + 1; b < 3; ++b)
+      if (overlap(outs[a], ob[a], outs[b], ob[b])) return RABIT_EINVAL;
+  }
+  if (!workspace || workspace_bytes < grad_weight_workspace_bytes(out, in, P))
+    return RABIT_EWORKSPACE;
+  if (!aligned16(workspace)) return RABIT_EALIGN;
+  return dev_status(launch_grad_weight((const uint4*)L->planes, L->g, L->h, out, in, P, X, dY, m,
+                                       dW, dg, dh, (flags & RABIT_GRAD_ACCUMULATE) ? 1 : 0,
+                                       workspace, (hipStream_t)stream));
 }
 
 // --------------------------------------------------------------------------
@@ -315,7 +396,7 @@ size_t decode_ws(const rabit_decoder_cfg* c, int batch, DecodeWs* w, void* base)
   return off + w->lin_bytes;
 }
 
-LinSeg seg_of(const rabit_layer& L, double* part) {
+extern "C++" LinSeg seg_of(const rabit_layer& L, double* part) {
   return LinSeg{(const uint4*)L.planes, L.g, L.h, L.out_features, part, L.n_paths};
 }
 

@@ -225,6 +225,18 @@ hipError_t launch_gemm(const uint4* planes, const uint16_t* g, const uint16_t* h
                        const uint16_t* X, int m, void* Y, int y_dtype, void* ws, hipStream_t st,
                        int paths = 2);
 
+// training side (dW, dg, dh; dX through the GEMM of the transposed layer)
+size_t grad_weight_workspace_bytes(int out, int in, int P);
+size_t grad_input_workspace_bytes(int out, int in, int m, int P);
+hipError_t launch_transpose_planes(const uint4* planes, int out, int in, int P, uint4* planes_t,
+                                   hipStream_t st);
+hipError_t launch_grad_input(const uint4* planes, const uint16_t* g, const uint16_t* h, int out,
+                             int in, int P, const uint16_t* dY, int m, void* dX, int dx_dtype,
+                             void* ws, hipStream_t st);
+hipError_t launch_grad_weight(const uint4* planes, const uint16_t* g, const uint16_t* h, int out,
+                              int in, int P, const uint16_t* X, const uint16_t* dY, int m, float* dW,
+                              float* dg, float* dh, int accumulate, void* ws, hipStream_t st);
+
 // decode glue (plain bf16 stand-ins around the binary linear layers)
 hipError_t launch_rmsnorm(const uint16_t* x, uint16_t* y, int batch, int n, float eps, hipStream_t st);
 hipError_t launch_attn_1tok(const float* v, int kv_rows, uint16_t* a, int batch, int n_heads,

@@ -1,0 +1,429 @@
+// Training side of one layer (RaBiT paper §4.2, "Backward Pass and Parameter
+// Updates"): the straight-through gradient to the shared weight, the scale
+// gradients with the cores held constant, and the gradient to the layer input.
+//
+//   dW[o][i]  = Σ_n dY[n][o] X[n][i]                       (gradient of W_hat)
+//   dg_p[o]   = Σ_i dW[o][i] B_p[o][i] h_p[i]              (= Σ_n dY ⊙ B_p (h_p ⊙ x_n))
+//   dh_p[i]   = Σ_o dW[o][i] B_p[o][i] g_p[o]              (= Σ_n x_n ⊙ B_pᵀ (g_p ⊙ dY_n))
+//   dX        = dY W_hat = the prefill GEMM of the layer W_hatᵀ (cores B_pᵀ,
+//               output scales h_p, input scales g_p)
+//
+// k_grad_w computes 256 x 128 tiles of dW on the bf16 matrix cores (MFMA
+// 16x16x32, fp32 accumulation; bf16 x bf16 products are exact in fp32) and,
+// from the same accumulators, the tile's partial sums of dg and dh: dW is
+// written once and never read back. The contraction runs over the tokens n,
+// which are the slow index of both X [N][in] and dY [N][out]; the loaders
+// turn 8 token rows of 4 columns into 4 column chunks of 8 tokens (the MFMA
+// operand order) on the way into LDS.
+#include <algorithm>
+#include <type_traits>
+
+#include "rabit_internal.h"
+
+namespace rabit {
+
+namespace {
+
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int kTI = 256;  // dW tile: columns i
+constexpr int kTO = 128;  // dW tile: rows o
+constexpr int kK = 32;    // tokens per step
+
+__host__ inline size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// 16-byte chunk slot of column q inside one 8-token group: an XOR
+// swizzle so that the loaders' stores (lanes 4 columns apart) and the
+// fragment reads (16 consecutive columns) both spread over the LDS banks
+__device__ __forceinline__ int slot(int q) { return q ^ ((q >> 3) & 3); }
+
+struct GradWs {
+  float* prow;  // [ceil(in/256)][P][128*ceil(out/128)]: per column tile, Σ over its columns
+  float* pcol;  // [ceil(out/128)][P][256*ceil(in/256)]: per row tile, Σ over its rows
+};
+
+__host__ inline GradWs carve_grad(void* ws, int out, int in, int P) {
+  const size_t to = (out + kTO - 1) / kTO, ti = (in + kTI - 1) / kTI;
+  GradWs w;
+  w.prow = (float*)ws;
+  w.pcol = (float*)((char*)ws + a256(ti * P * to * kTO * 4));
+  return w;
+}
+
+__host__ inline size_t grad_ws_bytes(int out, int in, int P) {
+  const size_t to = (out + kTO - 1) / kTO, ti = (in + kTI - 1) / kTI;
+  return a256(ti * P * to * kTO * 4) + a256(to * P * ti * kTI * 4);
+}
+
+// ---------------------------------------------------------------------------
+// Bit transpose of the planes: the layer W_hatᵀ (out' = in, in' = out).
+// One wave per destination slab (rg', kg', p): destination rows i in
+// [64 rg', 64 rg' + 64) are source columns, destination columns o in
+// [128 kg', 128 kg' + 128) are source rows. Lane l holds 64 source bits of
+// rows 128 kg' + l and 128 kg' + 64 + l; ballot c over the wave collects
+// column c of both 64-row blocks, which lane c stores as its unit.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_transpose_planes(const uint32_t* __restrict__ src, int out,
+                                                          int in, int P, uint4* __restrict__ dst) {
+  const int RGt = row_groups(in), KGt = col_groups(out), KGs = col_groups(in);
+  const int RGs = row_groups(out);
+  const int slab = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (slab >= RGt * KGt * P) return;
+  const int l = threadIdx.x & 63;
+  const int p = slab % P, kgt = (slab / P) % KGt, rgt = slab / (P * KGt);
+  const int kgs = rgt >> 1, half = rgt & 1;
+  uint2 w[2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int o = 128 * kgt + 64 * b + l;
+    w[b] = make_uint2(0, 0);
+    if ((o >> 6) < RGs)
+      w[b] = *(const uint2*)(src + 4 * unit_index(o >> 6, kgs, p, o & 63, KGs, P) + 2 * half);
+  }
+  uint4 mine = make_uint4(0, 0, 0, 0);
+#pragma unroll 8
+  for (int c = 0; c < 64; ++c) {
+    const uint32_t s0 = c < 32 ? w[0].x >> c : w[0].y >> (c - 32);
+    const uint32_t s1 = c < 32 ? w[1].x >> c : w[1].y >> (c - 32);
+    const uint64_t m0 = __ballot(s0 & 1u), m1 = __ballot(s1 & 1u);
+    if (l == c) mine = make_uint4((uint32_t)m0, (uint32_t)(m0 >> 32), (uint32_t)m1, (uint32_t)(m1 >> 32));
+  }
+  dst[unit_index(rgt, kgt, p, l, KGt, P)] = mine;
+}
+
+// ---------------------------------------------------------------------------
+// dW tile (256 columns i x 128 rows o) and the tile's scale-gradient partials.
+//
+// Wave w of the workgroup owns i in [128 (w & 1), +128) and o in
+// [64 (w >> 1), +64) of the tile: 8 x 4 matrix tiles of 16 x 16 (a wave tile
+// of 128 x 64 reads 12 KiB of LDS per 32 matrix ops; the LDS read rate, not
+// the matrix cores, bounds smaller wave tiles). MFMA rows are columns i of dW
+// (A = X chunks), MFMA columns are rows o (B = dY chunks), the contraction is
+// 32 tokens: lane (fr, fg) supplies tokens 8 fg .. 8 fg + 7 of column fr. The
+// result lane l, register r holds dW[o = l % 16][i = 4 (l / 16) + r] of each
+// 16 x 16 tile: four consecutive i, one 16-byte store.
+// ---------------------------------------------------------------------------
+template <int P>
+__global__ __launch_bounds__(256, 2) void k_grad_w(const uint16_t* __restrict__ X,
+                                                   const uint16_t* __restrict__ dY, int M, int out,
+                                                   int in, const uint32_t* __restrict__ planes,
+                                                   const uint16_t* __restrict__ g,
+                                                   const uint16_t* __restrict__ h, float* dW,
+                                                   int accumulate, GradWs ws) {
+  const int nbx = (in + kTI - 1) / kTI, nby = (out + kTO - 1) / kTO;
+  // tiles in i-fastest order; each XCD (workgroup id mod 8) takes a
+  // contiguous run of tiles when the count divides by 8
+  const int T = nbx * nby;
+  int tile = blockIdx.x;
+  if ((T & 7) == 0) tile = (blockIdx.x & 7) * (T >> 3) + (blockIdx.x >> 3);
+  const int bx = tile % nbx, by = tile / nbx;
+  const int i0 = bx * kTI, o0 = by * kTO;
+  const int tid = threadIdx.x, l = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wi = wv & 1, wo = wv >> 1;
+  const int fr = l & 15, fg = l >> 4;
+  const int KG = col_groups(in);
+
+  __shared__ __align__(16) uint4 sA[2][4][kTI];  // [buf][token group][slot(i)]: X
+  __shared__ __align__(16) uint4 sB[2][4][kTO];  // [buf][token group][slot(o)]: dY
+  __shared__ uint32_t sBitsW[P][2][4][kTO];  // [p][column group of the tile][word][row o]
+  __shared__ float sG[P][kTO];
+  __shared__ __align__(16) float sH[P][kTI];
+  __shared__ __align__(16) float sRed[2][P][kTI];
+
+  // side loads for the epilogue, issued before the main loop
+  for (int t = tid; t < P * 2 * kTO; t += 256) {
+    const int p = t / (2 * kTO), c = (t / kTO) & 1, r = t % kTO, o = o0 + r;
+    uint4 u = make_uint4(0, 0, 0, 0);
+    if ((o >> 6) < row_groups(out) && 2 * bx + c < KG)
+      u = ((const uint4*)planes)[unit_index(o >> 6, 2 * bx + c, p, o & 63, KG, P)];
+    sBitsW[p][c][0][r] = u.x;
+    sBitsW[p][c][1][r] = u.y;
+    sBitsW[p][c][2][r] = u.z;
+    sBitsW[p][c][3][r] = u.w;
+  }
+  for (int t = tid; t < P * kTO; t += 256) {
+    const int p = t / kTO, r = t % kTO, o = o0 + r;
+    sG[p][r] = o < out ? f16_bits_to_f32(g[(size_t)p * out + o]) : 0.f;
+  }
+  for (int t = tid; t < P * kTI; t += 256) {
+    const int p = t / kTI, r = t % kTI, i = i0 + r;
+    sH[p][r] = i < in ? f16_bits_to_f32(h[(size_t)p * in + i]) : 0.f;
+  }
+
+  // loaders, per thread and step: X columns i0 + 4 qx .. + 3 and dY columns
+  // o0 + 2 qy, + 1, each for tokens 8 ng .. 8 ng + 7 of the step
+  // token group = wave: the rows of a load are uniform (scalar addresses)
+  const int ng = __builtin_amdgcn_readfirstlane(tid >> 6), qx = tid & 63, qy = tid & 63;
+  const int cx = i0 + 4 * qx, cy = o0 + 2 * qy;
+  const bool vx = (in & 3) == 0 && cx + 4 <= in;
+  const bool vy = (out & 1) == 0 && cy + 2 <= out;
+  uint2 rx[8];
+  uint32_t ry[8];
+  // rows past M read row M - 1 (in bounds) and are zeroed
+  auto load = [&](int ks) {
+    const int nb = ks * kK + 8 * ng;
+    if (vx) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) rx[j] = *(const uint2*)(X + (size_t)min(nb + j, M - 1) * in + cx);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const size_t row = (size_t)min(nb + j, M - 1) * in;
+        uint32_t e[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) e[c] = cx + c < in ? X[row + min(cx + c, in - 1)] : 0u;
+        rx[j] = make_uint2(e[0] | (e[1] << 16), e[2] | (e[3] << 16));
+      }
+    }
+    if (vy) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ry[j] = *(const uint32_t*)(dY + (size_t)min(nb + j, M - 1) * out + cy);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const size_t row = (size_t)min(nb + j, M - 1) * out;
+        const uint32_t e0 = cy < out ? dY[row + min(cy, out - 1)] : 0u;
+        const uint32_t e1 = cy + 1 < out ? dY[row + min(cy + 1, out - 1)] : 0u;
+        ry[j] = e0 | (e1 << 16);
+      }
+    }
+    if (nb + 8 > M) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (nb + j >= M) {
+          rx[j] = make_uint2(0, 0);
+          ry[j] = 0u;
+        }
+    }
+  };
+  // 8 token rows of a column pair -> two chunks of 8 tokens (one per column)
+  auto chunks = [](const uint32_t (&v)[8], uint4& lo, uint4& hi) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      (&lo.x)[k] = (v[2 * k] & 0xFFFFu) | (v[2 * k + 1] << 16);
+      (&hi.x)[k] = (v[2 * k] >> 16) | (v[2 * k + 1] & 0xFFFF0000u);
+    }
+  };
+  auto store = [&](int buf) {
+    uint32_t t[8];
+    uint4 c0, c1;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) t[j] = rx[j].x;
+    chunks(t, c0, c1);
+    sA[buf][ng][slot(4 * qx)] = c0;
+    sA[buf][ng][slot(4 * qx + 1)] = c1;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) t[j] = rx[j].y;
+    chunks(t, c0, c1);
+    sA[buf][ng][slot(4 * qx + 2)] = c0;
+    sA[buf][ng][slot(4 * qx + 3)] = c1;
+    chunks(ry, c0, c1);
+    sB[buf][ng][slot(2 * qy)] = c0;
+    sB[buf][ng][slot(2 * qy + 1)] = c1;
+  };
+
+  v4f acc[8][4];
+#pragma unroll
+  for (int a = 0; a < 8; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+  const int nsteps = (M + kK - 1) / kK;
+  if (nsteps > 0) {
+    load(0);
+    store(0);
+  }
+  __syncthreads();
+  for (int ks = 0; ks < nsteps; ++ks) {
+    const int buf = ks & 1;
+    if (ks + 1 < nsteps) load(ks + 1);  // in flight during the matrix ops
+    v8bf fb[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) fb[b] = __builtin_bit_cast(v8bf, sB[buf][fg][slot(64 * wo + 16 * b + fr)]);
+#pragma unroll
+    for (int a = 0; a < 8; ++a) {
+      const v8bf fa = __builtin_bit_cast(v8bf, sA[buf][fg][slot(128 * wi + 16 * a + fr)]);
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb[b], acc[a][b], 0, 0, 0);
+    }
+    if (ks + 1 < nsteps) store(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- scale-gradient partials, one 16-column block a at a time. Lane
+  // (fr, fg) of tile (a, b) holds row o = o0 + 64 wo + 16 b + fr, columns
+  // i = i0 + 128 wi + 16 a + 4 fg + r. The bit of (o, i) is bit i % 32 of
+  // word (i % 128) / 32 = a / 2 of the row's unit in column group 2 bx + wi.
+  // Row sums (dg): each lane adds its columns, then the 4 lane groups
+  // (xor 16, 32), then the two waves that share the rows (in LDS, wave wi = 0
+  // first). Column sums (dh): each lane adds its 4 rows, then the 16 lanes of
+  // its DPP row, then the two waves that share the columns.
+  // pass 1, column sums (dh). The two passes are split by a barrier: with both
+  // sums in one pass the scheduler keeps every accumulator alive to the end
+  // and the kernel spills.
+#pragma unroll
+  for (int a = 0; a < 8; ++a) {
+    const int il = 128 * wi + 16 * a + 4 * fg;  // tile column of register r = 0
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      float cs[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int ol = 64 * wo + 16 * b + fr;
+        const uint32_t word = sBitsW[p][wi][a >> 1][ol];
+        const float go = sG[p][ol];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          // B_p = -1 flips the sign of the scale factor, not of dW
+          const uint32_t sgn = ((word >> ((16 * a + 4 * fg + r) & 31)) & 1u) << 31;
+          cs[r] += acc[a][b][r] * __uint_as_float(__float_as_uint(go) ^ sgn);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float v = cs[r];
+        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xf, 0xf, false));
+        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xf, 0xf, false));
+        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xf, 0xf, false));
+        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xf, 0xf, false));
+        cs[r] = v;
+      }
+      if (fr == 0) *(float4*)&sRed[wo][p][il] = make_float4(cs[0], cs[1], cs[2], cs[3]);
+    }
+  }
+  __syncthreads();
+  for (int t = tid; t < P * kTI; t += 256) {
+    const int p = t / kTI, r = t % kTI;
+    ws.pcol[((size_t)by * P + p) * ((size_t)nbx * kTI) + i0 + r] = sRed[0][p][r] + sRed[1][p][r];
+  }
+  __syncthreads();
+
+  // pass 2, dW stores and row sums (dg). A full tile without accumulation
+  // stores 16 bytes per lane and tile with no guards; the other copy guards
+  // every element.
+  float rs[P][4];
+#pragma unroll
+  for (int p = 0; p < P; ++p)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) rs[p][b] = 0.f;
+  auto pass2 = [&](auto fast_tag) {
+    constexpr bool kFast = decltype(fast_tag)::value;
+#pragma unroll
+    for (int a = 0; a < 8; ++a) {
+      const int il = 128 * wi + 16 * a + 4 * fg;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int o = o0 + 64 * wo + 16 * b + fr, i = i0 + il;
+        float* d = dW + (size_t)o * in + i;
+        if (kFast) {
+          *(float4*)d = make_float4(acc[a][b][0], acc[a][b][1], acc[a][b][2], acc[a][b][3]);
+        } else if (o < out) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (i + r < in) d[r] = accumulate ? d[r] + acc[a][b][r] : acc[a][b][r];
+        }
+      }
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        const float4 hv = *(const float4*)&sH[p][il];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const uint32_t word = sBitsW[p][wi][a >> 1][64 * wo + 16 * b + fr];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const uint32_t sgn = ((word >> ((16 * a + 4 * fg + r) & 31)) & 1u) << 31;
+            rs[p][b] += acc[a][b][r] * __uint_as_float(__float_as_uint((&hv.x)[r]) ^ sgn);
+          }
+        }
+      }
+    }
+  };
+  if ((in & 3) == 0 && i0 + kTI <= in && o0 + kTO <= out && !accumulate)
+    pass2(std::true_type{});
+  else
+    pass2(std::false_type{});
+#pragma unroll
+  for (int p = 0; p < P; ++p)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      float v = rs[p][b];
+      v += __shfl_xor(v, 16, 64);
+      v += __shfl_xor(v, 32, 64);
+      if (fg == 0) sRed[wi][p][64 * wo + 16 * b + fr] = v;
+    }
+  __syncthreads();
+  for (int t = tid; t < P * kTO; t += 256) {
+    const int p = t / kTO, r = t % kTO;
+    ws.prow[((size_t)bx * P + p) * ((size_t)nby * kTO) + o0 + r] = sRed[0][p][r] + sRed[1][p][r];
+  }
+}
+
+// dg[p][o] = Σ_bx prow[bx][p][o], dh[p][i] = Σ_by pcol[by][p][i], ascending
+__global__ __launch_bounds__(256) void k_grad_reduce(GradWs ws, int out, int in, int P,
+                                                     float* dg, float* dh, int accumulate) {
+  const int nbx = (in + kTI - 1) / kTI, nby = (out + kTO - 1) / kTO;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  const int ng = P * out;
+  if (idx < ng) {
+    const int p = idx / out, o = idx % out;
+    float v = 0.f;
+    for (int b = 0; b < nbx; ++b) v += ws.prow[((size_t)b * P + p) * ((size_t)nby * kTO) + o];
+    dg[idx] = accumulate ? dg[idx] + v : v;
+  } else if (idx < ng + P * in) {
+    const int k = idx - ng, p = k / in, i = k % in;
+    float v = 0.f;
+    for (int b = 0; b < nby; ++b) v += ws.pcol[((size_t)b * P + p) * ((size_t)nbx * kTI) + i];
+    dh[k] = accumulate ? dh[k] + v : v;
+  }
+}
+
+}  // namespace
+
+size_t grad_weight_workspace_bytes(int out, int in, int P) { return grad_ws_bytes(out, in, P); }
+
+size_t grad_input_workspace_bytes(int out, int in, int m, int P) {
+  // transposed planes, then the prefill GEMM's workspace for the layer W_hatᵀ
+  size_t planes_t = (size_t)row_groups(in) * col_groups(out) * P * 64 * 16;
+  return a256(planes_t) + gemm_workspace_bytes(in, out, m);
+}
+
+hipError_t launch_transpose_planes(const uint4* planes, int out, int in, int P, uint4* planes_t,
+                                   hipStream_t st) {
+  const int slabs = row_groups(in) * col_groups(out) * P;
+  hipLaunchKernelGGL(k_transpose_planes, dim3((slabs + 3) / 4), dim3(256), 0, st,
+                     (const uint32_t*)planes, out, in, P, planes_t);
+  return hipGetLastError();
+}
+
+hipError_t launch_grad_input(const uint4* planes, const uint16_t* g, const uint16_t* h, int out,
+                             int in, int P, const uint16_t* dY, int m, void* dX, int dx_dtype,
+                             void* ws, hipStream_t st) {
+  uint4* pt = (uint4*)ws;
+  const size_t planes_t = (size_t)row_groups(in) * col_groups(out) * P * 64 * 16;
+  hipError_t e = launch_transpose_planes(planes, out, in, P, pt, st);
+  if (e != hipSuccess) return e;
+  // W_hatᵀ: out' = in, in' = out, output scales h, input scales g
+  return launch_gemm(pt, h, g, in, out, dY, m, dX, dx_dtype, (char*)ws + a256(planes_t), st, P);
+}
+
+hipError_t launch_grad_weight(const uint4* planes, const uint16_t* g, const uint16_t* h, int out,
+                              int in, int P, const uint16_t* X, const uint16_t* dY, int m, float* dW,
+                              float* dg, float* dh, int accumulate, void* ws, hipStream_t st) {
+  GradWs w = carve_grad(ws, out, in, P);
+  const int tiles = ((out + kTO - 1) / kTO) * ((in + kTI - 1) / kTI);
+  if (P == 3)
+    hipLaunchKernelGGL(k_grad_w<3>, dim3(tiles), dim3(256), 0, st, X, dY, m, out, in,
+                       (const uint32_t*)planes, g, h, dW, accumulate, w);
+  else
+    hipLaunchKernelGGL(k_grad_w<2>, dim3(tiles), dim3(256), 0, st, X, dY, m, out, in,
+                       (const uint32_t*)planes, g, h, dW, accumulate, w);
+  const int n = P * (out + in);
+  hipLaunchKernelGGL(k_grad_reduce, dim3((n + 255) / 256), dim3(256), 0, st, w, out, in, P, dg, dh,
+                     accumulate);
+  return hipGetLastError();
+}
+
+}  // namespace rabit

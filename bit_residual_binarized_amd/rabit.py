@@ -35,7 +35,9 @@ EXPORTS = [
     "rabit_gemm_workspace_bytes", "rabit_pack", "rabit_unpack", "rabit_gemv", "rabit_gemm",
     "rabit_decode_workspace_bytes", "rabit_decode_step", "rabit_status_string",
     "rabit_layout_version", "rabit_test_f64_to_16", "rabit_gemv_partial", "rabit_gemv_reduce",
-    "rabit_gemv_partial_multi", "rabit_stream_read",
+    "rabit_gemv_partial_multi", "rabit_stream_read", "rabit_grad_input_workspace_bytes",
+    "rabit_grad_weight_workspace_bytes", "rabit_transpose_planes", "rabit_grad_input",
+    "rabit_grad_weight",
 ]
 
 
@@ -102,6 +104,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "rabit_layout_version": (i32, []),
         "rabit_test_f64_to_16": (ctypes.c_int, [vp, vp, i32, i32, vp]),
         "rabit_stream_read": (ctypes.c_int, [vp, sz, vp, vp]),
+        "rabit_grad_input_workspace_bytes": (sz, [i32, i32, i32]),
+        "rabit_grad_weight_workspace_bytes": (sz, [i32, i32]),
+        "rabit_transpose_planes": (ctypes.c_int, [lp, vp, vp]),
+        "rabit_grad_input": (ctypes.c_int, [lp, vp, i32, vp, i32, vp, sz, vp]),
+        "rabit_grad_weight": (ctypes.c_int, [lp, vp, vp, i32, vp, vp, vp, u32, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -274,6 +281,74 @@ def gemm(layer: PackedLayer, xm: torch.Tensor, y_dtype: int = RABIT_OUT_F32,
     _check(lib.rabit_gemm(ctypes.byref(lc), _ptr(xm), m, _ptr(y), y_dtype, _ptr(workspace),
                           workspace.numel(), _stream(stream)), "rabit_gemm")
     return y
+
+
+# --- training side (rabit_grad_* in rabit.h) ---
+RABIT_GRAD_ACCUMULATE = 1
+
+
+def transpose_planes(layer: PackedLayer, out: torch.Tensor | None = None,
+                     stream=None) -> torch.Tensor:
+    """Planes of the layer W_hatᵀ (uint8 buffer in layout V1)."""
+    nb = planes_bytes(layer.in_features, layer.out_features, layer.n_paths)
+    if out is None:
+        out = torch.empty(nb, dtype=torch.uint8, device=layer.planes.device)
+    lc = layer.c()
+    _check(load().rabit_transpose_planes(ctypes.byref(lc), _ptr(out), _stream(stream)),
+           "rabit_transpose_planes")
+    return out
+
+
+def grad_input_workspace(layer: PackedLayer, m: int) -> torch.Tensor:
+    nb = load().rabit_grad_input_workspace_bytes(layer.out_features, layer.in_features, m)
+    return _ws(nb, layer.planes.device)
+
+
+def grad_weight_workspace(layer: PackedLayer) -> torch.Tensor:
+    nb = load().rabit_grad_weight_workspace_bytes(layer.out_features, layer.in_features)
+    return _ws(nb, layer.planes.device)
+
+
+def grad_input(layer: PackedLayer, dy: torch.Tensor, dx_dtype: int = RABIT_OUT_F32,
+               dx: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+               stream=None) -> torch.Tensor:
+    """dX = dY W_hat for dY [M][out] bf16."""
+    lib = load()
+    assert dy.dtype == torch.bfloat16 and dy.is_contiguous()
+    m = dy.shape[0]
+    if dx is None:
+        dt = torch.float32 if dx_dtype == RABIT_OUT_F32 else torch.bfloat16
+        dx = torch.empty(m, layer.in_features, dtype=dt, device=dy.device)
+    if workspace is None:
+        workspace = grad_input_workspace(layer, m)
+    lc = layer.c()
+    _check(lib.rabit_grad_input(ctypes.byref(lc), _ptr(dy), m, _ptr(dx), dx_dtype, _ptr(workspace),
+                                workspace.numel(), _stream(stream)), "rabit_grad_input")
+    return dx
+
+
+def grad_weight(layer: PackedLayer, x: torch.Tensor, dy: torch.Tensor, dw=None, dg=None, dh=None,
+                accumulate: bool = False, workspace: torch.Tensor | None = None, stream=None):
+    """(dW [out][in], dg [P][out], dh [P][in]) in float32 for X [M][in] and
+    dY [M][out] (bf16)."""
+    lib = load()
+    assert x.dtype == torch.bfloat16 and dy.dtype == torch.bfloat16
+    assert x.is_contiguous() and dy.is_contiguous() and x.shape[0] == dy.shape[0]
+    m, dev, P = x.shape[0], x.device, layer.n_paths
+    if dw is None:
+        dw = torch.empty(layer.out_features, layer.in_features, dtype=torch.float32, device=dev)
+    if dg is None:
+        dg = torch.empty(P, layer.out_features, dtype=torch.float32, device=dev)
+    if dh is None:
+        dh = torch.empty(P, layer.in_features, dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = grad_weight_workspace(layer)
+    lc = layer.c()
+    _check(lib.rabit_grad_weight(ctypes.byref(lc), _ptr(x), _ptr(dy), m, _ptr(dw), _ptr(dg),
+                                 _ptr(dh), RABIT_GRAD_ACCUMULATE if accumulate else 0,
+                                 _ptr(workspace), workspace.numel(), _stream(stream)),
+           "rabit_grad_weight")
+    return dw, dg, dh
 
 
 MATRICES = ("q", "k", "v", "o", "gate", "up", "down")

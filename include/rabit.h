@@ -212,6 +212,71 @@ int rabit_gemm(const rabit_layer *layer, const uint16_t *X, int32_t m,
                void *stream);
 
 /*
+ * Training side of one layer (paper §4.2, "The Coupled Forward Pass" and
+ * "Backward Pass and Parameter Updates"). A training step derives the cores
+ * from the shared weight W_FP with the current scales (rabit_pack with
+ * RABIT_SCALES_GIVEN) and runs the forward with rabit_gemm; the calls below
+ * are its backward, for the loss gradient dY at the layer output. The pages
+ * omit the formulas; the reading used here:
+ *   dW   = Σ_n dY[n] X[n]ᵀ, the gradient of the effective weight W_hat, handed
+ *          to W_FP unchanged (the straight-through estimator), d_out x d_in;
+ *   dg_p = Σ_n dY[n] ⊙ (B_p (h_p ⊙ X[n])), dh_p = Σ_n X[n] ⊙ (B_pᵀ (g_p ⊙ dY[n]))
+ *          (chain rule with the cores B_p held constant, summed over the
+ *          samples of the batch);
+ *   dX   = dY W_hat (the gradient passed to the layer below).
+ * The scales are the layer's fp16 values.
+ */
+#define RABIT_GRAD_ACCUMULATE 1u  /* add into dW, dg, dh instead of overwriting */
+
+/* Workspace bytes of rabit_grad_input / rabit_grad_weight (2 or 3 paths). */
+size_t rabit_grad_input_workspace_bytes(int32_t out_features, int32_t in_features, int32_t m);
+size_t rabit_grad_weight_workspace_bytes(int32_t out_features, int32_t in_features);
+
+/*
+ * The planes of the layer W_hatᵀ (out' = in_features, in' = out_features,
+ * cores B_pᵀ; its scales are the layer's h as g' and g as h', used in place):
+ * bit (o, i) of B_p is written as bit (i, o) of path p in layout V1.
+ * planes_t  device, rabit_planes_bytes(in_features, out_features, n_paths)
+ *           bytes, written entirely; must not overlap the layer's buffers.
+ * Errors: RABIT_EINVAL, RABIT_ESHAPE, RABIT_EALIGN, RABIT_EUNSUPPORTED,
+ * RABIT_EDEVICE.
+ */
+int rabit_transpose_planes(const rabit_layer *layer, void *planes_t, void *stream);
+
+/*
+ * dX[n][j] = Σ_i dY[n][i] W_hat[i][j]: the planes are transposed into the
+ * workspace, then the prefill GEMM of W_hatᵀ runs (same arithmetic as
+ * rabit_gemm, with dY in the role of X).
+ * dY   device bfloat16 bit patterns [M][out], row-major.
+ * M    1 .. RABIT_MAX_GEMM_M.
+ * dX   device [M][in] float32 or bfloat16 (dx_dtype), written entirely; must
+ *      not overlap dY or the layer's buffers.
+ * Errors as rabit_gemm.
+ */
+int rabit_grad_input(const rabit_layer *layer, const uint16_t *dY, int32_t m, void *dX,
+                     int32_t dx_dtype, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * dW, dg and dh of the layer for one batch.
+ * X     device bfloat16 bit patterns [M][in] (the layer input of the forward).
+ * dY    device bfloat16 bit patterns [M][out].
+ * M     1 .. RABIT_MAX_GEMM_M.
+ * dW    device float32 [out][in], row-major.
+ * dg    device float32 [n_paths][out];  dh  device float32 [n_paths][in].
+ * flags 0 (overwrite) or RABIT_GRAD_ACCUMULATE (add to the values present,
+ *       e.g. over micro-batches).
+ * Arithmetic: dW on the bf16 matrix cores (products exact, fp32 sums);
+ * dg, dh from the fp32 dW values of each 128 x 128 tile (fp32 sums, tiles
+ * added in ascending order). Outputs must not overlap each other, X, dY or
+ * the layer's buffers.
+ * Errors: RABIT_EINVAL (null, flags, aliasing), RABIT_ESHAPE, RABIT_EALIGN,
+ * RABIT_EUNSUPPORTED, RABIT_EWORKSPACE, RABIT_EDEVICE.
+ */
+int rabit_grad_weight(const rabit_layer *layer, const uint16_t *X, const uint16_t *dY,
+                      int32_t m, float *dW, float *dg, float *dh, uint32_t flags,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Decoder configuration for rabit_decode_step (a Llama-style block; the pages
  * time Llama2 decoding, Table 7, without defining the block).
  */

@@ -169,3 +169,46 @@ def test_stream_read_errors(lib):
     assert lib.rabit_stream_read(P, 64, ctypes.c_void_p((2 << 20) + 4), None) == rabit.RABIT_EALIGN
     assert lib.rabit_stream_read(P, 72, Q, None) == rabit.RABIT_EALIGN
     assert lib.rabit_stream_read(P, 0, Q, None) == rabit.RABIT_OK  # nothing runs
+
+
+def test_training_sizes_and_errors(lib):
+    assert lib.rabit_grad_weight_workspace_bytes(4096, 11008) > 0
+    assert lib.rabit_grad_weight_workspace_bytes(0, 16) == 0
+    assert lib.rabit_grad_input_workspace_bytes(4096, 11008, 2048) > \
+        lib.rabit_gemm_workspace_bytes(11008, 4096, 2048)
+    assert lib.rabit_grad_input_workspace_bytes(4096, 4096, 0) == 0
+    L = fake_layer()
+    X, dY, dW, dg, dh, ws = (FAKE + (k << 32) for k in range(3, 9))
+    big = 1 << 40
+
+    def gw(layer=L, x=X, dy=dY, m=64, dw=dW, g=dg, h=dh, flags=0, w=ws, wsb=big):
+        return lib.rabit_grad_weight(ctypes.byref(layer), x, dy, m, dw, g, h, flags, w, wsb, None)
+    assert gw(x=0) == rabit.RABIT_EINVAL
+    assert gw(h=0) == rabit.RABIT_EINVAL
+    assert gw(flags=2) == rabit.RABIT_EINVAL
+    assert gw(m=0) == rabit.RABIT_ESHAPE
+    assert gw(m=(1 << 20) + 1) == rabit.RABIT_ESHAPE
+    assert gw(dw=dW + 4) == rabit.RABIT_EALIGN
+    assert gw(dw=X) == rabit.RABIT_EINVAL                 # dW aliases X
+    assert gw(g=dW + 256) == rabit.RABIT_EINVAL           # dg inside dW
+    assert gw(g=FAKE + (1 << 30)) == rabit.RABIT_EINVAL   # dg aliases the layer's g
+    assert gw(wsb=16) == rabit.RABIT_EWORKSPACE
+    assert gw(w=0) == rabit.RABIT_EWORKSPACE
+    assert gw(layer=fake_layer(paths=4)) == rabit.RABIT_EUNSUPPORTED
+    assert gw(layer=fake_layer(paths=3), wsb=16) == rabit.RABIT_EWORKSPACE
+
+    def gi(layer=L, dy=dY, m=64, dx=dW, dt=0, w=ws, wsb=big):
+        return lib.rabit_grad_input(ctypes.byref(layer), dy, m, dx, dt, w, wsb, None)
+    assert gi(dy=0) == rabit.RABIT_EINVAL
+    assert gi(dt=3) == rabit.RABIT_EINVAL
+    assert gi(m=0) == rabit.RABIT_ESHAPE
+    assert gi(dx=dY) == rabit.RABIT_EINVAL                # dX aliases dY
+    assert gi(dx=FAKE) == rabit.RABIT_EINVAL              # dX aliases the planes
+    assert gi(wsb=16) == rabit.RABIT_EWORKSPACE
+    assert gi(w=ws + 8) == rabit.RABIT_EALIGN
+
+    assert lib.rabit_transpose_planes(ctypes.byref(L), 0, None) == rabit.RABIT_EINVAL
+    assert lib.rabit_transpose_planes(ctypes.byref(L), FAKE + 16, None) == rabit.RABIT_EINVAL
+    assert lib.rabit_transpose_planes(ctypes.byref(L), dW + 8, None) == rabit.RABIT_EALIGN
+    assert lib.rabit_transpose_planes(ctypes.byref(fake_layer(version=0)), dW, None) == \
+        rabit.RABIT_EINVAL
