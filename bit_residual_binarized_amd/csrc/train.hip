@@ -31,6 +31,12 @@ constexpr int kTI = 256;  // dW tile: columns i
 constexpr int kTO = 128;  // dW tile: rows o
 constexpr int kK = 32;    // tokens per step
 
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// word 3 of a raw buffer descriptor on this architecture family (no format
+// conversion, no swizzle): out-of-range reads return 0
+constexpr int kBufferWord3 = 0x00020000;
+
 __host__ inline size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // 16-byte chunk slot of column q inside one 8-token group: an XOR
@@ -161,49 +167,61 @@ __global__ __launch_bounds__(256, 2) void k_grad_w(const uint16_t* __restrict__ 
   const bool vy = (out & 1) == 0 && cy + 2 <= out;
   uint2 rx[8];
   uint32_t ry[8];
-  // rows past M read row M - 1 (in bounds) and are zeroed
+  // Full-width columns: raw buffer loads from a per-step scalar base, the
+  // lane's column as the only per-lane offset and the token row as the scalar
+  // offset; the descriptor covers rows up to M only, so rows past M read 0.
+  // Ragged columns: element loads with clamped indices, masked.
   auto load = [&](int ks) {
-    const int nb = ks * kK + 8 * ng;
+    const int n0 = ks * kK;
+    const uint32_t left = (uint32_t)(M - n0);  // rows from n0 to M (>= 1)
     if (vx) {
+      const uint64_t nbytes = (uint64_t)left * in * 2;
+      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(X + (size_t)n0 * in), (short)0, (int)(nbytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : nbytes),
+          kBufferWord3);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) rx[j] = *(const uint2*)(X + (size_t)min(nb + j, M - 1) * in + cx);
+      for (int j = 0; j < 8; ++j) {
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, 2 * cx,
+                                                             (8 * ng + j) * in * 2, 0);
+        rx[j] = make_uint2(v.x, v.y);
+      }
     } else {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const size_t row = (size_t)min(nb + j, M - 1) * in;
+        const int n = n0 + 8 * ng + j;
+        const size_t row = (size_t)min(n, M - 1) * in;
         uint32_t e[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) e[c] = cx + c < in ? X[row + min(cx + c, in - 1)] : 0u;
-        rx[j] = make_uint2(e[0] | (e[1] << 16), e[2] | (e[3] << 16));
+        rx[j] = n < M ? make_uint2(e[0] | (e[1] << 16), e[2] | (e[3] << 16)) : make_uint2(0, 0);
       }
     }
     if (vy) {
+      const uint64_t nbytes = (uint64_t)left * out * 2;
+      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(dY + (size_t)n0 * out), (short)0, (int)(nbytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : nbytes),
+          kBufferWord3);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) ry[j] = *(const uint32_t*)(dY + (size_t)min(nb + j, M - 1) * out + cy);
+      for (int j = 0; j < 8; ++j)
+        ry[j] = __builtin_amdgcn_raw_buffer_load_b32(r, 2 * cy, (8 * ng + j) * out * 2, 0);
     } else {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const size_t row = (size_t)min(nb + j, M - 1) * out;
+        const int n = n0 + 8 * ng + j;
+        const size_t row = (size_t)min(n, M - 1) * out;
         const uint32_t e0 = cy < out ? dY[row + min(cy, out - 1)] : 0u;
         const uint32_t e1 = cy + 1 < out ? dY[row + min(cy + 1, out - 1)] : 0u;
-        ry[j] = e0 | (e1 << 16);
+        ry[j] = n < M ? (e0 | (e1 << 16)) : 0u;
       }
     }
-    if (nb + 8 > M) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (nb + j >= M) {
-          rx[j] = make_uint2(0, 0);
-          ry[j] = 0u;
-        }
-    }
   };
-  // 8 token rows of a column pair -> two chunks of 8 tokens (one per column)
+  // 8 token rows of a column pair -> two chunks of 8 tokens (one per column):
+  // dword k of a chunk holds tokens 2k, 2k + 1 (one byte permute each)
   auto chunks = [](const uint32_t (&v)[8], uint4& lo, uint4& hi) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      (&lo.x)[k] = (v[2 * k] & 0xFFFFu) | (v[2 * k + 1] << 16);
-      (&hi.x)[k] = (v[2 * k] >> 16) | (v[2 * k + 1] & 0xFFFF0000u);
+      (&lo.x)[k] = __builtin_amdgcn_perm(v[2 * k + 1], v[2 * k], 0x05040100u);
+      (&hi.x)[k] = __builtin_amdgcn_perm(v[2 * k + 1], v[2 * k], 0x07060302u);
     }
   };
   auto store = [&](int buf) {
