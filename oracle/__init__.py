@@ -12,3 +12,4 @@ of ``oracle.rabit_oracle`` for which pin covers which function.
 """
 from .rabit_oracle import *  # noqa: F401,F403
 from .rabit_train import *  # noqa: F401,F403
+from .rabit_init import *  # noqa: F401,F403
