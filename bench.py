@@ -217,7 +217,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of graph replay")
     ap.add_argument("--workload", default="mlp7b",
-                    choices=["mlp7b", "layer4096", "llama3-8b", "gemm", "llama70b", "table7", "train"],
+                    choices=["mlp7b", "layer4096", "llama3-8b", "gemm", "llama70b", "table7", "train",
+                             "init"],
                     help="mlp7b (default): the headline decode workload; the others measure the "
                          "remaining configurations (one JSON line each)")
     args = ap.parse_args()
@@ -236,7 +237,7 @@ def main():
     if args.workload != "mlp7b":
         extra = {"layer4096": bench_layer4096, "llama3-8b": bench_llama3_8b, "gemm": bench_gemm,
                  "llama70b": bench_llama70b, "table7": bench_table7,
-                 "train": bench_train}[args.workload]
+                 "train": bench_train, "init": bench_init}[args.workload]
         print(json.dumps(extra(args, rabit, torch)), flush=True)
         return
     hidden, ffn = 4096, 11008
@@ -708,6 +709,41 @@ def bench_train(args, rabit, torch):
                                      "unit": "TFLOP/s", "achieved": round(best_gw, 1),
                                      "frac": round(best_gw / 2500.0, 4),
                                      "launch_ms_gate_M8192": round(gw_launch, 4)})
+
+
+def bench_init(args, rabit, torch):
+    """Initialisation of the scales: iterative residual SVID (20 sweeps, 5
+    power passes per re-fit, two paths) on the Llama-2-7B layer shapes."""
+    from synth.inputs import seed_w, weight_f32
+    res = {}
+    P, T, K = 2, 20, 5
+    best = None
+    for (N, K_in, name) in ((4096, 4096, "q"), (11008, 4096, "gate"), (4096, 11008, "down")):
+        w = weight_f32(N, K_in, seed_w(7, 0, name), device="cuda")
+        g = torch.zeros(P, N, device="cuda")
+        h = torch.zeros(P, K_in, device="cuda")
+        pl = torch.zeros(rabit.planes_bytes(N, K_in, P), dtype=torch.uint8, device="cuda")
+        ws = rabit.svid_workspace(N, K_in)
+        run = lambda i: rabit.svid_init(w, P, T, K, g=g, h=h, planes=pl, workspace=ws)
+        run(0)
+        ms = _events_ms(torch, run, 1, reps=2)
+        passes = T * P * K
+        # per pass: W (4 B) and the other path's bits (1/8 B) per weight
+        alg = passes * N * K_in * (4 + (P - 1) / 8)
+        gbs = alg / (ms * 1e-3) / 1e9
+        res[f"{N}x{K_in}"] = {"ms": round(ms, 3), "passes": passes, "alg_gbs": round(gbs, 1),
+                              "us_per_pass": round(1e3 * ms / passes, 2)}
+        log(f"svid init {N}x{K_in}: {ms:.2f} ms for {passes} passes ({1e3 * ms / passes:.1f} us/pass), "
+            f"{gbs:.0f} GB/s algorithmic")
+        if name == "gate":
+            best = gbs
+        del w, g, h, pl, ws
+    return _line("Iterative residual SVID initialisation, algorithmic GB/s (W read per power pass), "
+                 "Llama-2-7B gate shape", round(best, 1), "GB/s",
+                 {"workload": "llama2-7b-svid-init", "sweeps": T, "power_passes": K, "paths": P},
+                 dtype="f32", runs=res,
+                 roofline={"bound": "hbm", "kernel": "k_svid_pass", "peak": 8000.0, "unit": "GB/s",
+                           "achieved": round(best, 1), "frac": round(best / 8000.0, 4)})
 
 
 def bench_llama70b(args, rabit, torch):

@@ -313,6 +313,45 @@ int rabit_grad_weight(const rabit_layer* L, const uint16_t* X, const uint16_t* d
 }
 
 // --------------------------------------------------------------------------
+// initialisation (iterative residual SVID)
+// --------------------------------------------------------------------------
+size_t rabit_svid_workspace_bytes(int32_t out, int32_t in) {
+  if (check_dims(out, in)) return 0;
+  return svid_workspace_bytes(out, in);
+}
+
+int rabit_svid_init(const float* W, int32_t out, int32_t in, int32_t n_paths, int32_t sweeps,
+                    int32_t passes, const float* f_out, const float* f_in, uint32_t flags, float* g,
+                    float* h, void* planes, void* workspace, size_t workspace_bytes, void* stream) {
+  if (n_paths != 2 && n_paths != 3) return RABIT_EUNSUPPORTED;
+  int s = check_dims(out, in);
+  if (s) return s;
+  if (sweeps < 1 || sweeps > 1000 || passes < 1 || passes > 63 || (passes & 1) == 0)
+    return RABIT_ESHAPE;
+  if (!W || !g || !h || !planes) return RABIT_EINVAL;
+  if (flags & ~RABIT_SVID_CONTINUE) return RABIT_EINVAL;
+  if (!aligned16(W) || !aligned16(g) || !aligned16(h) || !aligned16(planes) ||
+      (f_out && !aligned16(f_out)) || (f_in && !aligned16(f_in)))
+    return RABIT_EALIGN;
+  const size_t wb = (size_t)out * in * 4, gb = (size_t)n_paths * out * 4,
+               hb = (size_t)n_paths * in * 4, pb = rabit_planes_bytes(out, in, n_paths);
+  const void* outs[3] = {g, h, planes};
+  const size_t ob[3] = {gb, hb, pb};
+  for (int a = 0; a < 3; ++a) {
+    if (overlap(outs[a], ob[a], W, wb) || (f_out && overlap(outs[a], ob[a], f_out, (size_t)out * 4)) ||
+        (f_in && overlap(outs[a], ob[a], f_in, (size_t)in * 4)))
+      return RABIT_EINVAL;
+    for (int b = a + 1; b < 3; ++b)
+      if (overlap(outs[a], ob[a], outs[b], ob[b])) return RABIT_EINVAL;
+  }
+  if (!workspace || workspace_bytes < svid_workspace_bytes(out, in)) return RABIT_EWORKSPACE;
+  if (!aligned16(workspace)) return RABIT_EALIGN;
+  return dev_status(launch_svid(W, out, in, n_paths, sweeps, passes, f_out, f_in,
+                                (flags & RABIT_SVID_CONTINUE) != 0, g, h, (uint4*)planes, workspace,
+                                (hipStream_t)stream));
+}
+
+// --------------------------------------------------------------------------
 // decode step
 // --------------------------------------------------------------------------
 namespace {

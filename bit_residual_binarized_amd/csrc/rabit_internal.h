@@ -237,6 +237,12 @@ hipError_t launch_grad_weight(const uint4* planes, const uint16_t* g, const uint
                               int in, int P, const uint16_t* X, const uint16_t* dY, int m, float* dW,
                               float* dg, float* dh, int accumulate, void* ws, hipStream_t st);
 
+// initialisation: iterative residual SVID (g, h float32 [P][out], [P][in])
+size_t svid_workspace_bytes(int out, int in);
+hipError_t launch_svid(const float* W, int out, int in, int P, int sweeps, int passes,
+                       const float* f_out, const float* f_in, bool cont, float* g, float* h,
+                       uint4* planes, void* ws, hipStream_t st);
+
 // decode glue (plain bf16 stand-ins around the binary linear layers)
 hipError_t launch_rmsnorm(const uint16_t* x, uint16_t* y, int batch, int n, float eps, hipStream_t st);
 hipError_t launch_attn_1tok(const float* v, int kv_rows, uint16_t* a, int batch, int n_heads,

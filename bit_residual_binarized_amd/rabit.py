@@ -37,7 +37,7 @@ EXPORTS = [
     "rabit_layout_version", "rabit_test_f64_to_16", "rabit_gemv_partial", "rabit_gemv_reduce",
     "rabit_gemv_partial_multi", "rabit_stream_read", "rabit_grad_input_workspace_bytes",
     "rabit_grad_weight_workspace_bytes", "rabit_transpose_planes", "rabit_grad_input",
-    "rabit_grad_weight",
+    "rabit_grad_weight", "rabit_svid_workspace_bytes", "rabit_svid_init",
 ]
 
 
@@ -109,6 +109,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "rabit_transpose_planes": (ctypes.c_int, [lp, vp, vp]),
         "rabit_grad_input": (ctypes.c_int, [lp, vp, i32, vp, i32, vp, sz, vp]),
         "rabit_grad_weight": (ctypes.c_int, [lp, vp, vp, i32, vp, vp, vp, u32, vp, sz, vp]),
+        "rabit_svid_workspace_bytes": (sz, [i32, i32]),
+        "rabit_svid_init": (ctypes.c_int, [vp, i32, i32, i32, i32, i32, vp, vp, u32, vp, vp, vp, vp,
+                                           sz, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -349,6 +352,40 @@ def grad_weight(layer: PackedLayer, x: torch.Tensor, dy: torch.Tensor, dw=None, 
                                  _ptr(workspace), workspace.numel(), _stream(stream)),
            "rabit_grad_weight")
     return dw, dg, dh
+
+
+# --- initialisation (rabit_svid_init in rabit.h) ---
+RABIT_SVID_CONTINUE = 1
+
+
+def svid_workspace(out: int, inp: int, device="cuda") -> torch.Tensor:
+    return _ws(load().rabit_svid_workspace_bytes(out, inp), device)
+
+
+def svid_init(w: torch.Tensor, n_paths: int = 2, sweeps: int = 20, power_passes: int = 5,
+              f_out: torch.Tensor | None = None, f_in: torch.Tensor | None = None,
+              g: torch.Tensor | None = None, h: torch.Tensor | None = None,
+              planes: torch.Tensor | None = None, cont: bool = False,
+              workspace: torch.Tensor | None = None, stream=None):
+    """Iterative residual SVID of w (float32 [out, in], cuda): returns
+    (g [P][out], h [P][in] float32, planes uint8 in layout V1)."""
+    lib = load()
+    assert w.dtype == torch.float32 and w.is_contiguous()
+    out, inp = w.shape
+    dev = w.device
+    if g is None:
+        g = torch.zeros(n_paths, out, dtype=torch.float32, device=dev)
+    if h is None:
+        h = torch.zeros(n_paths, inp, dtype=torch.float32, device=dev)
+    if planes is None:
+        planes = torch.zeros(planes_bytes(out, inp, n_paths), dtype=torch.uint8, device=dev)
+    if workspace is None:
+        workspace = svid_workspace(out, inp, dev)
+    _check(lib.rabit_svid_init(_ptr(w), out, inp, n_paths, sweeps, power_passes, _ptr(f_out),
+                               _ptr(f_in), RABIT_SVID_CONTINUE if cont else 0, _ptr(g), _ptr(h),
+                               _ptr(planes), _ptr(workspace), workspace.numel(), _stream(stream)),
+           "rabit_svid_init")
+    return g, h, planes
 
 
 MATRICES = ("q", "k", "v", "o", "gate", "up", "down")

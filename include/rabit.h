@@ -277,6 +277,51 @@ int rabit_grad_weight(const rabit_layer *layer, const uint16_t *X, const uint16_
                       void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Initial scales of a layer (paper §4.3 "Iterative Residual SVID" eq. and
+ * "I/O Channel Importance-Scaled Preconditioning" eqs.; App. F.1/F.3: 20
+ * sweeps). Sweep t re-fits path i = 1..n_paths in order to
+ * R_i = W' − Σ_{j≠i} g_j ⊙ B_j ⊙ h_j (paths before i from this sweep, after i
+ * from the previous one; all zero before the first sweep, so sweep 1 is the
+ * greedy fit) with SVID(R_i): B_i = sign(R_i) and g_i h_iᵀ the leading
+ * rank-1 term of |R_i| (SVID is not defined on the pages; this is the plain
+ * reading, the exact minimiser of ||R_i − g_i ⊙ B_i ⊙ h_i|| over signs and
+ * non-negative rank-1 scales). W' = f_out ⊙ W ⊙ f_in (f = s^a, the channel
+ * importance factors; NULL = 1), and the scales are mapped back:
+ * g_i = g_i' / f_out, h_i = h_i' / f_in.
+ *
+ * The rank-1 term is computed by power iteration on |R_i|, warm-started
+ * from h_i: power_passes (odd, 1..63; 5 reach the exact SVID to about 1e-9
+ * on the synthetic layers, 3 leave about 1e-2 after 20 sweeps) reads of W
+ * per re-fit, alternating
+ * rows (u = |R_i| v) and columns (v = |R_i|ᵀ u), starting and ending with
+ * rows; then with σ = ||u|| / ||v||, g_i = u / (sqrt(σ) ||v||) and
+ * h_i = sqrt(σ) v / ||v||. R is formed in float32: fl(fl(f_out W) f_in), then
+ * each other path's fl(g_j h_j) subtracted in path order.
+ *
+ * W       device float32 [out][in].
+ * f_out   device float32 [out] or NULL;  f_in  device float32 [in] or NULL
+ *         (positive).
+ * flags   0, or RABIT_SVID_CONTINUE: g, h and planes hold a previous result
+ *         (original domain) that stands for the paths before the first sweep.
+ * g, h    device float32 [n_paths][out], [n_paths][in]: the scales (written;
+ *         read first with RABIT_SVID_CONTINUE).
+ * planes  device, rabit_planes_bytes(out, in, n_paths) bytes, layout V1: the
+ *         bits of each B_i of the last sweep.
+ * The scales are float32, as learnable parameters; a packed layer takes them
+ * rounded to fp16 (rabit_pack with RABIT_SCALES_GIVEN re-derives the cores).
+ * Errors: RABIT_EINVAL (null, flags, aliasing), RABIT_ESHAPE (sizes, sweeps
+ * < 1 or > 1000, power_passes even or out of range), RABIT_EALIGN,
+ * RABIT_EUNSUPPORTED (n_paths), RABIT_EWORKSPACE, RABIT_EDEVICE.
+ */
+#define RABIT_SVID_CONTINUE 1u
+
+size_t rabit_svid_workspace_bytes(int32_t out_features, int32_t in_features);
+int rabit_svid_init(const float *W, int32_t out_features, int32_t in_features, int32_t n_paths,
+                    int32_t sweeps, int32_t power_passes, const float *f_out, const float *f_in,
+                    uint32_t flags, float *g, float *h, void *planes, void *workspace,
+                    size_t workspace_bytes, void *stream);
+
+/*
  * Decoder configuration for rabit_decode_step (a Llama-style block; the pages
  * time Llama2 decoding, Table 7, without defining the block).
  */

@@ -42,7 +42,7 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["svid", "residual_svid", "svid_objective"]
+__all__ = ["svid", "svid_leading", "residual_svid", "svid_objective"]
 
 
 def svid(r: np.ndarray):
@@ -54,6 +54,21 @@ def svid(r: np.ndarray):
     u, sig, vt = np.linalg.svd(a, full_matrices=False)
     u0, v0 = u[:, 0], vt[0]
     if u0.sum() < 0:               # the sign of a singular pair is arbitrary
+        u0, v0 = -u0, -v0
+    root = np.sqrt(sig[0])
+    return s, root * np.maximum(u0, 0.0), root * np.maximum(v0, 0.0)
+
+
+def svid_leading(r: np.ndarray):
+    """The same (s, g, h) as ``svid`` for large matrices: the leading singular
+    triple from scipy's sparse SVD (ARPACK, k = 1) instead of the full SVD (a
+    library step; pinned against ``svid`` on small matrices)."""
+    from scipy.sparse.linalg import svds
+    r = np.asarray(r, dtype=np.float64)
+    s = r < 0
+    u, sig, vt = svds(np.abs(r), k=1, tol=1e-12)
+    u0, v0 = u[:, 0], vt[0]
+    if u0.sum() < 0:
         u0, v0 = -u0, -v0
     root = np.sqrt(sig[0])
     return s, root * np.maximum(u0, 0.0), root * np.maximum(v0, 0.0)

@@ -212,3 +212,30 @@ def test_training_sizes_and_errors(lib):
     assert lib.rabit_transpose_planes(ctypes.byref(L), dW + 8, None) == rabit.RABIT_EALIGN
     assert lib.rabit_transpose_planes(ctypes.byref(fake_layer(version=0)), dW, None) == \
         rabit.RABIT_EINVAL
+
+
+def test_svid_errors(lib):
+    assert lib.rabit_svid_workspace_bytes(4096, 11008) > 0
+    assert lib.rabit_svid_workspace_bytes(0, 8) == 0
+    W, g, h, pl, ws = (FAKE + (k << 32) for k in range(10, 15))
+    big = 1 << 40
+
+    def sv(w=W, out=256, inp=512, P=2, sweeps=20, passes=3, fo=None, fi=None, flags=0, G=g, H=h,
+           planes=pl, wsp=ws, wsb=big):
+        return lib.rabit_svid_init(w, out, inp, P, sweeps, passes, fo, fi, flags, G, H, planes, wsp,
+                                   wsb, None)
+    assert sv(P=4) == rabit.RABIT_EUNSUPPORTED
+    assert sv(P=1) == rabit.RABIT_EUNSUPPORTED
+    assert sv(out=0) == rabit.RABIT_ESHAPE
+    assert sv(sweeps=0) == rabit.RABIT_ESHAPE
+    assert sv(passes=2) == rabit.RABIT_ESHAPE
+    assert sv(passes=65) == rabit.RABIT_ESHAPE
+    assert sv(w=0) == rabit.RABIT_EINVAL
+    assert sv(planes=0) == rabit.RABIT_EINVAL
+    assert sv(flags=2) == rabit.RABIT_EINVAL
+    assert sv(G=W) == rabit.RABIT_EINVAL                 # g aliases W
+    assert sv(H=g + 512) == rabit.RABIT_EINVAL           # h inside g
+    assert sv(fo=g) == rabit.RABIT_EINVAL                # f_out aliases g
+    assert sv(fi=FAKE + (20 << 32) + 4) == rabit.RABIT_EALIGN
+    assert sv(wsb=16) == rabit.RABIT_EWORKSPACE
+    assert sv(P=3, wsb=16) == rabit.RABIT_EWORKSPACE

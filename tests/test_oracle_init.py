@@ -6,7 +6,7 @@ import math
 import numpy as np
 import pytest
 
-from oracle import svid, residual_svid, svid_objective
+from oracle import svid, svid_leading, residual_svid, svid_objective
 from synth.inputs import weight_f32
 
 
@@ -96,3 +96,12 @@ def test_preconditioning_maps_back():
     wh = sum(_what(*p) for p in pre)
     assert np.linalg.norm(fo[:, None] * (w - wh) * fi[None, :]) == pytest.approx(
         svid_objective(fo[:, None] * w * fi[None, :], direct), rel=1e-9)
+
+
+def test_leading_triple_matches_full_svd():
+    w = weight_f32(120, 200, 41).numpy().astype(np.float64)
+    s, g, h = svid(w)
+    s2, g2, h2 = svid_leading(w)
+    assert np.array_equal(s, s2)
+    np.testing.assert_allclose(g2, g, rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(h2, h, rtol=1e-9, atol=1e-12)
