@@ -13,7 +13,8 @@
 //
 // Arithmetic: R in float32 (W' = fl(fl(f_out W) f_in), then each other path's
 // fl(g_j h_j) subtracted in path order), pass sums in float32 inside a tile,
-// tiles added in float64 in ascending order, vectors stored in float32.
+// tiles added in float64 (four interleaved slices in ascending order, then
+// the slices in order), vectors stored in float32.
 #include <algorithm>
 #include <math.h>
 
@@ -35,8 +36,8 @@ struct SvidWs {
   float* u;         // [out]
   float* v;         // [in]
   float* part;      // pass partials: rows pass [ceil(in/256)][out], columns pass [ceil(out/64)][in]
-  double* sq_u;     // [ceil(out/256)] partial Σ u²
-  double* sq_v;     // [ceil(in/256)] partial Σ v²
+  double* sq_u;     // [ceil(out/64)] partial Σ u²
+  double* sq_v;     // [ceil(in/64)] partial Σ v²
 };
 
 __host__ inline size_t part_elems(int out, int in) {
@@ -51,7 +52,7 @@ __host__ inline SvidWs carve_svid(void* ws, int out, int in, int P) {
   w.u = (float*)p;   p += a256((size_t)out * 4);
   w.v = (float*)p;   p += a256((size_t)in * 4);
   w.part = (float*)p; p += a256(part_elems(out, in) * 4);
-  w.sq_u = (double*)p; p += a256((size_t)((out + kRedWg - 1) / kRedWg) * 8);
+  w.sq_u = (double*)p; p += a256((size_t)((out + 63) / 64) * 8);
   w.sq_v = (double*)p;
   return w;
 }
@@ -59,7 +60,7 @@ __host__ inline SvidWs carve_svid(void* ws, int out, int in, int P) {
 __host__ inline size_t svid_ws_bytes(int out, int in, int P) {
   return a256((size_t)P * out * 4) + a256((size_t)P * in * 4) + a256((size_t)out * 4) +
          a256((size_t)in * 4) + a256(part_elems(out, in) * 4) +
-         a256((size_t)((out + kRedWg - 1) / kRedWg) * 8) + a256((size_t)((in + kRedWg - 1) / kRedWg) * 8);
+         a256((size_t)((out + 63) / 64) * 8) + a256((size_t)((in + 63) / 64) * 8);
 }
 
 // One pass over a 64 x 256 tile. Thread (c4 = tid % 64, q = tid / 64) holds
@@ -97,6 +98,7 @@ __global__ __launch_bounds__(256) void k_svid_pass(const float* __restrict__ W,
     for (int c = 0; c < 4; ++c) hj[j][c] = (j < P && j != path) ? ws.hp[(size_t)j * in + min(ic + c, in - 1)] : 0.f;
 
   float colacc[4] = {0.f, 0.f, 0.f, 0.f};
+  float rv[16];                    // ROWS: this thread's share of each row
   __shared__ float s_row[kR];      // ROWS: per row of the tile
   __shared__ float s_col[4][kC];   // COLS: per wave, per column
 
@@ -139,10 +141,7 @@ __global__ __launch_bounds__(256) void k_svid_pass(const float* __restrict__ W,
       nib |= (ok && r[c] < 0.f) ? (1u << c) : 0u;
     }
     if (ROWS) {
-      float s = a[0] * vin[0] + a[1] * vin[1] + a[2] * vin[2] + a[3] * vin[3];
-#pragma unroll
-      for (int k = 32; k >= 1; k >>= 1) s += __shfl_xor(s, k, 64);
-      if (c4 == 0) s_row[16 * q + rr] = s;
+      rv[rr] = ((a[0] * vin[0] + a[1] * vin[1]) + a[2] * vin[2]) + a[3] * vin[3];
     } else {
       const float uo = orow ? vecin[o] : 0.f;
 #pragma unroll
@@ -159,6 +158,32 @@ __global__ __launch_bounds__(256) void k_svid_pass(const float* __restrict__ W,
     }
   }
   if (ROWS) {
+    // sum each of the 16 rows over the 64 lanes: a butterfly that halves the
+    // number of rows a lane holds at each of the xor 32, 16, 8, 4 steps, then
+    // xor 2 and 1; lane l ends with row 8 b5 + 4 b4 + 2 b3 + b2 (bits of l)
+    const int l = c4;
+    float t8[8], t4[4], t2[2];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const bool hi = l & 32;
+      t8[k] = (hi ? rv[8 + k] : rv[k]) + __shfl_xor(hi ? rv[k] : rv[8 + k], 32, 64);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const bool hi = l & 16;
+      t4[k] = (hi ? t8[4 + k] : t8[k]) + __shfl_xor(hi ? t8[k] : t8[4 + k], 16, 64);
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const bool hi = l & 8;
+      t2[k] = (hi ? t4[2 + k] : t4[k]) + __shfl_xor(hi ? t4[k] : t4[2 + k], 8, 64);
+    }
+    const bool hi = l & 4;
+    float t1 = (hi ? t2[1] : t2[0]) + __shfl_xor(hi ? t2[0] : t2[1], 4, 64);
+    t1 += __shfl_xor(t1, 2, 64);
+    t1 += __shfl_xor(t1, 1, 64);
+    const int row = 8 * ((l >> 5) & 1) + 4 * ((l >> 4) & 1) + 2 * ((l >> 3) & 1) + ((l >> 2) & 1);
+    if ((l & 3) == 0) s_row[16 * q + row] = t1;
     __syncthreads();
     if (tid < kR) {
       const int o = o0 + tid;
@@ -173,28 +198,42 @@ __global__ __launch_bounds__(256) void k_svid_pass(const float* __restrict__ W,
   }
 }
 
-// vec[e] = Σ_t part[t][e] (ascending t, float64), and Σ vec² per workgroup
-__global__ __launch_bounds__(kRedWg) void k_svid_reduce(const float* __restrict__ part, int nt, int n,
-                                                        float* vec, double* sq) {
-  const int e = blockIdx.x * kRedWg + threadIdx.x;
-  double v = 0.0;
-  if (e < n) {
-    for (int t = 0; t < nt; ++t) v += (double)part[(size_t)t * n + e];
-    vec[e] = (float)v;
-  }
-  const double f = e < n ? (double)(float)v : 0.0;
-  double s = f * f;
+// vec[e] = Σ_t part[t][e] in float64: slice k (of 4) adds the partials
+// t ≡ k (mod 4) in ascending t, eight loads in flight, and the four slice sums
+// are added in slice order; Σ vec² per workgroup of 64 elements
+__global__ __launch_bounds__(256) void k_svid_reduce(const float* __restrict__ part, int nt, int n,
+                                                     float* vec, double* sq) {
+  const int k = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int e = blockIdx.x * 64 + l;
+  const int ec = min(e, n - 1);
+  double acc = 0.0;
+  for (int t0 = k; t0 < nt; t0 += 32) {
+    float x[8];
 #pragma unroll
-  for (int k = 32; k >= 1; k >>= 1) s += __shfl_xor(s, k, 64);
-  __shared__ double sw[kRedWg / 64];
-  if ((threadIdx.x & 63) == 0) sw[threadIdx.x >> 6] = s;
+    for (int u = 0; u < 8; ++u) {
+      const int t = t0 + 4 * u;
+      x[u] = part[(size_t)min(t, nt - 1) * n + ec];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc += t0 + 4 * u < nt ? (double)x[u] : 0.0;
+  }
+  __shared__ double sl[4][64];
+  sl[k][l] = acc;
   __syncthreads();
-  if (threadIdx.x == 0) sq[blockIdx.x] = ((sw[0] + sw[1]) + sw[2]) + sw[3];
+  if (k == 0) {
+    const double v = ((sl[0][l] + sl[1][l]) + sl[2][l]) + sl[3][l];
+    const float f = (float)v;
+    if (e < n) vec[e] = f;
+    double s2 = e < n ? (double)f * f : 0.0;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) s2 += __shfl_xor(s2, m, 64);
+    if (l == 0) sq[blockIdx.x] = s2;
+  }
 }
 
-// v = the path's h (warm start) or ones (cold start), and its Σ v²
-__global__ __launch_bounds__(kRedWg) void k_svid_start(SvidWs ws, int in, int path, int cold) {
-  const int e = blockIdx.x * kRedWg + threadIdx.x;
+// v = the path's h (warm start) or ones (cold start), and Σ v² per 64 elements
+__global__ __launch_bounds__(64) void k_svid_start(SvidWs ws, int in, int path, int cold) {
+  const int e = blockIdx.x * 64 + threadIdx.x;
   float x = 0.f;
   if (e < in) {
     x = cold ? 1.0f : ws.hp[(size_t)path * in + e];
@@ -202,25 +241,32 @@ __global__ __launch_bounds__(kRedWg) void k_svid_start(SvidWs ws, int in, int pa
   }
   double s = (double)x * x;
 #pragma unroll
-  for (int k = 32; k >= 1; k >>= 1) s += __shfl_xor(s, k, 64);
-  __shared__ double sw[kRedWg / 64];
-  if ((threadIdx.x & 63) == 0) sw[threadIdx.x >> 6] = s;
-  __syncthreads();
-  if (threadIdx.x == 0) ws.sq_v[blockIdx.x] = ((sw[0] + sw[1]) + sw[2]) + sw[3];
+  for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m, 64);
+  if (threadIdx.x == 0) ws.sq_v[blockIdx.x] = s;
 }
 
 // g_path = u / (sqrt(σ) ||v||), h_path = sqrt(σ) v / ||v||, σ = ||u|| / ||v||
 __global__ __launch_bounds__(kRedWg) void k_svid_extract(SvidWs ws, int out, int in, int path) {
-  __shared__ double s_nu, s_nv;
-  if (threadIdx.x == 0) {
-    double a = 0.0, b = 0.0;
-    for (int k = 0; k < (out + kRedWg - 1) / kRedWg; ++k) a += ws.sq_u[k];
-    for (int k = 0; k < (in + kRedWg - 1) / kRedWg; ++k) b += ws.sq_v[k];
-    s_nu = sqrt(a);
-    s_nv = sqrt(b);
+  // ||u||², ||v||²: thread t adds entries t, t + 256, ... of the per-64
+  // partial arrays, then a fixed tree over the workgroup (the same bits in
+  // every workgroup)
+  const int nsu = (out + 63) / 64, nsv = (in + 63) / 64;
+  double a = 0.0, b = 0.0;
+  for (int k = threadIdx.x; k < nsu; k += kRedWg) a += ws.sq_u[k];
+  for (int k = threadIdx.x; k < nsv; k += kRedWg) b += ws.sq_v[k];
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    a += __shfl_xor(a, m, 64);
+    b += __shfl_xor(b, m, 64);
+  }
+  __shared__ double s_a[kRedWg / 64], s_b[kRedWg / 64];
+  if ((threadIdx.x & 63) == 0) {
+    s_a[threadIdx.x >> 6] = a;
+    s_b[threadIdx.x >> 6] = b;
   }
   __syncthreads();
-  const double nu = s_nu, nv = s_nv;
+  const double nu = sqrt(((s_a[0] + s_a[1]) + s_a[2]) + s_a[3]);
+  const double nv = sqrt(((s_b[0] + s_b[1]) + s_b[2]) + s_b[3]);
   const bool ok = nu > 0.0 && nv > 0.0;
   const double sig = ok ? nu / nv : 0.0, rs = sqrt(sig);
   const int e = blockIdx.x * kRedWg + threadIdx.x;
@@ -285,20 +331,20 @@ hipError_t launch_svid(const float* W, int out, int in, int P, int sweeps, int p
   }
   const int nct = (in + kC - 1) / kC, nrt = (out + kR - 1) / kR;
   const dim3 tiles(nct * nrt), blk(256);
-  const dim3 gu((out + kRedWg - 1) / kRedWg), gv((in + kRedWg - 1) / kRedWg);
+  const dim3 gu((out + 63) / 64), gv((in + 63) / 64);
   const dim3 ge((std::max(out, in) + kRedWg - 1) / kRedWg);
   for (int t = 0; t < sweeps; ++t) {
     for (int i = 0; i < P; ++i) {
-      hipLaunchKernelGGL(k_svid_start, gv, dim3(kRedWg), 0, st, w, in, i, (!cont && t == 0) ? 1 : 0);
+      hipLaunchKernelGGL(k_svid_start, gv, dim3(64), 0, st, w, in, i, (!cont && t == 0) ? 1 : 0);
       for (int k = 0; k < passes; ++k) {
         if ((k & 1) == 0) {  // rows pass: u = |R| v (the first also writes the bits of B_i)
           hipLaunchKernelGGL(k_svid_pass<true>, tiles, blk, 0, st, W, f_out, f_in, out, in, P, i,
                              (uint32_t*)planes, w, k == 0 ? 1 : 0);
-          hipLaunchKernelGGL(k_svid_reduce, gu, dim3(kRedWg), 0, st, w.part, nct, out, w.u, w.sq_u);
+          hipLaunchKernelGGL(k_svid_reduce, gu, dim3(256), 0, st, w.part, nct, out, w.u, w.sq_u);
         } else {             // columns pass: v = |R|ᵀ u
           hipLaunchKernelGGL(k_svid_pass<false>, tiles, blk, 0, st, W, f_out, f_in, out, in, P, i,
                              (uint32_t*)planes, w, 0);
-          hipLaunchKernelGGL(k_svid_reduce, gv, dim3(kRedWg), 0, st, w.part, nrt, in, w.v, w.sq_v);
+          hipLaunchKernelGGL(k_svid_reduce, gv, dim3(256), 0, st, w.part, nrt, in, w.v, w.sq_v);
         }
       }
       hipLaunchKernelGGL(k_svid_extract, ge, dim3(kRedWg), 0, st, w, out, in, i);
