@@ -632,10 +632,29 @@ def bench_gemm(args, rabit, torch):
                                      "mfma_frac_fp16": round(tf / 2500.0, 4)}
             log(f"gemm 3-bit {N}x{K} M={M}: {ms:.3f} ms {tf:.1f} TFLOP/s")
             del X, ws, Y
+    # the effective-weight variant (fp16 W_hat per tile): dense-equivalent 2 M N K
+    resw = {}
+    for (N, K) in ((14336, 4096), (4096, 14336)):
+        for P in (2, 3):
+            pl = rabit.PackedLayer.empty(N, K, n_paths=P)
+            w = weight_f32(N, K, seed_w(4, P, "gate" if N > K else "down"), device="cuda")
+            rabit.pack(w, pl, workspace=wsh[0])
+            del w
+            for M in (2048, 8192):
+                X = act_bf16(M, K, seed_x(4, M)).cuda()
+                ws = rabit.gemm_workspace(pl, M)
+                Y = torch.empty(M, N, device="cuda")
+                rabit.gemm(pl, X, y=Y, workspace=ws, weff=True)
+                ms = _events_ms(torch, lambda i: rabit.gemm(pl, X, y=Y, workspace=ws, weff=True), 10)
+                tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+                resw[f"{N}x{K}_P{P}_M{M}"] = {"ms": round(ms, 4), "tflops_dense_equiv": round(tf, 1)}
+                log(f"gemm weff P={P} {N}x{K} M={M}: {ms:.3f} ms {tf:.1f} dense-equivalent TFLOP/s")
+                del X, ws, Y
     best = max(v["tflops"] for v in res.values())
     return _line("Residual-binary prefill GEMM TFLOP/s (4 M N K, fp16 MFMA)", best, "TFLOP/s",
                  {"workload": "llama3-8b-mlp-gemm", "M": [512, 2048, 8192]}, dtype="fp16",
-                 runs=res, runs_3bit=res3, roofline={"bound": "mfma", "peak": 2500.0, "unit": "TFLOP/s",
+                 runs=res, runs_3bit=res3, runs_weff=resw,
+                 roofline={"bound": "mfma", "peak": 2500.0, "unit": "TFLOP/s",
                                      "achieved": best, "frac": round(best / 2500.0, 4)})
 
 
@@ -672,10 +691,14 @@ def bench_train(args, rabit, torch):
             fwd = lambda i: rabit.gemm(pl, X, rabit.RABIT_OUT_BF16, y=Y, workspace=wsf)
             gx = lambda i: rabit.grad_input(pl, dY, rabit.RABIT_OUT_BF16, dx=dX, workspace=wsx)
             gw = lambda i: rabit.grad_weight(pl, X, dY, dw=dW, dg=dg, dh=dh, workspace=wsw)
-            for f in (derive, fwd, gx, gw):
+            fwdw = lambda i: rabit.gemm(pl, X, rabit.RABIT_OUT_BF16, y=Y, workspace=wsf, weff=True)
+            gxw = lambda i: rabit.grad_input(pl, dY, rabit.RABIT_OUT_BF16, dx=dX, workspace=wsx,
+                                             weff=True)
+            for f in (derive, fwd, gx, gw, fwdw, gxw):
                 f(0)
             t = {k: _events_ms(torch, f, 5) for k, f in
                  (("derive", derive), ("forward", fwd), ("grad_input", gx), ("grad_weight", gw))}
+            tw = {k: _events_ms(torch, f, 5) for k, f in (("forward", fwdw), ("grad_input", gxw))}
             dense = {
                 "forward": _events_ms(torch, lambda i: torch.mm(X, wd.t()), 5),
                 "grad_input": _events_ms(torch, lambda i: torch.mm(dY, wd), 5),
@@ -683,6 +706,7 @@ def bench_train(args, rabit, torch):
             }
             flop = 2.0 * M * N * K
             ours = sum(t.values())
+            ours_w = t["derive"] + tw["forward"] + tw["grad_input"] + t["grad_weight"]
             dn = sum(dense.values())
             tf_gw = flop / (t["grad_weight"] * 1e-3) / 1e12
             if tf_gw > best_gw and M == 8192:
@@ -695,10 +719,13 @@ def bench_train(args, rabit, torch):
                 "dense_bf16_ms_step": round(dn, 4),
                 "grad_weight_tflops": round(tf_gw, 1),
                 "step_tflops_dense_equiv": round(3 * flop / (ours * 1e-3) / 1e12, 1),
-                "speedup_vs_dense": round(dn / ours, 3)}
+                "speedup_vs_dense": round(dn / ours, 3),
+                "weff_ms": {k: round(v, 4) for k, v in tw.items()}, "weff_ms_step": round(ours_w, 4),
+                "weff_speedup_vs_dense": round(dn / ours_w, 3)}
             log(f"train {N}x{K} M={M}: derive {t['derive']:.3f} fwd {t['forward']:.3f} "
                 f"dX {t['grad_input']:.3f} dW {t['grad_weight']:.3f} ms (dW {tf_gw:.0f} TFLOP/s); "
-                f"step {ours:.3f} ms vs dense bf16 {dn:.3f} ms")
+                f"step {ours:.3f} ms vs dense bf16 {dn:.3f} ms; fp16 W_hat tiles: fwd {tw['forward']:.3f} "
+                f"dX {tw['grad_input']:.3f} step {ours_w:.3f} ms")
             del X, dY, Y, dX, dW, wsf, wsx, wsw
         del w, wd, pl
     gate = res["11008x4096_M8192"]

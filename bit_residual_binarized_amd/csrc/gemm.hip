@@ -22,6 +22,7 @@ namespace rabit {
 namespace {
 
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kBN = 128, kBK = 64;
@@ -41,9 +42,9 @@ __host__ inline size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // split of K over grid.z: enough workgroups to fill the chip, at least four
 // 64-column steps per slice
-__host__ inline int split_k(int out, int in, int m, int P) {
+__host__ inline int split_k(int out, int in, int m, int bm, int bn = kBN) {
   const int Kp = col_groups(in) * 128;
-  const int tiles = ((out + kBN - 1) / kBN) * ((m + bm_of(P) - 1) / bm_of(P));
+  const int tiles = ((out + bn - 1) / bn) * ((m + bm - 1) / bm);
   int z = std::max(1, (512 + tiles - 1) / tiles);
   z = std::min(z, std::max(1, Kp / (4 * kBK)));
   return std::min(z, 16);
@@ -65,7 +66,8 @@ __host__ inline GemmWs carve(void* ws, int out, int in, int m, int P) {
 
 __host__ inline size_t ws_bytes_p(int out, int in, int m, int P) {
   const size_t Kp = (size_t)col_groups(in) * 128;
-  const int z = split_k(out, in, m, P);
+  // the exact path's tiles (bm_of(P) rows) or the effective-weight path's (128)
+  const int z = std::max(split_k(out, in, m, bm_of(P)), split_k(out, in, m, 128, 2 * kBN));
   return a256((size_t)m * Kp * 2) + a256((size_t)m * 4) + a256((size_t)P * (Kp / 32) * 16 * 4) +
          (z > 1 ? a256((size_t)z * m * out * 4) : 0);
 }
@@ -78,6 +80,7 @@ __host__ inline size_t ws_bytes(int out, int in, int m) {
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
   return __builtin_bit_cast(uint16_t, (_Float16)f);
 }
+__device__ __forceinline__ uint32_t f16_to_bits(float f) { return f32_to_f16_bits(f); }
 
 // One workgroup per row of X: row maximum, exponent, scaled fp16 copy.
 __global__ __launch_bounds__(256) void k_gemm_prep_x(const uint16_t* __restrict__ X, int in, int Kp,
@@ -127,14 +130,25 @@ __global__ void k_gemm_prep_h(const uint16_t* __restrict__ h, int in, int Kp, in
 // of the 32-column block. X goes through a double-buffered LDS tile (one
 // barrier per step). The next step's X rows, plane words and h pairs are
 // loaded into registers while the current step runs on the matrix cores.
-template <int P>
+//
+// WEFF: the effective weight of the tile, Σ_p g_p[n] (±h_p[k]), is formed in
+// fp16 before the matrix op instead of one matrix op per path: with
+// f[n] = max_p g_p[n] and r_p = g_p / f (fp16, in [0, 1]), the B fragment is
+// e = Σ_p r_p (±h_p) by packed fp16 multiply-adds (path order) and f[n] is
+// applied in the epilogue. One accumulator set; 128 x 256 tiles for any P,
+// each wave 64 output columns.
+template <int P, bool WEFF>
 __global__ __launch_bounds__(256, 2) void k_gemm(const uint4* __restrict__ planes,
                                               const uint16_t* __restrict__ g, int out, int M,
                                               int Kp, int ksteps, GemmWs ws, void* Y, int y_dtype) {
-  constexpr int kBM = bm_of(P), MT = kBM / 16;  // 16-row matrix tiles per wave
-  const int n0 = blockIdx.x * kBN, m0 = blockIdx.y * kBM;
+  constexpr int kBM = WEFF ? 128 : bm_of(P), MT = kBM / 16;  // 16-row matrix tiles per wave
+  constexpr int NA = WEFF ? 1 : P;                             // accumulator sets
+  // 16-column fragments per wave: 2 (exact path), 4 (WEFF: one fragment
+  // build feeds four matrix ops per X fragment read, as in the exact path)
+  constexpr int NJ = WEFF ? 4 : 2;
+  const int n0 = blockIdx.x * (64 * NJ), m0 = blockIdx.y * kBM;
   const int tid = threadIdx.x, l = tid & 63;
-  const int wn = __builtin_amdgcn_readfirstlane(tid >> 6) * 32;
+  const int wn = __builtin_amdgcn_readfirstlane(tid >> 6) * (16 * NJ);
   const int KG = Kp / 128;
   const int nb = Kp / 32;
   const int out_pad = row_groups(out) * 64;
@@ -146,45 +160,88 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint4* __restrict__ plane
   __shared__ __align__(16) uint32_t sA[2][kBM * kLdsStride];
   __shared__ __align__(16) uint32_t sH[2][P][2][16];  // [buffer][p][sub]: the step's h pairs
 
-  v4f acc[P][MT][2];
+  v4f acc[NA][MT][NJ];
 #pragma unroll
-  for (int p = 0; p < P; ++p)
+  for (int p = 0; p < NA; ++p)
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) acc[p][i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < NJ; ++j) acc[p][i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
 
   // A loader: thread -> row m0 + (tid >> 1), half (tid & 1) of the 64 columns
   const int am = m0 + (tid >> 1), ah = tid & 1;
   const bool aload = (tid >> 1) < kBM;  // all threads with 128 rows, half with 64
   const bool avalid = aload && am < M;
   const uint4* asrc = (const uint4*)(ws.xh + (size_t)min(am, M - 1) * Kp) + ah * 4;
-  // B: the words of rows n0 + wn + 16 j + fr (clamped into the padded rows)
-  const uint32_t* wsrc[P][2];
+  // B: the words of rows n0 + wn + 16 j + fr. These rows lie in one 64-row
+  // group (n0 + wn is a multiple of 16 NJ), so one base pointer per path
+  // serves every j (row 16 j is 16 j units further); a group past the last
+  // is clamped to it (those columns are not stored).
+  const uint32_t* wsrc[P];
+  {
+    const int base = n0 + wn;
+    const int rg = min(base >> 6, out_pad / 64 - 1);
 #pragma unroll
-  for (int p = 0; p < P; ++p)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int bn = min(n0 + wn + 16 * j + fr, out_pad - 1);
-      wsrc[p][j] = (const uint32_t*)(planes + unit_index(bn >> 6, 0, p, bn & 63, KG, P));
-    }
+    for (int p = 0; p < P; ++p)
+      wsrc[p] = (const uint32_t*)(planes + unit_index(rg, 0, p, (base & 63) + fr, KG, P));
+  }
   // h pairs of the step, staged through LDS by threads 0 .. 32 P - 1: (p, sub, pair)
   const bool hload = tid < 32 * P;
   const int hp = hload ? tid >> 5 : 0, hs = (tid >> 4) & 1, hq = tid & 15;
   const uint32_t* hsrc = ws.hpairs + (size_t)hp * nb * 16 + hs * 16 + hq;
 
+  // WEFF: per fragment column n (j = 0, 1), f = max_p g_p[n] and the fp16
+  // ratios r_p = g_p / f, duplicated into both halves of a dword
+  uint32_t rpair[P][NJ];
+  if (WEFF) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int n = min(n0 + wn + 16 * j + fr, out - 1);
+      float gv[P], f = 0.f;
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        gv[p] = f16_bits_to_f32(g[(size_t)p * out + n]);
+        f = fmaxf(f, gv[p]);
+      }
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        const uint32_t rb = f16_to_bits(f > 0.f ? gv[p] / f : 0.f);
+        rpair[p][j] = rb | (rb << 16);
+      }
+    }
+  }
+
+  // WEFF: the step's plane words of the workgroup's 256 rows go through LDS
+  // (thread t loads row n0 + t of every path), which keeps the registers of
+  // four fragments per wave free for the accumulators
+  constexpr int NW = WEFF ? 2 : 1;
+  __shared__ __align__(16) uint2 sW[NW][WEFF ? P : 1][WEFF ? 256 : 1];
+  const uint32_t* wrow[P];
+  if (WEFF) {
+    const int r = n0 + tid;
+    const int rg = min(r >> 6, out_pad / 64 - 1);
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+      wrow[p] = (const uint32_t*)(planes + unit_index(rg, 0, p, r & 63, KG, P));
+  }
+
   uint4 ra[4];
-  uint2 rw[P][2];   // [p][j]: words 2 ks, 2 ks + 1 of the row (the two 32-column blocks)
+  uint2 rw[P][WEFF ? 1 : NJ];  // [p][j]: words 2 ks, 2 ks + 1 of the row (the two 32-column blocks)
   uint32_t rh = 0;
   auto load = [&](int ks) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) ra[q] = asrc[(size_t)ks * 8 + q];
+    // column group ks / 2 is P x 64 units (4 dwords each) after group 0
+    const size_t wo = (size_t)(ks >> 1) * (P * 64 * 4) + 2 * (ks & 1);
 #pragma unroll
-    for (int p = 0; p < P; ++p)
+    for (int p = 0; p < P; ++p) {
+      if (WEFF) {
+        rw[p][0] = *(const uint2*)(wrow[p] + wo);
+      } else {
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        // column group ks / 2 is P x 64 units (4 dwords each) after group 0
-        rw[p][j] = *(const uint2*)(wsrc[p][j] + (size_t)(ks >> 1) * (P * 64 * 4) + 2 * (ks & 1));
+        for (int j = 0; j < NJ; ++j) rw[p][j] = *(const uint2*)(wsrc[p] + 64 * j + wo);
+      }
+    }
     if (hload) rh = hsrc[(size_t)ks * 32];
   };
   auto store_a = [&](int buf) {
@@ -194,6 +251,10 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint4* __restrict__ plane
       for (int q = 0; q < 4; ++q) *(uint4*)(da + 4 * q) = avalid ? ra[q] : make_uint4(0, 0, 0, 0);
     }
     if (hload) sH[buf][hp][hs][hq] = rh;
+    if (WEFF) {
+#pragma unroll
+      for (int p = 0; p < P; ++p) sW[buf & (NW - 1)][p][tid] = rw[p][0];
+    }
   };
   if (ks0 < ks1) {
     load(ks0);
@@ -208,11 +269,13 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint4* __restrict__ plane
   constexpr bool kFull = decltype(full_tag)::value;
   for (int ks = ks0; ks < ks1; ++ks) {
     const int buf = (ks - ks0) & 1;
-    uint2 cw[P][2];
+    uint2 cw[P][WEFF ? 1 : NJ];  // WEFF reads its words from LDS where it uses them
+    if (!WEFF) {
 #pragma unroll
-    for (int p = 0; p < P; ++p)
+      for (int p = 0; p < P; ++p)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) cw[p][j] = rw[p][j];
+        for (int j = 0; j < NJ; ++j) cw[p][WEFF ? 0 : j] = rw[p][WEFF ? 0 : j];
+    }
     if (ks + 1 < ks1) load(ks + 1);  // in flight during the matrix ops
 
     const uint32_t* a0 = sA[buf] + fr * kLdsStride + 4 * fg;
@@ -221,15 +284,41 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint4* __restrict__ plane
       v8h fa[MT];
 #pragma unroll
       for (int i = 0; i < MT; ++i) fa[i] = *(const v8h*)(a0 + 16 * i * kLdsStride + 16 * sub);
+      // dword c of a fragment holds columns (m, m + 16), m = 4 fg + c: the
+      // sign bits are bits m and m + 16 of the word, moved to bits 15 and 31
+      const int sh = 15 - 4 * fg;
+      if (WEFF) {
+        uint4 hh[P];
+#pragma unroll
+        for (int p = 0; p < P; ++p) hh[p] = *(const uint4*)(&sH[buf][p][sub][4 * fg]);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          uint32_t e[4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            h2v t;
+#pragma unroll
+            for (int p = 0; p < P; ++p) {
+              const uint32_t w = ((const uint32_t*)&sW[buf & (NW - 1)][p][wn + 16 * j + fr])[sub];
+              const h2v x = __builtin_bit_cast(h2v, (&hh[p].x)[c] ^ ((w << (sh - c)) & 0x80008000u));
+              const h2v r = __builtin_bit_cast(h2v, rpair[p][j]);
+              t = p == 0 ? r * x : __builtin_elementwise_fma(r, x, t);
+            }
+            e[c] = __builtin_bit_cast(uint32_t, t);
+          }
+          const v8h fb = __builtin_bit_cast(v8h, make_uint4(e[0], e[1], e[2], e[3]));
+#pragma unroll
+          for (int i = 0; i < MT; ++i)
+            if (kFull || i < mtiles)
+              acc[0][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[i], fb, acc[0][i][j], 0, 0, 0);
+        }
+      } else {
 #pragma unroll
       for (int p = 0; p < P; ++p) {
         const uint4 hh = *(const uint4*)(&sH[buf][p][sub][4 * fg]);
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const uint32_t w = sub ? cw[p][j].y : cw[p][j].x;
-          // dword c holds columns (m, m + 16), m = 4 fg + c: the sign bits are
-          // bits m and m + 16 of the word, moved to bits 15 and 31
-          const int sh = 15 - 4 * fg;
+          const uint32_t w = sub ? cw[p][WEFF ? 0 : j].y : cw[p][WEFF ? 0 : j].x;
           uint4 e;
           e.x = hh.x ^ ((w << sh) & 0x80008000u);
           e.y = hh.y ^ ((w << (sh - 1)) & 0x80008000u);
@@ -241,6 +330,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint4* __restrict__ plane
             if (kFull || i < mtiles)
               acc[p][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[i], fb, acc[p][i][j], 0, 0, 0);
         }
+      }
       }
     }
     if (ks + 1 < ks1) store_a(buf ^ 1);
@@ -255,19 +345,25 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint4* __restrict__ plane
   // epilogue: C[i][j] of a 16x16 tile: lane l, reg r -> row 4(l/16)+r, col l%16
   const bool split = gridDim.z > 1;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < NJ; ++j) {
     const int n = n0 + wn + 16 * j + (l & 15);
     if (n >= out) continue;
-    const float g0 = f16_bits_to_f32(g[n]), g1 = f16_bits_to_f32(g[out + n]);
-    const float g2 = P == 3 ? f16_bits_to_f32(g[2 * out + n]) : 0.f;
+    float g0 = f16_bits_to_f32(g[n]);
+    if (WEFF) {  // f[n] = max_p g_p[n], as in the prologue
+#pragma unroll
+      for (int p = 1; p < P; ++p) g0 = fmaxf(g0, f16_bits_to_f32(g[(size_t)p * out + n]));
+    }
+    const float g1 = (!WEFF) ? f16_bits_to_f32(g[out + n]) : 0.f;
+    const float g2 = (!WEFF && P == 3) ? f16_bits_to_f32(g[2 * out + n]) : 0.f;
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = m0 + 16 * i + 4 * (l >> 4) + r;
         if (m >= M) continue;
-        float v = g0 * acc[0][i][j][r] + g1 * acc[1][i][j][r];
-        if (P == 3) v += g2 * acc[P - 1][i][j][r];
+        float v = g0 * acc[0][i][j][r];
+        if (!WEFF) v += g1 * acc[NA > 1 ? 1 : 0][i][j][r];
+        if (!WEFF && P == 3) v += g2 * acc[NA - 1][i][j][r];
         if (split) {
           ws.part[((size_t)blockIdx.z * M + m) * out + n] = v;
         } else {
@@ -303,21 +399,21 @@ size_t gemm_workspace_bytes(int out, int in, int m) { return ws_bytes(out, in, m
 
 hipError_t launch_gemm(const uint4* planes, const uint16_t* g, const uint16_t* h, int out, int in,
                        const uint16_t* X, int m, void* Y, int y_dtype, void* ws, hipStream_t st,
-                       int paths) {
+                       int paths, bool weff) {
   if (paths != 2 && paths != 3) return hipErrorInvalidValue;
   const int Kp = col_groups(in) * 128;
   GemmWs w = carve(ws, out, in, m, paths);
   hipLaunchKernelGGL(k_gemm_prep_x, dim3(m), dim3(256), 0, st, X, in, Kp, w);
   const int nh = paths * (Kp / 32) * 16;
   hipLaunchKernelGGL(k_gemm_prep_h, dim3((nh + 255) / 256), dim3(256), 0, st, h, in, Kp, paths, w);
-  const int Z = split_k(out, in, m, paths);
+  const int bm = weff ? 128 : bm_of(paths), bn = weff ? 2 * kBN : kBN;
+  const int Z = split_k(out, in, m, bm, bn);
   const int steps = Kp / kBK;
   const int per = (steps + Z - 1) / Z;
-  const dim3 grid((out + kBN - 1) / kBN, (m + bm_of(paths) - 1) / bm_of(paths), Z);
-  if (paths == 3)
-    hipLaunchKernelGGL(k_gemm<3>, grid, dim3(256), 0, st, planes, g, out, m, Kp, per, w, Y, y_dtype);
-  else
-    hipLaunchKernelGGL(k_gemm<2>, grid, dim3(256), 0, st, planes, g, out, m, Kp, per, w, Y, y_dtype);
+  const dim3 grid((out + bn - 1) / bn, (m + bm - 1) / bm, Z);
+  auto kern = paths == 3 ? (weff ? k_gemm<3, true> : k_gemm<3, false>)
+                         : (weff ? k_gemm<2, true> : k_gemm<2, false>);
+  hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, planes, g, out, m, Kp, per, w, Y, y_dtype);
   if (Z > 1) {
     const size_t n = (size_t)m * out;
     hipLaunchKernelGGL(k_gemm_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, w, out,

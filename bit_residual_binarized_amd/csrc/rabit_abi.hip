@@ -214,6 +214,12 @@ int rabit_gemv_reduce(const rabit_layer* L, int32_t batch, void* y, int32_t y_dt
 
 int rabit_gemm(const rabit_layer* L, const uint16_t* X, int32_t m, void* Y, int32_t y_dtype,
                void* workspace, size_t workspace_bytes, void* stream) {
+  return rabit_gemm_ex(L, X, m, Y, y_dtype, 0u, workspace, workspace_bytes, stream);
+}
+
+int rabit_gemm_ex(const rabit_layer* L, const uint16_t* X, int32_t m, void* Y, int32_t y_dtype,
+                  uint32_t flags, void* workspace, size_t workspace_bytes, void* stream) {
+  if (flags & ~RABIT_GEMM_WEFF) return RABIT_EINVAL;
   int s = check_layer(L);
   if (s) return s;
   if (!X || !Y) return RABIT_EINVAL;
@@ -228,7 +234,8 @@ int rabit_gemm(const rabit_layer* L, const uint16_t* X, int32_t m, void* Y, int3
   if (!workspace || workspace_bytes < gemm_workspace_bytes(out, in, m)) return RABIT_EWORKSPACE;
   if (!aligned16(workspace)) return RABIT_EALIGN;
   return dev_status(launch_gemm((const uint4*)L->planes, L->g, L->h, out, in, X, m, Y, y_dtype,
-                                workspace, (hipStream_t)stream, L->n_paths));
+                                workspace, (hipStream_t)stream, L->n_paths,
+                                (flags & RABIT_GEMM_WEFF) != 0));
 }
 
 // --------------------------------------------------------------------------
@@ -266,6 +273,13 @@ int rabit_transpose_planes(const rabit_layer* L, void* planes_t, void* stream) {
 
 int rabit_grad_input(const rabit_layer* L, const uint16_t* dY, int32_t m, void* dX,
                      int32_t dx_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return rabit_grad_input_ex(L, dY, m, dX, dx_dtype, 0u, workspace, workspace_bytes, stream);
+}
+
+int rabit_grad_input_ex(const rabit_layer* L, const uint16_t* dY, int32_t m, void* dX,
+                        int32_t dx_dtype, uint32_t flags, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  if (flags & ~RABIT_GEMM_WEFF) return RABIT_EINVAL;
   int s = check_layer(L);
   if (s) return s;
   if (!dY || !dX) return RABIT_EINVAL;
@@ -279,7 +293,8 @@ int rabit_grad_input(const rabit_layer* L, const uint16_t* dY, int32_t m, void* 
     return RABIT_EWORKSPACE;
   if (!aligned16(workspace)) return RABIT_EALIGN;
   return dev_status(launch_grad_input((const uint4*)L->planes, L->g, L->h, out, in, P, dY, m, dX,
-                                      dx_dtype, workspace, (hipStream_t)stream));
+                                      dx_dtype, workspace, (hipStream_t)stream,
+                                      (flags & RABIT_GEMM_WEFF) != 0));
 }
 
 int rabit_grad_weight(const rabit_layer* L, const uint16_t* X, const uint16_t* dY, int32_t m,

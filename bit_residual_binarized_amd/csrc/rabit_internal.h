@@ -221,9 +221,11 @@ hipError_t launch_gemv_multi(const LinSeg* segs, int nseg, int in, const uint16_
                              const double* stats, float eps, hipStream_t st);
 
 size_t gemm_workspace_bytes(int out, int in, int m);
+// weff: form the effective weight per tile in fp16 (one matrix op per tile
+// instead of one per path)
 hipError_t launch_gemm(const uint4* planes, const uint16_t* g, const uint16_t* h, int out, int in,
                        const uint16_t* X, int m, void* Y, int y_dtype, void* ws, hipStream_t st,
-                       int paths = 2);
+                       int paths = 2, bool weff = false);
 
 // training side (dW, dg, dh; dX through the GEMM of the transposed layer)
 size_t grad_weight_workspace_bytes(int out, int in, int P);
@@ -232,7 +234,7 @@ hipError_t launch_transpose_planes(const uint4* planes, int out, int in, int P, 
                                    hipStream_t st);
 hipError_t launch_grad_input(const uint4* planes, const uint16_t* g, const uint16_t* h, int out,
                              int in, int P, const uint16_t* dY, int m, void* dX, int dx_dtype,
-                             void* ws, hipStream_t st);
+                             void* ws, hipStream_t st, bool weff = false);
 hipError_t launch_grad_weight(const uint4* planes, const uint16_t* g, const uint16_t* h, int out,
                               int in, int P, const uint16_t* X, const uint16_t* dY, int m, float* dW,
                               float* dg, float* dh, int accumulate, void* ws, hipStream_t st);

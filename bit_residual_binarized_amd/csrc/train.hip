@@ -418,13 +418,13 @@ hipError_t launch_transpose_planes(const uint4* planes, int out, int in, int P, 
 
 hipError_t launch_grad_input(const uint4* planes, const uint16_t* g, const uint16_t* h, int out,
                              int in, int P, const uint16_t* dY, int m, void* dX, int dx_dtype,
-                             void* ws, hipStream_t st) {
+                             void* ws, hipStream_t st, bool weff) {
   uint4* pt = (uint4*)ws;
   const size_t planes_t = (size_t)row_groups(in) * col_groups(out) * P * 64 * 16;
   hipError_t e = launch_transpose_planes(planes, out, in, P, pt, st);
   if (e != hipSuccess) return e;
   // W_hatᵀ: out' = in, in' = out, output scales h, input scales g
-  return launch_gemm(pt, h, g, in, out, dY, m, dX, dx_dtype, (char*)ws + a256(planes_t), st, P);
+  return launch_gemm(pt, h, g, in, out, dY, m, dX, dx_dtype, (char*)ws + a256(planes_t), st, P, weff);
 }
 
 hipError_t launch_grad_weight(const uint4* planes, const uint16_t* g, const uint16_t* h, int out,

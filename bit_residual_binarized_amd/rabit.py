@@ -37,7 +37,8 @@ EXPORTS = [
     "rabit_layout_version", "rabit_test_f64_to_16", "rabit_gemv_partial", "rabit_gemv_reduce",
     "rabit_gemv_partial_multi", "rabit_stream_read", "rabit_grad_input_workspace_bytes",
     "rabit_grad_weight_workspace_bytes", "rabit_transpose_planes", "rabit_grad_input",
-    "rabit_grad_weight", "rabit_svid_workspace_bytes", "rabit_svid_init",
+    "rabit_grad_weight", "rabit_svid_workspace_bytes", "rabit_svid_init", "rabit_gemm_ex",
+    "rabit_grad_input_ex",
 ]
 
 
@@ -110,6 +111,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "rabit_grad_input": (ctypes.c_int, [lp, vp, i32, vp, i32, vp, sz, vp]),
         "rabit_grad_weight": (ctypes.c_int, [lp, vp, vp, i32, vp, vp, vp, u32, vp, sz, vp]),
         "rabit_svid_workspace_bytes": (sz, [i32, i32]),
+        "rabit_gemm_ex": (ctypes.c_int, [lp, vp, i32, vp, i32, u32, vp, sz, vp]),
+        "rabit_grad_input_ex": (ctypes.c_int, [lp, vp, i32, vp, i32, u32, vp, sz, vp]),
         "rabit_svid_init": (ctypes.c_int, [vp, i32, i32, i32, i32, i32, vp, vp, u32, vp, vp, vp, vp,
                                            sz, vp]),
     }
@@ -269,9 +272,14 @@ def gemm_workspace(layer: PackedLayer, m: int) -> torch.Tensor:
     return _ws(nb, layer.planes.device)
 
 
+RABIT_GEMM_WEFF = 1
+
+
 def gemm(layer: PackedLayer, xm: torch.Tensor, y_dtype: int = RABIT_OUT_F32,
          y: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
-         stream=None) -> torch.Tensor:
+         stream=None, weff: bool = False) -> torch.Tensor:
+    """Y = X W_hatᵀ; weff=True forms the effective weight per tile in fp16
+    (rabit_gemm_ex with RABIT_GEMM_WEFF)."""
     lib = load()
     assert xm.dtype == torch.bfloat16 and xm.is_contiguous()
     m = xm.shape[0]
@@ -281,8 +289,12 @@ def gemm(layer: PackedLayer, xm: torch.Tensor, y_dtype: int = RABIT_OUT_F32,
     if workspace is None:
         workspace = gemm_workspace(layer, m)
     lc = layer.c()
-    _check(lib.rabit_gemm(ctypes.byref(lc), _ptr(xm), m, _ptr(y), y_dtype, _ptr(workspace),
-                          workspace.numel(), _stream(stream)), "rabit_gemm")
+    if weff:
+        _check(lib.rabit_gemm_ex(ctypes.byref(lc), _ptr(xm), m, _ptr(y), y_dtype, RABIT_GEMM_WEFF,
+                                 _ptr(workspace), workspace.numel(), _stream(stream)), "rabit_gemm_ex")
+    else:
+        _check(lib.rabit_gemm(ctypes.byref(lc), _ptr(xm), m, _ptr(y), y_dtype, _ptr(workspace),
+                              workspace.numel(), _stream(stream)), "rabit_gemm")
     return y
 
 
@@ -314,7 +326,7 @@ def grad_weight_workspace(layer: PackedLayer) -> torch.Tensor:
 
 def grad_input(layer: PackedLayer, dy: torch.Tensor, dx_dtype: int = RABIT_OUT_F32,
                dx: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
-               stream=None) -> torch.Tensor:
+               stream=None, weff: bool = False) -> torch.Tensor:
     """dX = dY W_hat for dY [M][out] bf16."""
     lib = load()
     assert dy.dtype == torch.bfloat16 and dy.is_contiguous()
@@ -325,8 +337,9 @@ def grad_input(layer: PackedLayer, dy: torch.Tensor, dx_dtype: int = RABIT_OUT_F
     if workspace is None:
         workspace = grad_input_workspace(layer, m)
     lc = layer.c()
-    _check(lib.rabit_grad_input(ctypes.byref(lc), _ptr(dy), m, _ptr(dx), dx_dtype, _ptr(workspace),
-                                workspace.numel(), _stream(stream)), "rabit_grad_input")
+    _check(lib.rabit_grad_input_ex(ctypes.byref(lc), _ptr(dy), m, _ptr(dx), dx_dtype,
+                                   RABIT_GEMM_WEFF if weff else 0, _ptr(workspace),
+                                   workspace.numel(), _stream(stream)), "rabit_grad_input_ex")
     return dx
 
 

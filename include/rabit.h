@@ -255,6 +255,10 @@ int rabit_transpose_planes(const rabit_layer *layer, void *planes_t, void *strea
  */
 int rabit_grad_input(const rabit_layer *layer, const uint16_t *dY, int32_t m, void *dX,
                      int32_t dx_dtype, void *workspace, size_t workspace_bytes, void *stream);
+/* rabit_grad_input with the options of rabit_gemm_ex (RABIT_GEMM_WEFF). */
+int rabit_grad_input_ex(const rabit_layer *layer, const uint16_t *dY, int32_t m, void *dX,
+                        int32_t dx_dtype, uint32_t flags, void *workspace, size_t workspace_bytes,
+                        void *stream);
 
 /*
  * dW, dg and dh of the layer for one batch.
@@ -320,6 +324,23 @@ int rabit_svid_init(const float *W, int32_t out_features, int32_t in_features, i
                     int32_t sweeps, int32_t power_passes, const float *f_out, const float *f_in,
                     uint32_t flags, float *g, float *h, void *planes, void *workspace,
                     size_t workspace_bytes, void *stream);
+
+/*
+ * rabit_gemm with options (flags 0 = rabit_gemm).
+ * RABIT_GEMM_WEFF: the effective weight W_hat (paper §4.1 "Multi-bit
+ *   Approximation via Stacking") of each tile is formed in fp16 and the
+ *   matrix cores run once per tile instead of once per path: with
+ *   f[i] = max_p g_p[i] and r_p = fp16(g_p[i] / f[i]), the tile holds
+ *   e[i][j] = Σ_p r_p (±h_p[j]) by fp16 multiply-adds in path order, and
+ *   Y = f ⊙ (X eᵀ) with fp32 accumulation. Each weight is rounded (about
+ *   2^-11 relative), so Y is no longer the exact ±h contraction; half the
+ *   matrix work of the exact path with two paths, a third with three.
+ * Errors as rabit_gemm; RABIT_EINVAL for unknown flags.
+ */
+#define RABIT_GEMM_WEFF 1u
+int rabit_gemm_ex(const rabit_layer *layer, const uint16_t *X, int32_t m, void *Y,
+                  int32_t y_dtype, uint32_t flags, void *workspace, size_t workspace_bytes,
+                  void *stream);
 
 /*
  * Decoder configuration for rabit_decode_step (a Llama-style block; the pages

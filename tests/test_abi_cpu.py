@@ -239,3 +239,12 @@ def test_svid_errors(lib):
     assert sv(fi=FAKE + (20 << 32) + 4) == rabit.RABIT_EALIGN
     assert sv(wsb=16) == rabit.RABIT_EWORKSPACE
     assert sv(P=3, wsb=16) == rabit.RABIT_EWORKSPACE
+
+
+def test_gemm_ex_flags(lib):
+    L = fake_layer()
+    X, Y, ws = FAKE + (3 << 30), FAKE + (4 << 30), FAKE + (5 << 30)
+    assert lib.rabit_gemm_ex(ctypes.byref(L), X, 8, Y, 0, 2, ws, 1 << 30, None) == rabit.RABIT_EINVAL
+    assert lib.rabit_gemm_ex(ctypes.byref(L), X, 0, Y, 0, 1, ws, 1 << 30, None) == rabit.RABIT_ESHAPE
+    assert lib.rabit_grad_input_ex(ctypes.byref(L), X, 8, Y, 0, 4, ws, 1 << 30, None) == rabit.RABIT_EINVAL
+    assert lib.rabit_grad_input_ex(ctypes.byref(L), X, 8, Y, 0, 1, ws, 16, None) == rabit.RABIT_EWORKSPACE
