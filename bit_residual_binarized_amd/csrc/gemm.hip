@@ -82,33 +82,65 @@ __device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
 }
 __device__ __forceinline__ uint32_t f16_to_bits(float f) { return f32_to_f16_bits(f); }
 
-// One workgroup per row of X: row maximum, exponent, scaled fp16 copy.
+// One wave per row of X: row maximum, exponent, scaled fp16 copy. Lane l
+// handles 32-column blocks l, l + 64, ...: four 16-byte loads of bf16, then
+// the block's κ order (dword m = columns m, m + 16) in four 16-byte stores.
 __global__ __launch_bounds__(256) void k_gemm_prep_x(const uint16_t* __restrict__ X, int in, int Kp,
-                                                     GemmWs ws) {
-  const int m = blockIdx.x;
+                                                     int M, GemmWs ws) {
+  const int m = blockIdx.x * 4 + (threadIdx.x >> 6), l = threadIdx.x & 63;
+  if (m >= M) return;
   const uint16_t* xr = X + (size_t)m * in;
+  const int nblk = Kp / 32;
+  const bool vec = (in & 7) == 0;  // rows 16-byte aligned
   float mx = 0.0f;
-  for (int j = threadIdx.x; j < in; j += 256) mx = fmaxf(mx, fabsf(bf16_bits_to_f32(xr[j])));
+  for (int b = l; b < nblk; b += 64) {
+    const int c0 = 32 * b;
+    if (vec && c0 + 32 <= in) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint4 t = *(const uint4*)(xr + c0 + 8 * q);
+        const uint32_t w[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          mx = fmaxf(mx, fmaxf(fabsf(__uint_as_float(w[k] << 16)), fabsf(__uint_as_float(w[k] & 0xFFFF0000u))));
+      }
+    } else {
+      for (int c = c0; c < min(c0 + 32, in); ++c) mx = fmaxf(mx, fabsf(bf16_bits_to_f32(xr[c])));
+    }
+  }
 #pragma unroll
   for (int s = 32; s >= 1; s >>= 1) mx = fmaxf(mx, __shfl_xor(mx, s, 64));
-  __shared__ float smx[4];
-  __shared__ int s_e;
-  if ((threadIdx.x & 63) == 0) smx[threadIdx.x >> 6] = mx;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const float t = fmaxf(fmaxf(smx[0], smx[1]), fmaxf(smx[2], smx[3]));
-    s_e = (t > 0.0f) ? 14 - ilogbf(t) : 0;
-  }
-  __syncthreads();
-  const int e = s_e;
+  const int e = (mx > 0.0f) ? 14 - ilogbf(mx) : 0;
   uint16_t* xo = ws.xh + (size_t)m * Kp;
-  for (int kk = threadIdx.x; kk < Kp; kk += 256) {
-    const int blk = kk >> 5, kap = kk & 31;
-    const int col = blk * 32 + (kap >> 1) + 16 * (kap & 1);
-    const float v = col < in ? bf16_bits_to_f32(xr[col]) : 0.0f;
-    xo[kk] = f32_to_f16_bits(ldexpf(v, e));
+  for (int b = l; b < nblk; b += 64) {
+    const int c0 = 32 * b;
+    float v[32];
+    if (vec && c0 + 32 <= in) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint4 t = *(const uint4*)(xr + c0 + 8 * q);
+        const uint32_t w[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          v[8 * q + 2 * k] = __uint_as_float(w[k] << 16);
+          v[8 * q + 2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < 32; ++c) v[c] = c0 + c < in ? bf16_bits_to_f32(xr[min(c0 + c, in - 1)]) : 0.0f;
+    }
+    // dword mm of the block = (column mm, column mm + 16), scaled by 2^e
+    uint32_t o[16];
+#pragma unroll
+    for (int mm = 0; mm < 16; ++mm)
+      o[mm] = (uint32_t)f32_to_f16_bits(ldexpf(v[mm], e)) |
+              ((uint32_t)f32_to_f16_bits(ldexpf(v[mm + 16], e)) << 16);
+    uint4* dst = (uint4*)(xo + c0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dst[q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
   }
-  if (threadIdx.x == 0) ws.rowexp[m] = e;
+  if (l == 0) ws.rowexp[m] = e;
 }
 
 __global__ void k_gemm_prep_h(const uint16_t* __restrict__ h, int in, int Kp, int P, GemmWs ws) {
@@ -403,7 +435,7 @@ hipError_t launch_gemm(const uint4* planes, const uint16_t* g, const uint16_t* h
   if (paths != 2 && paths != 3) return hipErrorInvalidValue;
   const int Kp = col_groups(in) * 128;
   GemmWs w = carve(ws, out, in, m, paths);
-  hipLaunchKernelGGL(k_gemm_prep_x, dim3(m), dim3(256), 0, st, X, in, Kp, w);
+  hipLaunchKernelGGL(k_gemm_prep_x, dim3((m + 3) / 4), dim3(256), 0, st, X, in, Kp, m, w);
   const int nh = paths * (Kp / 32) * 16;
   hipLaunchKernelGGL(k_gemm_prep_h, dim3((nh + 255) / 256), dim3(256), 0, st, h, in, Kp, paths, w);
   const int bm = weff ? 128 : bm_of(paths), bn = weff ? 2 * kBN : kBN;
