@@ -28,7 +28,10 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kTI = 256;  // dW tile: columns i
-constexpr int kTO = 128;  // dW tile: rows o
+constexpr int kTO = 128;  // dW tile: rows o (128: wave tiles 128 x 64 at two waves per SIMD;
+                          // 256: 128 x 128 at one wave per SIMD, accumulators in AGPRs)
+constexpr int kBO = kTO / 32;   // 16-row matrix tiles per wave along o
+constexpr int kCY = kTO / 64;   // dY columns per loader thread
 constexpr int kK = 32;    // tokens per step
 
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
@@ -111,7 +114,7 @@ __global__ __launch_bounds__(256) void k_transpose_planes(const uint32_t* __rest
 // 16 x 16 tile: four consecutive i, one 16-byte store.
 // ---------------------------------------------------------------------------
 template <int P>
-__global__ __launch_bounds__(256, 2) void k_grad_w(const uint16_t* __restrict__ X,
+__global__ __launch_bounds__(256, kTO == 256 ? 1 : 2) void k_grad_w(const uint16_t* __restrict__ X,
                                                    const uint16_t* __restrict__ dY, int M, int out,
                                                    int in, const uint32_t* __restrict__ planes,
                                                    const uint16_t* __restrict__ g,
@@ -136,7 +139,7 @@ __global__ __launch_bounds__(256, 2) void k_grad_w(const uint16_t* __restrict__ 
   __shared__ uint32_t sBitsW[P][2][4][kTO];  // [p][column group of the tile][word][row o]
   __shared__ float sG[P][kTO];
   __shared__ __align__(16) float sH[P][kTI];
-  __shared__ __align__(16) float sRed[2][P][kTI];
+  __shared__ __align__(16) float sRed[2][P][kTI > kTO ? kTI : kTO];
 
   // side loads for the epilogue, issued before the main loop
   for (int t = tid; t < P * 2 * kTO; t += 256) {
@@ -159,14 +162,14 @@ __global__ __launch_bounds__(256, 2) void k_grad_w(const uint16_t* __restrict__ 
   }
 
   // loaders, per thread and step: X columns i0 + 4 qx .. + 3 and dY columns
-  // o0 + 2 qy, + 1, each for tokens 8 ng .. 8 ng + 7 of the step
+  // o0 + kCY qy .. + kCY - 1, each for tokens 8 ng .. 8 ng + 7 of the step
   // token group = wave: the rows of a load are uniform (scalar addresses)
   const int ng = __builtin_amdgcn_readfirstlane(tid >> 6), qx = tid & 63, qy = tid & 63;
-  const int cx = i0 + 4 * qx, cy = o0 + 2 * qy;
+  const int cx = i0 + 4 * qx, cy = o0 + kCY * qy;
   const bool vx = (in & 3) == 0 && cx + 4 <= in;
-  const bool vy = (out & 1) == 0 && cy + 2 <= out;
+  const bool vy = (out % kCY) == 0 && cy + kCY <= out;
   uint2 rx[8];
-  uint32_t ry[8];
+  uint2 ry[8];  // kCY = 2: .x only
   // Full-width columns: raw buffer loads from a per-step scalar base, the
   // lane's column as the only per-lane offset and the token row as the scalar
   // offset; the descriptor covers rows up to M only, so rows past M read 0.
@@ -202,16 +205,23 @@ __global__ __launch_bounds__(256, 2) void k_grad_w(const uint16_t* __restrict__ 
           (void*)(dY + (size_t)n0 * out), (short)0, (int)(nbytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : nbytes),
           kBufferWord3);
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        ry[j] = __builtin_amdgcn_raw_buffer_load_b32(r, 2 * cy, (8 * ng + j) * out * 2, 0);
+      for (int j = 0; j < 8; ++j) {
+        if (kCY == 4) {
+          const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, 2 * cy, (8 * ng + j) * out * 2, 0);
+          ry[j] = make_uint2(v.x, v.y);
+        } else {
+          ry[j] = make_uint2(__builtin_amdgcn_raw_buffer_load_b32(r, 2 * cy, (8 * ng + j) * out * 2, 0), 0u);
+        }
+      }
     } else {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int n = n0 + 8 * ng + j;
         const size_t row = (size_t)min(n, M - 1) * out;
-        const uint32_t e0 = cy < out ? dY[row + min(cy, out - 1)] : 0u;
-        const uint32_t e1 = cy + 1 < out ? dY[row + min(cy + 1, out - 1)] : 0u;
-        ry[j] = n < M ? (e0 | (e1 << 16)) : 0u;
+        uint32_t e[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int c = 0; c < kCY; ++c) e[c] = cy + c < out ? dY[row + min(cy + c, out - 1)] : 0u;
+        ry[j] = n < M ? make_uint2(e[0] | (e[1] << 16), e[2] | (e[3] << 16)) : make_uint2(0u, 0u);
       }
     }
   };
@@ -237,16 +247,21 @@ __global__ __launch_bounds__(256, 2) void k_grad_w(const uint16_t* __restrict__ 
     chunks(t, c0, c1);
     sA[buf][ng][slot(4 * qx + 2)] = c0;
     sA[buf][ng][slot(4 * qx + 3)] = c1;
-    chunks(ry, c0, c1);
-    sB[buf][ng][slot(2 * qy)] = c0;
-    sB[buf][ng][slot(2 * qy + 1)] = c1;
+#pragma unroll
+    for (int h2 = 0; h2 < kCY / 2; ++h2) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) t[j] = h2 ? ry[j].y : ry[j].x;
+      chunks(t, c0, c1);
+      sB[buf][ng][slot(kCY * qy + 2 * h2)] = c0;
+      sB[buf][ng][slot(kCY * qy + 2 * h2 + 1)] = c1;
+    }
   };
 
-  v4f acc[8][4];
+  v4f acc[8][kBO];
 #pragma unroll
   for (int a = 0; a < 8; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = (v4f){0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < kBO; ++b) acc[a][b] = (v4f){0.f, 0.f, 0.f, 0.f};
 
   const int nsteps = (M + kK - 1) / kK;
   if (nsteps > 0) {
@@ -257,14 +272,15 @@ __global__ __launch_bounds__(256, 2) void k_grad_w(const uint16_t* __restrict__ 
   for (int ks = 0; ks < nsteps; ++ks) {
     const int buf = ks & 1;
     if (ks + 1 < nsteps) load(ks + 1);  // in flight during the matrix ops
-    v8bf fb[4];
+    v8bf fb[kBO];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) fb[b] = __builtin_bit_cast(v8bf, sB[buf][fg][slot(64 * wo + 16 * b + fr)]);
+    for (int b = 0; b < kBO; ++b)
+      fb[b] = __builtin_bit_cast(v8bf, sB[buf][fg][slot((kTO / 2) * wo + 16 * b + fr)]);
 #pragma unroll
     for (int a = 0; a < 8; ++a) {
       const v8bf fa = __builtin_bit_cast(v8bf, sA[buf][fg][slot(128 * wi + 16 * a + fr)]);
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
+      for (int b = 0; b < kBO; ++b)
         acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb[b], acc[a][b], 0, 0, 0);
     }
     if (ks + 1 < nsteps) store(buf ^ 1);
@@ -289,8 +305,8 @@ __global__ __launch_bounds__(256, 2) void k_grad_w(const uint16_t* __restrict__ 
     for (int p = 0; p < P; ++p) {
       float cs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int ol = 64 * wo + 16 * b + fr;
+      for (int b = 0; b < kBO; ++b) {
+        const int ol = (kTO / 2) * wo + 16 * b + fr;
         const uint32_t word = sBitsW[p][wi][a >> 1][ol];
         const float go = sG[p][ol];
 #pragma unroll
@@ -319,22 +335,23 @@ __global__ __launch_bounds__(256, 2) void k_grad_w(const uint16_t* __restrict__ 
   }
   __syncthreads();
 
-  // pass 2, dW stores and row sums (dg). A full tile without accumulation
-  // stores 16 bytes per lane and tile with no guards; the other copy guards
-  // every element.
-  float rs[P][4];
-#pragma unroll
-  for (int p = 0; p < P; ++p)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) rs[p][b] = 0.f;
+  // pass 2, dW stores and row sums (dg), one 16-row block b at a time (its
+  // sums reduced before the next block starts, so few values stay live). A
+  // full tile without accumulation stores 16 bytes per lane and tile with no
+  // guards; the other copy guards every element.
   auto pass2 = [&](auto fast_tag) {
     constexpr bool kFast = decltype(fast_tag)::value;
 #pragma unroll
-    for (int a = 0; a < 8; ++a) {
-      const int il = 128 * wi + 16 * a + 4 * fg;
+    for (int b = 0; b < kBO; ++b) {
+      const int ol = (kTO / 2) * wo + 16 * b + fr;
+      const int o = o0 + ol;
+      float rs[P];
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int o = o0 + 64 * wo + 16 * b + fr, i = i0 + il;
+      for (int p = 0; p < P; ++p) rs[p] = 0.f;
+#pragma unroll
+      for (int a = 0; a < 8; ++a) {
+        const int il = 128 * wi + 16 * a + 4 * fg;
+        const int i = i0 + il;
         float* d = dW + (size_t)o * in + i;
         if (kFast) {
           *(float4*)d = make_float4(acc[a][b][0], acc[a][b][1], acc[a][b][2], acc[a][b][3]);
@@ -343,19 +360,23 @@ __global__ __launch_bounds__(256, 2) void k_grad_w(const uint16_t* __restrict__ 
           for (int r = 0; r < 4; ++r)
             if (i + r < in) d[r] = accumulate ? d[r] + acc[a][b][r] : acc[a][b][r];
         }
-      }
 #pragma unroll
-      for (int p = 0; p < P; ++p) {
-        const float4 hv = *(const float4*)&sH[p][il];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const uint32_t word = sBitsW[p][wi][a >> 1][64 * wo + 16 * b + fr];
+        for (int p = 0; p < P; ++p) {
+          const float4 hv = *(const float4*)&sH[p][il];
+          const uint32_t word = sBitsW[p][wi][a >> 1][ol];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const uint32_t sgn = ((word >> ((16 * a + 4 * fg + r) & 31)) & 1u) << 31;
-            rs[p][b] += acc[a][b][r] * __uint_as_float(__float_as_uint((&hv.x)[r]) ^ sgn);
+            rs[p] += acc[a][b][r] * __uint_as_float(__float_as_uint((&hv.x)[r]) ^ sgn);
           }
         }
+      }
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        float v = rs[p];
+        v += __shfl_xor(v, 16, 64);
+        v += __shfl_xor(v, 32, 64);
+        if (fg == 0) sRed[wi][p][ol] = v;
       }
     }
   };
@@ -363,15 +384,6 @@ __global__ __launch_bounds__(256, 2) void k_grad_w(const uint16_t* __restrict__ 
     pass2(std::true_type{});
   else
     pass2(std::false_type{});
-#pragma unroll
-  for (int p = 0; p < P; ++p)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      float v = rs[p][b];
-      v += __shfl_xor(v, 16, 64);
-      v += __shfl_xor(v, 32, 64);
-      if (fg == 0) sRed[wi][p][64 * wo + 16 * b + fr] = v;
-    }
   __syncthreads();
   for (int t = tid; t < P * kTO; t += 256) {
     const int p = t / kTO, r = t % kTO;
