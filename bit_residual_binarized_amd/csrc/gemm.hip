@@ -165,7 +165,7 @@ __global__ void k_gemm_prep_h(const uint16_t* __restrict__ h, int in, int Kp, in
 //
 // WEFF: the effective weight of the tile, Σ_p g_p[n] (±h_p[k]), is formed in
 // fp16 before the matrix op instead of one matrix op per path: with
-// f[n] = max_p g_p[n] and r_p = g_p / f (fp16, in [0, 1]), the B fragment is
+// f[n] = max_p |g_p[n]| and r_p = g_p / f (fp16, in [-1, 1]), the B fragment is
 // e = Σ_p r_p (±h_p) by packed fp16 multiply-adds (path order) and f[n] is
 // applied in the epilogue. One accumulator set; 128 x 256 tiles for any P,
 // each wave 64 output columns.
@@ -233,7 +233,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint4* __restrict__ plane
 #pragma unroll
       for (int p = 0; p < P; ++p) {
         gv[p] = f16_bits_to_f32(g[(size_t)p * out + n]);
-        f = fmaxf(f, gv[p]);
+        f = fmaxf(f, fabsf(gv[p]));
       }
 #pragma unroll
       for (int p = 0; p < P; ++p) {
@@ -381,9 +381,10 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint4* __restrict__ plane
     const int n = n0 + wn + 16 * j + (l & 15);
     if (n >= out) continue;
     float g0 = f16_bits_to_f32(g[n]);
-    if (WEFF) {  // f[n] = max_p g_p[n], as in the prologue
+    if (WEFF) {  // f[n] = max_p |g_p[n]|, as in the prologue
+      g0 = fabsf(g0);
 #pragma unroll
-      for (int p = 1; p < P; ++p) g0 = fmaxf(g0, f16_bits_to_f32(g[(size_t)p * out + n]));
+      for (int p = 1; p < P; ++p) g0 = fmaxf(g0, fabsf(f16_bits_to_f32(g[(size_t)p * out + n])));
     }
     const float g1 = (!WEFF) ? f16_bits_to_f32(g[out + n]) : 0.f;
     const float g2 = (!WEFF && P == 3) ? f16_bits_to_f32(g[2 * out + n]) : 0.f;

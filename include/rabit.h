@@ -330,7 +330,7 @@ int rabit_svid_init(const float *W, int32_t out_features, int32_t in_features, i
  * RABIT_GEMM_WEFF: the effective weight W_hat (paper §4.1 "Multi-bit
  *   Approximation via Stacking") of each tile is formed in fp16 and the
  *   matrix cores run once per tile instead of once per path: with
- *   f[i] = max_p g_p[i] and r_p = fp16(g_p[i] / f[i]), the tile holds
+ *   f[i] = max_p |g_p[i]| and r_p = fp16(g_p[i] / f[i]), the tile holds
  *   e[i][j] = Σ_p r_p (±h_p[j]) by fp16 multiply-adds in path order, and
  *   Y = f ⊙ (X eᵀ) with fp32 accumulation. Each weight is rounded (about
  *   2^-11 relative), so Y is no longer the exact ±h contraction; half the
