@@ -29,7 +29,10 @@ constexpr int kBN = 128, kBK = 64;
 // token rows per workgroup: 128 with two paths; 64 with three (the third
 // accumulator set would not fit the registers of two waves per SIMD)
 __host__ __device__ constexpr int bm_of(int P) { return P == 2 ? 128 : 64; }
-constexpr int kLdsStride = 36;  // dwords per 64-column row in LDS (32 + 4 padding)
+// output columns per workgroup: 128 on the exact path; 256 on the
+// effective-weight path with two paths, 128 with three (the three ratio
+// registers per fragment column would spill with four fragments per wave)
+__host__ __device__ constexpr int bn_of(int P, bool weff) { return weff && P == 2 ? 256 : 128; }
 
 struct GemmWs {
   uint16_t* xh;      // fp16 [m][Kp], κ-permuted inside 32-column blocks
@@ -67,7 +70,7 @@ __host__ inline GemmWs carve(void* ws, int out, int in, int m, int P) {
 __host__ inline size_t ws_bytes_p(int out, int in, int m, int P) {
   const size_t Kp = (size_t)col_groups(in) * 128;
   // the exact path's tiles (bm_of(P) rows) or the effective-weight path's (128)
-  const int z = std::max(split_k(out, in, m, bm_of(P)), split_k(out, in, m, 128, 2 * kBN));
+  const int z = std::max(split_k(out, in, m, bm_of(P)), split_k(out, in, m, 128, bn_of(P, true)));
   return a256((size_t)m * Kp * 2) + a256((size_t)m * 4) + a256((size_t)P * (Kp / 32) * 16 * 4) +
          (z > 1 ? a256((size_t)z * m * out * 4) : 0);
 }
@@ -154,33 +157,109 @@ __global__ void k_gemm_prep_h(const uint16_t* __restrict__ h, int in, int Kp, in
   ws.hpairs[idx] = lo | (hi << 16);
 }
 
-// 128 x 128 output tile per workgroup and K slice blockIdx.z, 64 columns per
-// step. Wave w owns output columns [32 w, 32 w + 32) for all 128 rows, and
-// builds its own ±h_p fragments in registers from the plane words (no LDS for
-// the weights): lane (fr, fg) of fragment (p, j, sub) holds rows κ = 8 fg ..
-// 8 fg + 7 of column n0 + 32 w + 16 j + fr, i.e. pairs (m, m + 16), m = 4 fg + c,
-// of the 32-column block. X goes through a double-buffered LDS tile (one
-// barrier per step). The next step's X rows, plane words and h pairs are
-// loaded into registers while the current step runs on the matrix cores.
+// Raw (untyped, unswizzled) buffer resource word 3.
+constexpr int kBufWord3 = 0x00020000;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Direct buffer-to-LDS loads of 16 and 4 bytes per lane: lane l writes its
+// bytes at dst + size * l. (Plain device functions: inside a kernel template
+// the builtin keeps the host pass from emitting the kernel's launch handle.)
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, lds_void* dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void lds_load4(__amdgpu_buffer_rsrc_t r, lds_void* dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 4, voff, 0, 0, 0);
+}
+
+// s_waitcnt immediate: at most n vector-memory loads of this wave in flight
+// and (lgkm0) none of its LDS accesses; expcnt unconstrained
+__host__ __device__ constexpr int vmcnt_imm(int n, bool lgkm0 = false) {
+  return (n & 15) | ((n >> 4) << 14) | (7 << 4) | ((lgkm0 ? 0 : 15) << 8);
+}
+
+// Workgroup barrier after this wave's loads but the last N have landed in
+// LDS and its own LDS reads are done. A fence (__syncthreads) would wait for
+// every load in flight, direct-to-LDS ones included; the empty asm
+// statements keep the compiler from moving memory accesses across the
+// barrier instead.
+template <int N>
+__device__ __forceinline__ void ring_barrier() {
+  __builtin_amdgcn_sched_barrier(0);  // no instruction moves across a step boundary
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(N, true));
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// LDS bytes of one stage of the main loop's ring (X rows, plane words and h
+// pairs of one 64-column step), and the ring depth: four stages where two
+// workgroups fit a CU's 160 KiB of LDS, else three
+__host__ __device__ constexpr int stage_bytes(int BM, int BN, int P) { return BM * 128 + P * BN * 8 + 1024; }
+__host__ __device__ constexpr int n_stages(int BM, int BN, int P) {
+  return 2 * 4 * stage_bytes(BM, BN, P) <= 160 * 1024 ? 4 : 3;
+}
+
+// kBM x kBN output tile per workgroup and K slice blockIdx.z, 64 columns per
+// step. Wave w owns output columns [16 NJ w, 16 NJ (w + 1)) for all kBM rows,
+// and builds its own ±h_p fragments in registers from the plane words: lane
+// (fr, fg) of fragment (p, j, sub) holds rows κ = 8 fg .. 8 fg + 7 of column
+// n0 + 16 NJ w + 16 j + fr, i.e. pairs (m, m + 16), m = 4 fg + c, of the
+// 32-column block.
+//
+// Operands flow through a ring of NS LDS stages filled by direct
+// buffer-to-LDS loads, NS - 1 steps ahead of the matrix ops: no staging
+// registers and no per-step address arithmetic (the step selects the buffer
+// descriptor's base; rows past M and steps past the slice read as zero from
+// the descriptor's bound). Every wave issues the same number of loads per
+// stage, so one vmcnt value waits for a stage; one barrier per step publishes
+// the stage and frees the one the next loads overwrite.
 //
 // WEFF: the effective weight of the tile, Σ_p g_p[n] (±h_p[k]), is formed in
 // fp16 before the matrix op instead of one matrix op per path: with
 // f[n] = max_p |g_p[n]| and r_p = g_p / f (fp16, in [-1, 1]), the B fragment is
 // e = Σ_p r_p (±h_p) by packed fp16 multiply-adds (path order) and f[n] is
-// applied in the epilogue. One accumulator set; 128 x 256 tiles for any P,
-// each wave 64 output columns.
+// applied in the epilogue. One accumulator set; 128-row tiles of 256 output
+// columns with two paths (64 per wave) and 128 with three (32 per wave).
 template <int P, bool WEFF>
 __global__ __launch_bounds__(256, 2) void k_gemm(const uint4* __restrict__ planes,
                                               const uint16_t* __restrict__ g, int out, int M,
                                               int Kp, int ksteps, GemmWs ws, void* Y, int y_dtype) {
   constexpr int kBM = WEFF ? 128 : bm_of(P), MT = kBM / 16;  // 16-row matrix tiles per wave
-  constexpr int NA = WEFF ? 1 : P;                             // accumulator sets
-  // 16-column fragments per wave: 2 (exact path), 4 (WEFF: one fragment
-  // build feeds four matrix ops per X fragment read, as in the exact path)
-  constexpr int NJ = WEFF ? 4 : 2;
-  const int n0 = blockIdx.x * (64 * NJ), m0 = blockIdx.y * kBM;
+  constexpr int kBNt = bn_of(P, WEFF);
+  constexpr int NA = WEFF ? 1 : P;  // accumulator sets
+  constexpr int NJ = kBNt / 64;     // 16-column fragments per wave
+  constexpr int NS = n_stages(kBM, kBNt, P);
+  // loads per wave and stage: X in 16-byte units (4 KiB per workgroup-wide
+  // load), words in 4-byte units (1 KiB), h pairs in one load (8 P lanes
+  // carry pairs, the others read zeros: no lane is masked off, since a
+  // masked load is a branch that costs the compiler its count of the loads
+  // in flight)
+  constexpr int LA = kBM / 32, LW = P * kBNt / 128, NL = LA + LW + 1;
+  // each part of each stage is an object of its own, so that the compiler
+  // sees that reading one stage does not wait for loads into the others
+  __shared__ __align__(16) uint32_t sa0[kBM * 32], sa1[kBM * 32], sa2[kBM * 32], sa3[kBM * 32];
+  __shared__ __align__(16) uint2 sw0[P * kBNt], sw1[P * kBNt], sw2[P * kBNt], sw3[P * kBNt];
+  __shared__ __align__(16) uint32_t sh0[256], sh1[256], sh2[256], sh3[256];
+  struct SP {
+    uint32_t* a;  // row r: 128 bytes; 16-byte slot s holds column block s ^ (r & 7): the 8
+                  // rows that one 128-byte phase of a fragment read touches hit 8 slots
+    uint2* w;     // [p][n]: words 2 ks, 2 ks + 1 of row n0 + n, path p
+    uint32_t* h;  // h pair e = 32 p + 16 sub + q (the step's two 32-column blocks) at
+                  // 64 (e / 8 P) + e % 8 P: 8 P pairs per wave's 64-dword slot
+  };
+  auto stage = [&](auto U) __attribute__((always_inline)) -> SP {
+    constexpr int u = decltype(U)::value;
+    if constexpr (u == 0) return SP{sa0, sw0, sh0};
+    else if constexpr (u == 1) return SP{sa1, sw1, sh1};
+    else if constexpr (u == 2) return SP{sa2, sw2, sh2};
+    else return SP{sa3, sw3, sh3};
+  };
+
+  const int n0 = blockIdx.x * kBNt, m0 = blockIdx.y * kBM;
   const int tid = threadIdx.x, l = tid & 63;
-  const int wn = __builtin_amdgcn_readfirstlane(tid >> 6) * (16 * NJ);
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = w * (16 * NJ);
   const int KG = Kp / 128;
   const int nb = Kp / 32;
   const int out_pad = row_groups(out) * 64;
@@ -188,9 +267,6 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint4* __restrict__ plane
   // 16-row MFMA tiles of the workgroup that hold rows of X (uniform)
   const int mtiles = __builtin_amdgcn_readfirstlane(min(MT, max(0, (M - m0 + 15) / 16)));
   const int fr = l & 15, fg = l >> 4;
-
-  __shared__ __align__(16) uint32_t sA[2][kBM * kLdsStride];
-  __shared__ __align__(16) uint32_t sH[2][P][2][16];  // [buffer][p][sub]: the step's h pairs
 
   v4f acc[NA][MT][NJ];
 #pragma unroll
@@ -200,30 +276,62 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint4* __restrict__ plane
 #pragma unroll
       for (int j = 0; j < NJ; ++j) acc[p][i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-  // A loader: thread -> row m0 + (tid >> 1), half (tid & 1) of the 64 columns
-  const int am = m0 + (tid >> 1), ah = tid & 1;
-  const bool aload = (tid >> 1) < kBM;  // all threads with 128 rows, half with 64
-  const bool avalid = aload && am < M;
-  const uint4* asrc = (const uint4*)(ws.xh + (size_t)min(am, M - 1) * Kp) + ah * 4;
-  // B: the words of rows n0 + wn + 16 j + fr. These rows lie in one 64-row
-  // group (n0 + wn is a multiple of 16 NJ), so one base pointer per path
-  // serves every j (row 16 j is 16 j units further); a group past the last
-  // is clamped to it (those columns are not stored).
-  const uint32_t* wsrc[P];
-  {
-    const int base = n0 + wn;
-    const int rg = min(base >> 6, out_pad / 64 - 1);
+  // ---- loader: per-lane byte offsets, the same for every step ----
+  // X: load i of wave w fills rows 8 (4 i + w) .. + 7; lane l: row
+  // 8 (4 i + w) + (l >> 3), LDS slot l & 7, column block (l & 7) ^ (row & 7)
+  uint32_t offA[LA];
 #pragma unroll
-    for (int p = 0; p < P; ++p)
-      wsrc[p] = (const uint32_t*)(planes + unit_index(rg, 0, p, (base & 63) + fr, KG, P));
+  for (int i = 0; i < LA; ++i) {
+    const int r = 8 * (4 * i + w) + (l >> 3);
+    offA[i] = (uint32_t)r * (uint32_t)Kp * 2u + 16u * (uint32_t)((l & 7) ^ (r & 7));
   }
-  // h pairs of the step, staged through LDS by threads 0 .. 32 P - 1: (p, sub, pair)
-  const bool hload = tid < 32 * P;
-  const int hp = hload ? tid >> 5 : 0, hs = (tid >> 4) & 1, hq = tid & 15;
-  const uint32_t* hsrc = ws.hpairs + (size_t)hp * nb * 16 + hs * 16 + hq;
+  // words: load i of wave w, lane l: element e = 64 (4 i + w) + l of [P][kBNt][2]
+  // (rows past the last 64-row group read that group; they are not stored)
+  uint32_t offW[LW];
+#pragma unroll
+  for (int i = 0; i < LW; ++i) {
+    const int e = 64 * (4 * i + w) + l;
+    const int p = e / (2 * kBNt), n = (e >> 1) % kBNt, d = e & 1;
+    const int rg = min((n0 + n) >> 6, out_pad / 64 - 1);
+    offW[i] = (uint32_t)(unit_index(rg, 0, p, n & 63, KG, P) * 16 + 4 * d);
+  }
+  // h pairs: lane l < 8 P of wave w loads pair e = 8 P w + l of [P][2][16];
+  // the other lanes read past the descriptor's bound (zeros)
+  const uint32_t offH = l < 8 * P ? 4u * (uint32_t)(((8 * P * w + l) >> 5) * nb * 16 + ((8 * P * w + l) & 31))
+                                  : 0x7FFFFFF0u;
+  const size_t plane_bytes = (size_t)(out_pad / 64) * KG * P * 1024;
+  const size_t x_bytes = (size_t)(M - m0) * Kp * 2;
+  auto issue = [&](SP S, int k) __attribute__((always_inline)) {
+    const bool live = k < ks1;  // uniform: later steps only keep the load count
+    {
+      const size_t kb = (size_t)k * kBK * 2;
+      const uint32_t n = live ? (uint32_t)min(x_bytes - kb, (size_t)0xFFFFFFFFu) : 0u;
+      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)((const char*)(ws.xh + (size_t)m0 * Kp) + kb), (short)0, (int)n, kBufWord3);
+#pragma unroll
+      for (int i = 0; i < LA; ++i)
+        lds_load16(r, (lds_void*)(S.a + (4 * i + w) * 256), offA[i]);
+    }
+    {
+      const size_t kb = (size_t)(k >> 1) * P * 1024 + 8 * (k & 1);
+      const uint32_t n = live ? (uint32_t)(plane_bytes - kb) : 0u;
+      const __amdgpu_buffer_rsrc_t r =
+          __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)planes + kb), (short)0, (int)n, kBufWord3);
+#pragma unroll
+      for (int i = 0; i < LW; ++i)
+        lds_load4(r, (lds_void*)((uint32_t*)S.w + (4 * i + w) * 64), offW[i]);
+    }
+    {
+      const size_t kb = (size_t)k * 32 * 4;
+      const uint32_t n = live ? (uint32_t)((size_t)P * nb * 16 * 4 - kb) : 0u;
+      const __amdgpu_buffer_rsrc_t r =
+          __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)ws.hpairs + kb), (short)0, (int)n, kBufWord3);
+      lds_load4(r, (lds_void*)(S.h + 64 * w), offH);
+    }
+  };
 
-  // WEFF: per fragment column n (j = 0, 1), f = max_p g_p[n] and the fp16
-  // ratios r_p = g_p / f, duplicated into both halves of a dword
+  // WEFF: per fragment column n (j = 0 .. NJ - 1), f = max_p |g_p[n]| and the
+  // fp16 ratios r_p = g_p / f, duplicated into both halves of a dword
   uint32_t rpair[P][NJ];
   if (WEFF) {
 #pragma unroll
@@ -243,86 +351,34 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint4* __restrict__ plane
     }
   }
 
-  // WEFF: the step's plane words of the workgroup's 256 rows go through LDS
-  // (thread t loads row n0 + t of every path), which keeps the registers of
-  // four fragments per wave free for the accumulators
-  constexpr int NW = WEFF ? 2 : 1;
-  __shared__ __align__(16) uint2 sW[NW][WEFF ? P : 1][WEFF ? 256 : 1];
-  const uint32_t* wrow[P];
-  if (WEFF) {
-    const int r = n0 + tid;
-    const int rg = min(r >> 6, out_pad / 64 - 1);
-#pragma unroll
-    for (int p = 0; p < P; ++p)
-      wrow[p] = (const uint32_t*)(planes + unit_index(rg, 0, p, r & 63, KG, P));
-  }
-
-  uint4 ra[4];
-  uint2 rw[P][WEFF ? 1 : NJ];  // [p][j]: words 2 ks, 2 ks + 1 of the row (the two 32-column blocks)
-  uint32_t rh = 0;
-  auto load = [&](int ks) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) ra[q] = asrc[(size_t)ks * 8 + q];
-    // column group ks / 2 is P x 64 units (4 dwords each) after group 0
-    const size_t wo = (size_t)(ks >> 1) * (P * 64 * 4) + 2 * (ks & 1);
-#pragma unroll
-    for (int p = 0; p < P; ++p) {
-      if (WEFF) {
-        rw[p][0] = *(const uint2*)(wrow[p] + wo);
-      } else {
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) rw[p][j] = *(const uint2*)(wsrc[p] + 64 * j + wo);
-      }
-    }
-    if (hload) rh = hsrc[(size_t)ks * 32];
-  };
-  auto store_a = [&](int buf) {
-    if (aload) {
-      uint32_t* da = sA[buf] + (tid >> 1) * kLdsStride + ah * 16;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) *(uint4*)(da + 4 * q) = avalid ? ra[q] : make_uint4(0, 0, 0, 0);
-    }
-    if (hload) sH[buf][hp][hs][hq] = rh;
-    if (WEFF) {
-#pragma unroll
-      for (int p = 0; p < P; ++p) sW[buf & (NW - 1)][p][tid] = rw[p][0];
-    }
-  };
-  if (ks0 < ks1) {
-    load(ks0);
-    store_a(0);
-  }
-  __syncthreads();
-
-  // the main loop, in a copy without per-tile guards for full 128-row tiles
-  // (a guard per matrix op splits the loop into small blocks that the
-  // scheduler cannot overlap)
-  auto run = [&](auto full_tag) {
-  constexpr bool kFull = decltype(full_tag)::value;
-  for (int ks = ks0; ks < ks1; ++ks) {
-    const int buf = (ks - ks0) & 1;
-    uint2 cw[P][WEFF ? 1 : NJ];  // WEFF reads its words from LDS where it uses them
+  auto hpos = [](int e) { return 64 * (e / (8 * P)) + e % (8 * P); };
+  // the matrix ops of one step from stage S
+  const int xsw = fr & 7;  // this lane's X rows 16 i + fr share the slot swizzle
+  auto compute = [&](SP S, auto full_tag) __attribute__((always_inline)) {
+    constexpr bool kFull = decltype(full_tag)::value;
+    uint2 cw[P][WEFF ? 1 : NJ];  // exact path: this lane's words, both 32-column blocks
     if (!WEFF) {
 #pragma unroll
       for (int p = 0; p < P; ++p)
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) cw[p][WEFF ? 0 : j] = rw[p][WEFF ? 0 : j];
+        for (int j = 0; j < NJ; ++j) cw[p][WEFF ? 0 : j] = S.w[p * kBNt + wn + 16 * j + fr];
     }
-    if (ks + 1 < ks1) load(ks + 1);  // in flight during the matrix ops
-
-    const uint32_t* a0 = sA[buf] + fr * kLdsStride + 4 * fg;
+    const uint32_t* a0 = S.a + fr * 32;
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
+      // one half's X fragments live at a time (two halves' did not fit the
+      // registers of two waves per SIMD with two paths)
+      if (sub) __builtin_amdgcn_sched_barrier(0);
       v8h fa[MT];
 #pragma unroll
-      for (int i = 0; i < MT; ++i) fa[i] = *(const v8h*)(a0 + 16 * i * kLdsStride + 16 * sub);
+      for (int i = 0; i < MT; ++i) fa[i] = *(const v8h*)(a0 + 512 * i + 4 * ((fg + 4 * sub) ^ xsw));
       // dword c of a fragment holds columns (m, m + 16), m = 4 fg + c: the
       // sign bits are bits m and m + 16 of the word, moved to bits 15 and 31
       const int sh = 15 - 4 * fg;
       if (WEFF) {
         uint4 hh[P];
 #pragma unroll
-        for (int p = 0; p < P; ++p) hh[p] = *(const uint4*)(&sH[buf][p][sub][4 * fg]);
+        for (int p = 0; p < P; ++p) hh[p] = *(const uint4*)(S.h + hpos(32 * p + 16 * sub + 4 * fg));
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
           uint32_t e[4];
@@ -331,8 +387,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint4* __restrict__ plane
             h2v t;
 #pragma unroll
             for (int p = 0; p < P; ++p) {
-              const uint32_t w = ((const uint32_t*)&sW[buf & (NW - 1)][p][wn + 16 * j + fr])[sub];
-              const h2v x = __builtin_bit_cast(h2v, (&hh[p].x)[c] ^ ((w << (sh - c)) & 0x80008000u));
+              const uint32_t wd = ((const uint32_t*)(S.w + p * kBNt + wn + 16 * j + fr))[sub];
+              const h2v x = __builtin_bit_cast(h2v, (&hh[p].x)[c] ^ ((wd << (sh - c)) & 0x80008000u));
               const h2v r = __builtin_bit_cast(h2v, rpair[p][j]);
               t = p == 0 ? r * x : __builtin_elementwise_fma(r, x, t);
             }
@@ -346,33 +402,61 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint4* __restrict__ plane
         }
       } else {
 #pragma unroll
-      for (int p = 0; p < P; ++p) {
-        const uint4 hh = *(const uint4*)(&sH[buf][p][sub][4 * fg]);
+        for (int p = 0; p < P; ++p) {
+          const uint4 hh = *(const uint4*)(S.h + hpos(32 * p + 16 * sub + 4 * fg));
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const uint32_t w = sub ? cw[p][WEFF ? 0 : j].y : cw[p][WEFF ? 0 : j].x;
-          uint4 e;
-          e.x = hh.x ^ ((w << sh) & 0x80008000u);
-          e.y = hh.y ^ ((w << (sh - 1)) & 0x80008000u);
-          e.z = hh.z ^ ((w << (sh - 2)) & 0x80008000u);
-          e.w = hh.w ^ ((w << (sh - 3)) & 0x80008000u);
-          const v8h fb = __builtin_bit_cast(v8h, e);
+          for (int j = 0; j < NJ; ++j) {
+            const uint32_t wd = sub ? cw[p][WEFF ? 0 : j].y : cw[p][WEFF ? 0 : j].x;
+            uint4 e;
+            e.x = hh.x ^ ((wd << sh) & 0x80008000u);
+            e.y = hh.y ^ ((wd << (sh - 1)) & 0x80008000u);
+            e.z = hh.z ^ ((wd << (sh - 2)) & 0x80008000u);
+            e.w = hh.w ^ ((wd << (sh - 3)) & 0x80008000u);
+            const v8h fb = __builtin_bit_cast(v8h, e);
 #pragma unroll
-          for (int i = 0; i < MT; ++i)
-            if (kFull || i < mtiles)
-              acc[p][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[i], fb, acc[p][i][j], 0, 0, 0);
+            for (int i = 0; i < MT; ++i)
+              if (kFull || i < mtiles)
+                acc[p][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[i], fb, acc[p][i][j], 0, 0, 0);
+          }
         }
       }
-      }
     }
-    if (ks + 1 < ks1) store_a(buf ^ 1);
-    __syncthreads();
-  }
+  };
+
+  // step k from stage U: wait for this wave's loads of the stage (NS - 2
+  // later stages stay in flight), barrier (every wave's loads have landed and
+  // every wave is done with step k - 1), the matrix ops, then refill the
+  // stage step k - 1 used with step k + NS - 1 (issued after this step's LDS
+  // reads, the compiler adds no wait of its own for the loads in flight)
+  auto step = [&](auto U, int k, auto full_tag) __attribute__((always_inline)) {
+    constexpr int u = decltype(U)::value;
+    ring_barrier<(NS - 2) * NL>();
+    issue(stage(std::integral_constant<int, (u + NS - 1) % NS>{}), k + NS - 1);
+    compute(stage(U), full_tag);
+  };
+  issue(stage(std::integral_constant<int, 0>{}), ks0);
+  issue(stage(std::integral_constant<int, 1>{}), ks0 + 1);
+  if constexpr (NS == 4) issue(stage(std::integral_constant<int, 2>{}), ks0 + 2);
+  // the main loop, in a copy without per-tile guards for full tiles (a guard
+  // per matrix op splits the loop into small blocks that the scheduler cannot
+  // overlap), unrolled over the ring so that each stage is a distinct object.
+  // The unrolled steps run unconditionally: a step past the slice reads the
+  // zeros its zero-length descriptors return and adds exactly zero (a branch
+  // per step made the compiler wait for every load in flight at the joins).
+  auto run = [&](auto full_tag) __attribute__((always_inline)) {
+    for (int ks = ks0; ks < ks1; ks += NS) {
+      step(std::integral_constant<int, 0>{}, ks, full_tag);
+      step(std::integral_constant<int, 1>{}, ks + 1, full_tag);
+      step(std::integral_constant<int, 2>{}, ks + 2, full_tag);
+      if constexpr (NS == 4) step(std::integral_constant<int, 3>{}, ks + 3, full_tag);
+    }
   };
   if (mtiles == MT)
     run(std::true_type{});
   else
     run(std::false_type{});
+  // no load may still write this workgroup's LDS when it ends
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
   // epilogue: C[i][j] of a 16x16 tile: lane l, reg r -> row 4(l/16)+r, col l%16
   const bool split = gridDim.z > 1;
@@ -410,7 +494,6 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint4* __restrict__ plane
     }
   }
 }
-
 // split K: Y = 2^-rowexp Σ_z part[z] (ascending z)
 __global__ __launch_bounds__(256) void k_gemm_reduce(GemmWs ws, int out, int M, int Z, void* Y,
                                                      int y_dtype) {
@@ -439,7 +522,7 @@ hipError_t launch_gemm(const uint4* planes, const uint16_t* g, const uint16_t* h
   hipLaunchKernelGGL(k_gemm_prep_x, dim3((m + 3) / 4), dim3(256), 0, st, X, in, Kp, m, w);
   const int nh = paths * (Kp / 32) * 16;
   hipLaunchKernelGGL(k_gemm_prep_h, dim3((nh + 255) / 256), dim3(256), 0, st, h, in, Kp, paths, w);
-  const int bm = weff ? 128 : bm_of(paths), bn = weff ? 2 * kBN : kBN;
+  const int bm = weff ? 128 : bm_of(paths), bn = bn_of(paths, weff);
   const int Z = split_k(out, in, m, bm, bn);
   const int steps = Kp / kBK;
   const int per = (steps + Z - 1) / Z;
