@@ -251,7 +251,9 @@ def test_gemv_partial_multi_equals_gemv(gpu_lib):
             assert torch.equal(y, gpu_lib.gemv(L, x))
 
 
-GEMM_CASES = [(64, 256, 1), (130, 1000, 37), (256, 4096, 512), (1024, 4096, 130), (300, 1100, 257)]
+# (256, 4100, 64): 66 K steps over 16 split-K slices of 5, the last two empty
+GEMM_CASES = [(64, 256, 1), (130, 1000, 37), (256, 4096, 512), (1024, 4096, 130), (300, 1100, 257),
+              (256, 4100, 64)]
 
 
 @pytest.mark.parametrize("case", GEMM_CASES)

@@ -31,7 +31,8 @@ def packed(rabit, out, inp, seed, P):
 
 
 @pytest.mark.parametrize("P", [2, 3])
-@pytest.mark.parametrize("shape", [(256, 512, 64), (1000, 1100, 300), (130, 260, 1), (4096, 4096, 512)])
+@pytest.mark.parametrize("shape", [(256, 512, 64), (1000, 1100, 300), (130, 260, 1), (4096, 4096, 512),
+                                   (256, 4100, 64)])
 def test_gemm_weff(gpu_lib, shape, P):
     out, inp, m = shape
     say("gemm weff", shape, P)
