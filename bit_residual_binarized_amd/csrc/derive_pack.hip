@@ -48,31 +48,59 @@ __global__ __launch_bounds__(256) void k_derive_tile(
   __shared__ double scol[4][kTileCols];
   __shared__ uint32_t swords[2][NP > 0 ? NP : 1][64][4];  // [kg local][path - pb][row][word]
 
-  int cols[4];
+  // Every load below is issued unconditionally from a clamped index and
+  // masked afterwards: a load under a condition becomes a branch that waits
+  // for it, which left one row of loads in flight per wave.
+  int cols[4], cc[4];
   bool cval[4];
-  float h1f[4], h2f[4];
+  uint16_t hr1[4], hr2[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     cols[c] = col0 + l + 64 * c;
     cval[c] = cols[c] < in;
-    h1f[c] = (STAGE > 0 && cval[c]) ? f16_bits_to_f32(hh[cols[c]]) : 0.0f;
-    h2f[c] = (kB3 && cval[c]) ? f16_bits_to_f32(hh[in + cols[c]]) : 0.0f;
+    cc[c] = min(cols[c], in - 1);
+    hr1[c] = STAGE > 0 ? hh[cc[c]] : (uint16_t)0;
+    hr2[c] = kB3 ? hh[in + cc[c]] : (uint16_t)0;
+  }
+  // g of the wave's 16 rows: lane rr < 16 holds row 16 wv + rr (read per row
+  // with readlane)
+  const int grow = min(rt * kTileRows + wv * 16 + (l & 15), out - 1);
+  const uint32_t gr1 = STAGE > 0 ? gh[grow] : 0u;
+  const uint32_t gr2 = kB3 ? gh[out + grow] : 0u;
+  float h1f[4], h2f[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    h1f[c] = (STAGE > 0 && cval[c]) ? f16_bits_to_f32(hr1[c]) : 0.0f;
+    h2f[c] = (kB3 && cval[c]) ? f16_bits_to_f32(hr2[c]) : 0.0f;
   }
   double cp[4] = {0.0, 0.0, 0.0, 0.0};
 
-#pragma unroll 4
-  for (int rr = 0; rr < 16; ++rr) {
+  // rows in batches of kBatch: the batch's loads are all issued before its
+  // rows are processed (the per-row word writes are branches that the
+  // compiler does not move loads across)
+  constexpr int kBatch = 4;
+  for (int rb = 0; rb < 16; rb += kBatch) {
+  float wb[kBatch][4];
+#pragma unroll
+  for (int k = 0; k < kBatch; ++k) {
+    const int row = min(rt * kTileRows + wv * 16 + rb + k, out - 1);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) wb[k][c] = __builtin_nontemporal_load(W + (size_t)row * in + cc[c]);
+  }
+#pragma unroll
+  for (int k = 0; k < kBatch; ++k) {
+    const int rr = rb + k;
     const int rloc = wv * 16 + rr;
     const int row = rt * kTileRows + rloc;
     const bool rv = row < out;
-    const float* wrow = W + (size_t)(rv ? row : 0) * in;
-    const float g1f = (STAGE > 0 && rv) ? f16_bits_to_f32(gh[row]) : 0.0f;
-    const float g2f = (kB3 && rv) ? f16_bits_to_f32(gh[out + row]) : 0.0f;
+    const float g1f = (STAGE > 0 && rv) ? f16_bits_to_f32((uint16_t)__builtin_amdgcn_readlane(gr1, rr)) : 0.0f;
+    const float g2f = (kB3 && rv) ? f16_bits_to_f32((uint16_t)__builtin_amdgcn_readlane(gr2, rr)) : 0.0f;
+    const float* wv4 = wb[k];
     float a[4];
     bool b1[4], b2[4], b3[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const float v = (rv && cval[c]) ? __builtin_nontemporal_load(wrow + cols[c]) : 0.0f;
+      const float v = (rv && cval[c]) ? wv4[c] : 0.0f;
       b3[c] = false;
       if (STAGE > 0) {
         const float e = g1f * h1f[c];           // exact: fp16 x fp16 fits fp32
@@ -124,6 +152,7 @@ __global__ __launch_bounds__(256) void k_derive_tile(
       }
     }
   }
+  }
 
   if (SUMS) {
 #pragma unroll
@@ -155,7 +184,9 @@ __global__ __launch_bounds__(256) void k_derive_tile(
 }
 
 // Ordered reduction of the partials and rounding to fp16.
-__global__ __launch_bounds__(256) void k_finalize(const double* __restrict__ rowpart,
+// One wave per workgroup: the column sums read 8 B x (rows / 64) per thread,
+// and small workgroups spread those reads over many CUs.
+__global__ __launch_bounds__(64) void k_finalize(const double* __restrict__ rowpart,
                                                   const double* __restrict__ colpart, int out,
                                                   int in, int nct, int nrt,
                                                   uint16_t* __restrict__ g_out,
@@ -166,15 +197,17 @@ __global__ __launch_bounds__(256) void k_finalize(const double* __restrict__ row
   const double* p = row ? rowpart + t : colpart + (t - out);
   const int n = row ? nct : nrt;
   const size_t stride = row ? (size_t)out : (size_t)in;
-  // the tile partials are added strictly in order; the loads of 32 of them
-  // are in flight at a time (clamped index, masked)
+  // the tile partials are added strictly in order; the loads of 96 of them
+  // are in flight at a time (clamped index, masked): a 64-row tiling of an
+  // 11008-row layer has 172 column partials, two round trips
+  constexpr int kFly = 96;
   double s = 0.0;
-  for (int c0 = 0; c0 < n; c0 += 32) {
-    double v[32];
+  for (int c0 = 0; c0 < n; c0 += kFly) {
+    double v[kFly];
 #pragma unroll
-    for (int u = 0; u < 32; ++u) v[u] = p[(size_t)min(c0 + u, n - 1) * stride];
+    for (int u = 0; u < kFly; ++u) v[u] = p[(size_t)min(c0 + u, n - 1) * stride];
 #pragma unroll
-    for (int u = 0; u < 32; ++u) s += c0 + u < n ? v[u] : 0.0;
+    for (int u = 0; u < kFly; ++u) s += c0 + u < n ? v[u] : 0.0;
   }
   if (row)
     g_out[t] = f64_to_f16_rne(s / (double)in);
@@ -222,9 +255,9 @@ hipError_t launch_pack(const float* W, int out, int in, int P, bool meanabs, uin
   double* rowpart = (double*)ws;
   double* colpart = rowpart + (size_t)nct * out;
   const dim3 grid(nct, nrt), block(256);
-  const int fin_blocks = (out + in + 255) / 256;
+  const int fin_blocks = (out + in + 63) / 64;
   auto finalize = [&](int p) {
-    hipLaunchKernelGGL(k_finalize, dim3(fin_blocks), block, 0, st, rowpart, colpart, out, in, nct,
+    hipLaunchKernelGGL(k_finalize, dim3(fin_blocks), dim3(64), 0, st, rowpart, colpart, out, in, nct,
                        nrt, g + (size_t)p * out, h + (size_t)p * in);
   };
   if (meanabs) {
