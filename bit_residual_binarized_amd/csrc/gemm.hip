@@ -43,14 +43,31 @@ struct GemmWs {
 
 __host__ inline size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// split of K over grid.z: enough workgroups to fill the chip, at least four
-// 64-column steps per slice
+// split of K over grid.z (1..16 slices of at least four 64-column steps):
+// the z with the least modelled time, in units of one workgroup step. The
+// kernel takes ceil(z tiles / 512) rounds (two workgroups on each of 256 CUs)
+// of ceil(steps / z) steps plus about two for filling the ring and the
+// epilogue; a split adds the ordered reduce, which reads z and writes one
+// fp32 partial per output (about (z + 1) m out / 1.5e6 steps at 4 TB/s and
+// 1.5 us per step). Among equal kernel times the smallest z wins, so no
+// slice is ever empty.
 __host__ inline int split_k(int out, int in, int m, int bm, int bn = kBN) {
   const int Kp = col_groups(in) * 128;
-  const int tiles = ((out + bn - 1) / bn) * ((m + bm - 1) / bm);
-  int z = std::max(1, (512 + tiles - 1) / tiles);
-  z = std::min(z, std::max(1, Kp / (4 * kBK)));
-  return std::min(z, 16);
+  const int steps = Kp / kBK;
+  const long long tiles = (long long)((out + bn - 1) / bn) * ((m + bm - 1) / bm);
+  const int zmax = std::min(16, std::max(1, steps / 4));
+  int best = 1;
+  double best_cost = 0.0;
+  for (int z = 1; z <= zmax; ++z) {
+    const double rounds = (double)((z * tiles + 511) / 512);
+    double cost = rounds * (double)((steps + z - 1) / z + 2);
+    if (z > 1) cost += (double)(z + 1) * (double)m * (double)out / 1.5e6;
+    if (z == 1 || cost < best_cost) {
+      best = z;
+      best_cost = cost;
+    }
+  }
+  return best;
 }
 
 __host__ inline GemmWs carve(void* ws, int out, int in, int m, int P) {

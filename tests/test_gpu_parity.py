@@ -251,7 +251,7 @@ def test_gemv_partial_multi_equals_gemv(gpu_lib):
             assert torch.equal(y, gpu_lib.gemv(L, x))
 
 
-# (256, 4100, 64): 66 K steps over 16 split-K slices of 5, the last two empty
+# (256, 4100, 64): 66 K steps over 14 split-K slices of 5, the last one of a single step
 GEMM_CASES = [(64, 256, 1), (130, 1000, 37), (256, 4096, 512), (1024, 4096, 130), (300, 1100, 257),
               (256, 4100, 64)]
 
