@@ -475,20 +475,32 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint4* __restrict__ plane
   // no load may still write this workgroup's LDS when it ends
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
-  // epilogue: C[i][j] of a 16x16 tile: lane l, reg r -> row 4(l/16)+r, col l%16
+  // epilogue: C[i][j] of a 16x16 tile: lane l, reg r -> row 4(l/16)+r, col l%16.
+  // The scales and row exponents are all loaded first (clamped indices), so
+  // that no load waits behind a store's bounds check.
   const bool split = gridDim.z > 1;
+  uint16_t gq[NJ][P];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+#pragma unroll
+    for (int p = 0; p < P; ++p) gq[j][p] = g[(size_t)p * out + min(n0 + wn + 16 * j + (l & 15), out - 1)];
+  int rex[MT][4];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) rex[i][r] = split ? 0 : ws.rowexp[min(m0 + 16 * i + 4 * (l >> 4) + r, M - 1)];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int n = n0 + wn + 16 * j + (l & 15);
     if (n >= out) continue;
-    float g0 = f16_bits_to_f32(g[n]);
+    float g0 = f16_bits_to_f32(gq[j][0]);
     if (WEFF) {  // f[n] = max_p |g_p[n]|, as in the prologue
       g0 = fabsf(g0);
 #pragma unroll
-      for (int p = 1; p < P; ++p) g0 = fmaxf(g0, fabsf(f16_bits_to_f32(g[(size_t)p * out + n])));
+      for (int p = 1; p < P; ++p) g0 = fmaxf(g0, fabsf(f16_bits_to_f32(gq[j][p])));
     }
-    const float g1 = (!WEFF) ? f16_bits_to_f32(g[out + n]) : 0.f;
-    const float g2 = (!WEFF && P == 3) ? f16_bits_to_f32(g[2 * out + n]) : 0.f;
+    const float g1 = (!WEFF) ? f16_bits_to_f32(gq[j][P > 1 ? 1 : 0]) : 0.f;
+    const float g2 = (!WEFF && P == 3) ? f16_bits_to_f32(gq[j][P - 1]) : 0.f;
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
 #pragma unroll
@@ -501,7 +513,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint4* __restrict__ plane
         if (split) {
           ws.part[((size_t)blockIdx.z * M + m) * out + n] = v;
         } else {
-          const float y = ldexpf(v, -ws.rowexp[m]);
+          const float y = ldexpf(v, -rex[i][r]);
           if (y_dtype == RABIT_OUT_F32)
             ((float*)Y)[(size_t)m * out + n] = y;
           else
