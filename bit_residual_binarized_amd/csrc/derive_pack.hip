@@ -79,8 +79,10 @@ __global__ __launch_bounds__(256) void k_derive_tile(
   // rows are processed (the per-row word writes are branches that the
   // compiler does not move loads across)
   constexpr int kBatch = 4;
+#pragma unroll 1  // one batch of loads in registers at a time
   for (int rb = 0; rb < 16; rb += kBatch) {
   float wb[kBatch][4];
+  double lvb[kBatch];  // this lane's share (4 columns) of the batch's row sums
 #pragma unroll
   for (int k = 0; k < kBatch; ++k) {
     const int row = min(rt * kTileRows + wv * 16 + rb + k, out - 1);
@@ -123,11 +125,7 @@ __global__ __launch_bounds__(256) void k_derive_tile(
       lv += (double)a[1];
       lv += (double)a[2];
       lv += (double)a[3];
-      // halving tree: lane l and lane l^s form the same sum, so lane 0 ends
-      // with v[0] of the tree v[l] += v[l+s], s = 32..1
-#pragma unroll
-      for (int s = 32; s >= 1; s >>= 1) lv += __shfl_xor(lv, s, 64);
-      if (l == 0 && rv) rowpart[(size_t)ct * out + row] = lv;
+      lvb[k] = lv;
 #pragma unroll
       for (int c = 0; c < 4; ++c) cp[c] += (double)a[c];
     }
@@ -151,6 +149,27 @@ __global__ __launch_bounds__(256) void k_derive_tile(
         swords[k >> 2][q][rloc][k & 3] = myword;
       }
     }
+  }
+  if (SUMS) {
+    // The batch's 4 row sums over the 64 lanes by the halving tree
+    // v[l] += v[l + s], s = 32 .. 1, rows together: at s = 32 and 16 each lane
+    // keeps half of the rows it holds and adds the partner's share of them
+    // (the tree's two operands, in either order: IEEE addition commutes
+    // exactly); s = 8 .. 1 finish the one row left. Lane l ends with row
+    // 2 b5 + b4 of the batch (bits of l).
+    static_assert(kBatch == 4, "butterfly for four rows");
+    double t2[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const bool hi = l & 32;
+      t2[k] = (hi ? lvb[2 + k] : lvb[k]) + __shfl_xor(hi ? lvb[k] : lvb[2 + k], 32, 64);
+    }
+    const bool hi = l & 16;
+    double t1 = (hi ? t2[1] : t2[0]) + __shfl_xor(hi ? t2[0] : t2[1], 16, 64);
+#pragma unroll
+    for (int s = 8; s >= 1; s >>= 1) t1 += __shfl_xor(t1, s, 64);
+    const int row = rt * kTileRows + wv * 16 + rb + 2 * ((l >> 5) & 1) + ((l >> 4) & 1);
+    if ((l & 15) == 0 && row < out) rowpart[(size_t)ct * out + row] = t1;
   }
   }
 
