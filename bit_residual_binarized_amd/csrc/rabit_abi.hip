@@ -24,6 +24,11 @@ int check_dims(int64_t out, int64_t in) {
 }
 
 // layer header checks shared by every op that reads a packed layer
+// the prefill GEMM addresses a layer's planes with 32-bit buffer offsets
+bool gemm_planes_fit(const rabit_layer* L) {
+  return rabit_planes_bytes(L->out_features, L->in_features, L->n_paths) <= 0xFFFFFFFFull;
+}
+
 int check_layer(const rabit_layer* L) {
   if (!L) return RABIT_EINVAL;
   if (L->layout_version != RABIT_LAYOUT_V1) return RABIT_EINVAL;
@@ -222,6 +227,7 @@ int rabit_gemm_ex(const rabit_layer* L, const uint16_t* X, int32_t m, void* Y, i
   if (flags & ~RABIT_GEMM_WEFF) return RABIT_EINVAL;
   int s = check_layer(L);
   if (s) return s;
+  if (!gemm_planes_fit(L)) return RABIT_ESHAPE;
   if (!X || !Y) return RABIT_EINVAL;
   if (y_dtype != RABIT_OUT_F32 && y_dtype != RABIT_OUT_BF16) return RABIT_EINVAL;
   if (m < 1 || m > RABIT_MAX_GEMM_M) return RABIT_ESHAPE;
@@ -282,6 +288,7 @@ int rabit_grad_input_ex(const rabit_layer* L, const uint16_t* dY, int32_t m, voi
   if (flags & ~RABIT_GEMM_WEFF) return RABIT_EINVAL;
   int s = check_layer(L);
   if (s) return s;
+  if (!gemm_planes_fit(L)) return RABIT_ESHAPE;
   if (!dY || !dX) return RABIT_EINVAL;
   if (dx_dtype != RABIT_OUT_F32 && dx_dtype != RABIT_OUT_BF16) return RABIT_EINVAL;
   if (m < 1 || m > RABIT_MAX_GEMM_M) return RABIT_ESHAPE;

@@ -206,6 +206,8 @@ int rabit_gemv_partial_multi(const rabit_layer *layers, int32_t n, const uint16_
  * fp16); each X row is scaled by a power of two so that its largest |x| is
  * in [2^14, 2^15), rounded to fp16, and unscaled in the epilogue, where g_p
  * is applied in fp32.
+ * Errors: RABIT_ESHAPE also when the layer's planes take 4 GiB or more (the
+ * kernel addresses them with 32-bit offsets; rabit_grad_input likewise).
  */
 int rabit_gemm(const rabit_layer *layer, const uint16_t *X, int32_t m,
                void *Y, int32_t y_dtype, void *workspace, size_t workspace_bytes,

@@ -241,6 +241,21 @@ def test_svid_errors(lib):
     assert sv(P=3, wsb=16) == rabit.RABIT_EWORKSPACE
 
 
+def test_gemm_plane_size_limit(lib):
+    # 2^17 x 2^17 with two paths: 4 GiB of planes, beyond the GEMM's 32-bit
+    # offsets (the layer's buffers are placed apart so that only the size fails)
+    big = 1 << 17
+    L = fake_layer(out=big, inp=big, planes=FAKE, g=FAKE + (8 << 30), h=FAKE + (9 << 30))
+    X, Y, ws = FAKE + (10 << 30), FAKE + (11 << 30), FAKE + (12 << 30)
+    assert lib.rabit_planes_bytes(big, big, 2) == 1 << 32
+    assert lib.rabit_gemm(ctypes.byref(L), X, 8, Y, 0, ws, 1 << 40, None) == rabit.RABIT_ESHAPE
+    assert lib.rabit_gemm_ex(ctypes.byref(L), X, 8, Y, 0, 1, ws, 1 << 40, None) == rabit.RABIT_ESHAPE
+    assert lib.rabit_grad_input(ctypes.byref(L), X, 8, Y, 0, ws, 1 << 40, None) == rabit.RABIT_ESHAPE
+    # just below the limit the size check passes (the workspace check fails next)
+    L2 = fake_layer(out=big - 64, inp=big, planes=FAKE, g=FAKE + (8 << 30), h=FAKE + (9 << 30))
+    assert lib.rabit_gemm(ctypes.byref(L2), X, 8, Y, 0, ws, 16, None) == rabit.RABIT_EWORKSPACE
+
+
 def test_gemm_ex_flags(lib):
     L = fake_layer()
     X, Y, ws = FAKE + (3 << 30), FAKE + (4 << 30), FAKE + (5 << 30)
