@@ -383,9 +383,10 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint4* __restrict__ plane
     const uint32_t* a0 = S.a + fr * 32;
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
-      // one half's X fragments live at a time (two halves' did not fit the
-      // registers of two waves per SIMD with two paths)
-      if (sub) __builtin_amdgcn_sched_barrier(0);
+      // two paths: one half's X fragments live at a time (two halves' did
+      // not fit the registers of two waves per SIMD); three paths leave the
+      // scheduler free to overlap the halves
+      if (sub && P == 2) __builtin_amdgcn_sched_barrier(0);
       v8h fa[MT];
 #pragma unroll
       for (int i = 0; i < MT; ++i) fa[i] = *(const v8h*)(a0 + 512 * i + 4 * ((fg + 4 * sub) ^ xsw));
