@@ -105,9 +105,9 @@ __device__ __forceinline__ uint32_t f16_to_bits(float f) { return f32_to_f16_bit
 // One wave per row of X: row maximum, exponent, scaled fp16 copy. Lane l
 // handles 32-column blocks l, l + 64, ...: four 16-byte loads of bf16, then
 // the block's κ order (dword m = columns m, m + 16) in four 16-byte stores.
-__global__ __launch_bounds__(256) void k_gemm_prep_x(const uint16_t* __restrict__ X, int in, int Kp,
-                                                     int M, GemmWs ws) {
-  const int m = blockIdx.x * 4 + (threadIdx.x >> 6), l = threadIdx.x & 63;
+__device__ __forceinline__ void prep_x(const uint16_t* __restrict__ X, int in, int Kp, int M, GemmWs ws,
+                                       int blk) {
+  const int m = blk * 4 + (threadIdx.x >> 6), l = threadIdx.x & 63;
   if (m >= M) return;
   const uint16_t* xr = X + (size_t)m * in;
   const int nblk = Kp / 32;
@@ -163,8 +163,10 @@ __global__ __launch_bounds__(256) void k_gemm_prep_x(const uint16_t* __restrict_
   if (l == 0) ws.rowexp[m] = e;
 }
 
-__global__ void k_gemm_prep_h(const uint16_t* __restrict__ h, int in, int Kp, int P, GemmWs ws) {
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;  // (p, blk, pair)
+// h pairs (h[32 b + m], h[32 b + m + 16]) of every path and 32-column block
+__device__ __forceinline__ void prep_h(const uint16_t* __restrict__ h, int in, int Kp, int P, GemmWs ws,
+                                       int wg) {
+  const int idx = wg * 256 + threadIdx.x;  // (p, blk, pair)
   const int nb = Kp / 32;
   if (idx >= P * nb * 16) return;
   const int pr = idx & 15, blk = (idx >> 4) % nb, p = idx / (16 * nb);
@@ -172,6 +174,16 @@ __global__ void k_gemm_prep_h(const uint16_t* __restrict__ h, int in, int Kp, in
   const uint32_t lo = c0 < in ? h[(size_t)p * in + c0] : 0;
   const uint32_t hi = c1 < in ? h[(size_t)p * in + c1] : 0;
   ws.hpairs[idx] = lo | (hi << 16);
+}
+
+// The two preparations of a call in one launch: workgroups [0, nbx) take the
+// X rows (four per workgroup), the rest the h pairs (256 per workgroup).
+__global__ __launch_bounds__(256) void k_gemm_prep(const uint16_t* __restrict__ X, const uint16_t* __restrict__ h,
+                                                   int in, int Kp, int M, int P, int nbx, GemmWs ws) {
+  if ((int)blockIdx.x < nbx)
+    prep_x(X, in, Kp, M, ws, blockIdx.x);
+  else
+    prep_h(h, in, Kp, P, ws, blockIdx.x - nbx);
 }
 
 // Raw (untyped, unswizzled) buffer resource word 3.
@@ -549,9 +561,8 @@ hipError_t launch_gemm(const uint4* planes, const uint16_t* g, const uint16_t* h
   if (paths != 2 && paths != 3) return hipErrorInvalidValue;
   const int Kp = col_groups(in) * 128;
   GemmWs w = carve(ws, out, in, m, paths);
-  hipLaunchKernelGGL(k_gemm_prep_x, dim3((m + 3) / 4), dim3(256), 0, st, X, in, Kp, m, w);
-  const int nh = paths * (Kp / 32) * 16;
-  hipLaunchKernelGGL(k_gemm_prep_h, dim3((nh + 255) / 256), dim3(256), 0, st, h, in, Kp, paths, w);
+  const int nbx = (m + 3) / 4, nh = paths * (Kp / 32) * 16;
+  hipLaunchKernelGGL(k_gemm_prep, dim3(nbx + (nh + 255) / 256), dim3(256), 0, st, X, h, in, Kp, m, paths, nbx, w);
   const int bm = weff ? 128 : bm_of(paths), bn = bn_of(paths, weff);
   const int Z = split_k(out, in, m, bm, bn);
   const int steps = Kp / kBK;
