@@ -29,6 +29,11 @@ constexpr int kBN = 128, kBK = 64;
 // token rows per workgroup: 128 with two paths; 64 with three (the third
 // accumulator set would not fit the registers of two waves per SIMD)
 __host__ __device__ constexpr int bm_of(int P) { return P == 2 ? 128 : 64; }
+// Small token counts (decode batches, M <= 32): 32-row token tiles and 256
+// output columns per workgroup (64 per wave), K split up to 32 ways. The
+// ±h fragments are built once per weight whatever M, so a 128-row tile
+// would spend the same fragment work on at most a quarter of its rows.
+constexpr int kSmallM = 32, kSmallBM = 32, kSmallBN = 256, kSmallZcap = 32;
 // output columns per workgroup: 128 on the exact path; 256 on the
 // effective-weight path with two paths, 128 with three (the three ratio
 // registers per fragment column would spill with four fragments per wave)
@@ -51,11 +56,11 @@ __host__ inline size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 // fp32 partial per output (about (z + 1) m out / 1.5e6 steps at 4 TB/s and
 // 1.5 us per step). Among equal kernel times the smallest z wins, so no
 // slice is ever empty.
-__host__ inline int split_k(int out, int in, int m, int bm, int bn = kBN) {
+__host__ inline int split_k(int out, int in, int m, int bm, int bn = kBN, int zcap = 16) {
   const int Kp = col_groups(in) * 128;
   const int steps = Kp / kBK;
   const long long tiles = (long long)((out + bn - 1) / bn) * ((m + bm - 1) / bm);
-  const int zmax = std::min(16, std::max(1, steps / 4));
+  const int zmax = std::min(zcap, std::max(1, steps / 4));
   int best = 1;
   double best_cost = 0.0;
   for (int z = 1; z <= zmax; ++z) {
@@ -87,7 +92,8 @@ __host__ inline GemmWs carve(void* ws, int out, int in, int m, int P) {
 __host__ inline size_t ws_bytes_p(int out, int in, int m, int P) {
   const size_t Kp = (size_t)col_groups(in) * 128;
   // the exact path's tiles (bm_of(P) rows) or the effective-weight path's (128)
-  const int z = std::max(split_k(out, in, m, bm_of(P)), split_k(out, in, m, 128, bn_of(P, true)));
+  int z = std::max(split_k(out, in, m, bm_of(P)), split_k(out, in, m, 128, bn_of(P, true)));
+  if (m <= kSmallM) z = std::max(z, split_k(out, in, m, kSmallBM, kSmallBN, kSmallZcap));
   return a256((size_t)m * Kp * 2) + a256((size_t)m * 4) + a256((size_t)P * (Kp / 32) * 16 * 4) +
          (z > 1 ? a256((size_t)z * m * out * 4) : 0);
 }
@@ -250,12 +256,13 @@ __host__ __device__ constexpr int n_stages(int BM, int BN, int P) {
 // e = Σ_p r_p (±h_p) by packed fp16 multiply-adds (path order) and f[n] is
 // applied in the epilogue. One accumulator set; 128-row tiles of 256 output
 // columns with two paths (64 per wave) and 128 with three (32 per wave).
-template <int P, bool WEFF>
+template <int P, bool WEFF, bool SMALL = false>
 __global__ __launch_bounds__(256, 2) void k_gemm(const uint4* __restrict__ planes,
                                               const uint16_t* __restrict__ g, int out, int M,
                                               int Kp, int ksteps, GemmWs ws, void* Y, int y_dtype) {
-  constexpr int kBM = WEFF ? 128 : bm_of(P), MT = kBM / 16;  // 16-row matrix tiles per wave
-  constexpr int kBNt = bn_of(P, WEFF);
+  static_assert(!(SMALL && WEFF), "the small-M tiles are for the exact path");
+  constexpr int kBM = SMALL ? kSmallBM : WEFF ? 128 : bm_of(P), MT = kBM / 16;  // 16-row tiles per wave
+  constexpr int kBNt = SMALL ? kSmallBN : bn_of(P, WEFF);
   constexpr int NA = WEFF ? 1 : P;  // accumulator sets
   constexpr int NJ = kBNt / 64;     // 16-column fragments per wave
   constexpr int NS = n_stages(kBM, kBNt, P);
@@ -398,7 +405,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm(const uint4* __restrict__ plane
       // two paths: one half's X fragments live at a time (two halves' did
       // not fit the registers of two waves per SIMD); three paths leave the
       // scheduler free to overlap the halves
-      if (sub && P == 2) __builtin_amdgcn_sched_barrier(0);
+      if (sub && P == 2 && !SMALL) __builtin_amdgcn_sched_barrier(0);
       v8h fa[MT];
 #pragma unroll
       for (int i = 0; i < MT; ++i) fa[i] = *(const v8h*)(a0 + 512 * i + 4 * ((fg + 4 * sub) ^ xsw));
@@ -563,13 +570,14 @@ hipError_t launch_gemm(const uint4* planes, const uint16_t* g, const uint16_t* h
   GemmWs w = carve(ws, out, in, m, paths);
   const int nbx = (m + 3) / 4, nh = paths * (Kp / 32) * 16;
   hipLaunchKernelGGL(k_gemm_prep, dim3(nbx + (nh + 255) / 256), dim3(256), 0, st, X, h, in, Kp, m, paths, nbx, w);
-  const int bm = weff ? 128 : bm_of(paths), bn = bn_of(paths, weff);
-  const int Z = split_k(out, in, m, bm, bn);
+  const bool small = !weff && m <= kSmallM;
+  const int bm = small ? kSmallBM : weff ? 128 : bm_of(paths), bn = small ? kSmallBN : bn_of(paths, weff);
+  const int Z = small ? split_k(out, in, m, bm, bn, kSmallZcap) : split_k(out, in, m, bm, bn);
   const int steps = Kp / kBK;
   const int per = (steps + Z - 1) / Z;
   const dim3 grid((out + bn - 1) / bn, (m + bm - 1) / bm, Z);
-  auto kern = paths == 3 ? (weff ? k_gemm<3, true> : k_gemm<3, false>)
-                         : (weff ? k_gemm<2, true> : k_gemm<2, false>);
+  auto kern = paths == 3 ? (weff ? k_gemm<3, true> : small ? k_gemm<3, false, true> : k_gemm<3, false>)
+                         : (weff ? k_gemm<2, true> : small ? k_gemm<2, false, true> : k_gemm<2, false>);
   hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, planes, g, out, m, Kp, per, w, Y, y_dtype);
   if (Z > 1) {
     const size_t n = (size_t)m * out;

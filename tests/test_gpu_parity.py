@@ -252,8 +252,10 @@ def test_gemv_partial_multi_equals_gemv(gpu_lib):
 
 
 # (256, 4100, 64): 66 K steps over 14 split-K slices of 5, the last one of a single step
+# M <= 32 takes the small-token tiles: (256, 14336, 16) splits K 32 ways,
+# (300, 1100, 31) is ragged in every dimension
 GEMM_CASES = [(64, 256, 1), (130, 1000, 37), (256, 4096, 512), (1024, 4096, 130), (300, 1100, 257),
-              (256, 4100, 64)]
+              (256, 4100, 64), (1024, 4096, 8), (256, 14336, 16), (300, 1100, 31), (4096, 1024, 32)]
 
 
 @pytest.mark.parametrize("case", GEMM_CASES)

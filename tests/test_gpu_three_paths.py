@@ -227,7 +227,7 @@ def test_mixed_path_counts_are_rejected(gpu_lib):
 
 # (256, 4100, 64): 66 K steps over 14 split-K slices of 5, the last one of a single step
 @pytest.mark.parametrize("case", [(256, 512, 64), (300, 1000, 100), (1024, 4096, 200), (4096, 4096, 512),
-                                  (100, 300, 1), (256, 4100, 64)])
+                                  (100, 300, 1), (256, 4100, 64), (1024, 4096, 16), (300, 1100, 31)])
 def test_gemm3(gpu_lib, case):
     out, inp, m = case
     say("gemm 3 paths", case)
