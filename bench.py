@@ -224,8 +224,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build measures one GPU only; the multi-GPU split is a design "
-              "(DESIGN.md, 'Sharding'), run with --gpus 1", file=sys.stderr)
+        print("bench.py: measures one GPU; the multi-GPU split is not run here, use --gpus 1",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch

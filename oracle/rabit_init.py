@@ -16,7 +16,7 @@ Accurate and Efficient LLMs"):
   decomposition runs on W' = s_out^a_out ⊙ W_FP ⊙ s_in^a_in and the scales are
   mapped back with g_i = s_out^-a_out ⊙ g_i', h_i = s_in^-a_in ⊙ h_i'.
 
-Readings (listed in DESIGN.md):
+Readings:
 
 * SVID (not defined on the pages; the pages cite OneBit for it): B = sign(R)
   (+1 unless R < 0) and g hᵀ the best rank-1 approximation of |R| in the

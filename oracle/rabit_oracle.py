@@ -18,7 +18,7 @@ Accurate and Efficient LLMs", arXiv 2602.05367):
 * paper App. E.1 "Weight Packing": 32 columns per uint32, +1 -> 0, -1 -> 1
 * paper §5.4: inference is additions plus element-wise scaling
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
 
 * sign(v) is +1 unless v < 0 (so +0, -0 and NaN give +1; bit = 1 iff v < 0).
 * Bit t of word k holds column 32k + t (LSB first); padding bits are 0.

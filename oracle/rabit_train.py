@@ -17,8 +17,7 @@ Accurate and Efficient LLMs"):
 * paper §4.2 last paragraph and §5.4: inference (and the gradient to the
   layer input) uses the same effective weight.
 
-Readings (the formulas of both items are missing from the pages' text; each
-reading is listed in DESIGN.md):
+Readings (the formulas of both items are missing from the pages' text):
 
 * The loss gradient at the layer output is dY [N][d_out] (row n = sample n);
   the layer computes Y = X W_hatᵀ (X is [N][d_in], the inference convention

@@ -1,6 +1,6 @@
 """GPU parity: the HIP path through the C ABI against the CPU oracle.
 
-Bars (see DESIGN.md "Tolerances"): packed words and fp16 scales bit-exact;
+Bars: packed words and fp16 scales bit-exact;
 GEMV/GEMM/decode outputs within a normwise relative error of 2e-3 per batch
 row (max_i |y - ŷ| / max_i |ŷ|); unit-vector probes bit-exact.
 """
