@@ -218,7 +218,7 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of graph replay")
     ap.add_argument("--workload", default="mlp7b",
                     choices=["mlp7b", "layer4096", "llama3-8b", "gemm", "llama70b", "table7", "train",
-                             "init"],
+                             "init", "crossover"],
                     help="mlp7b (default): the headline decode workload; the others measure the "
                          "remaining configurations (one JSON line each)")
     args = ap.parse_args()
@@ -237,7 +237,7 @@ def main():
     if args.workload != "mlp7b":
         extra = {"layer4096": bench_layer4096, "llama3-8b": bench_llama3_8b, "gemm": bench_gemm,
                  "llama70b": bench_llama70b, "table7": bench_table7,
-                 "train": bench_train, "init": bench_init}[args.workload]
+                 "train": bench_train, "init": bench_init, "crossover": bench_crossover}[args.workload]
         print(json.dumps(extra(args, rabit, torch)), flush=True)
         return
     hidden, ffn = 4096, 11008
@@ -542,6 +542,44 @@ def bench_table7(args, rabit, torch):
     return _line("Residual-binary GEMV speed-up over dense bf16 GEMV, batch 1, cold (geometric mean over the "
                  "pages' 7B/13B shapes)", round(gm, 3), "x", {"workload": "table7-shapes-b1"},
                  dtype="fp4xfp6 vs bf16", runs=runs)
+
+
+def bench_crossover(args, rabit, torch):
+    """The GEMV (rabit_gemv) against the prefill GEMM (rabit_gemm, small-token
+    tiles up to M = 32) at batch / M = 2 .. 32 on the Llama-3-8B layer shapes:
+    microseconds per call, four calls per graph replay. The value is the
+    smallest batch from which the GEMM is faster on every MLP shape."""
+    from synth.inputs import act_bf16, seed_w, seed_x
+    shapes = [(14336, 4096, "gate/up"), (4096, 14336, "down"), (4096, 4096, "q/o"), (1024, 4096, "k/v")]
+    batches = (2, 4, 8, 16, 32)
+    runs, wsh = {}, [None]
+    first = {}
+    for si, (out, inp, name) in enumerate(shapes):
+        pl, _ = _pack_layer(rabit, torch, out, inp, seed_w(7, si, "q"), wsh)
+        row = {}
+        for b in batches:
+            x = act_bf16(b, inp, seed_x(7, b)).cuda()
+            y = torch.empty(b, out, device="cuda")
+            wsv, wsm = rabit.gemv_workspace(pl, b), rabit.gemm_workspace(pl, b)
+
+            def gv():
+                for _ in range(4):
+                    rabit.gemv(pl, x, y=y, workspace=wsv)
+
+            def gm():
+                for _ in range(4):
+                    rabit.gemm(pl, x, y=y, workspace=wsm)
+            tv = graph_ms(torch, gv, 20) * 1e3 / 4
+            tm = graph_ms(torch, gm, 20) * 1e3 / 4
+            row[str(b)] = {"gemv_us": round(tv, 1), "gemm_us": round(tm, 1), "gemv_over_gemm": round(tv / tm, 2)}
+            if tm < tv and name in ("gate/up", "down"):
+                first.setdefault(name, b)
+            log(f"crossover {name} {out}x{inp} batch {b}: gemv {tv:.1f} us, gemm {tm:.1f} us")
+        runs[f"{out}x{inp} {name}"] = row
+    value = max(first.values()) if len(first) == 2 else None
+    return _line("Smallest batch from which the prefill GEMM beats the GEMV on the Llama-3-8B MLP shapes",
+                 value, "batch", {"workload": "llama3-8b-shapes-gemv-vs-gemm", "batches": list(batches)},
+                 higher=False, dtype="fp4xfp6 vs fp16", runs=runs)
 
 
 def _decoder_layers(rabit, torch, cfg_id, H, F, kv, n_layers):
