@@ -46,6 +46,13 @@ int check_layer(const rabit_layer* L) {
   return RABIT_OK;
 }
 
+// does [p, p + n) overlap any buffer of the layer (every path's plane, g and h)?
+bool overlaps_layer(const void* p, size_t n, const rabit_layer* L) {
+  const int P = L->n_paths, out = L->out_features, in = L->in_features;
+  return overlap(p, n, L->planes, rabit_planes_bytes(out, in, P)) ||
+         overlap(p, n, L->g, (size_t)2 * P * out) || overlap(p, n, L->h, (size_t)2 * P * in);
+}
+
 }  // namespace
 
 extern "C" {
@@ -138,8 +145,7 @@ int check_gemv_y(const rabit_layer* L, int32_t batch, void* y, int32_t y_dtype, 
   if (!aligned16(y)) return RABIT_EALIGN;
   const int out = L->out_features, in = L->in_features;
   const size_t yb = (size_t)batch * out * (y_dtype == RABIT_OUT_F32 ? 4 : 2);
-  if ((x && overlap(y, yb, x, (size_t)batch * in * 2)) ||
-      overlap(y, yb, L->planes, rabit_planes_bytes(out, in, 2)))
+  if ((x && overlap(y, yb, x, (size_t)batch * in * 2)) || overlaps_layer(y, yb, L))
     return RABIT_EINVAL;
   return RABIT_OK;
 }
@@ -157,7 +163,7 @@ int rabit_gemv(const rabit_layer* L, const uint16_t* x, int32_t batch, void* y, 
   const size_t wsb = gemv_workspace_bytes(L->out_features, L->in_features, batch);
   const size_t yb = (size_t)batch * L->out_features * (y_dtype == RABIT_OUT_F32 ? 4 : 2);
   if (overlap(workspace, wsb, x, (size_t)batch * L->in_features * 2) ||
-      overlap(workspace, wsb, y, yb))
+      overlap(workspace, wsb, y, yb) || overlaps_layer(workspace, wsb, L))
     return RABIT_EINVAL;
   return dev_status(launch_gemv((const uint4*)L->planes, L->g, L->h, L->out_features,
                                 L->in_features, x, batch, y, y_dtype, workspace,
@@ -170,7 +176,9 @@ int rabit_gemv_partial(const rabit_layer* L, const uint16_t* x, int32_t batch, v
   if (s) return s;
   if ((s = check_gemv_x(L, x))) return s;
   const size_t wsb = gemv_workspace_bytes(L->out_features, L->in_features, batch);
-  if (overlap(workspace, wsb, x, (size_t)batch * L->in_features * 2)) return RABIT_EINVAL;
+  if (overlap(workspace, wsb, x, (size_t)batch * L->in_features * 2) ||
+      overlaps_layer(workspace, wsb, L))
+    return RABIT_EINVAL;
   return dev_status(launch_gemv_partial((const uint4*)L->planes, L->g, L->h, L->out_features,
                                         L->in_features, x, batch, workspace, (hipStream_t)stream,
                                         L->n_paths));
@@ -198,10 +206,7 @@ int rabit_gemv_partial_multi(const rabit_layer* Ls, int32_t n, const uint16_t* x
   if (!aligned16(workspace)) return RABIT_EALIGN;
   if (overlap(workspace, off, x, (size_t)batch * in * 2)) return RABIT_EINVAL;
   for (int i = 0; i < n; ++i)
-    if (overlap(workspace, off, Ls[i].planes, rabit_planes_bytes(Ls[i].out_features, in, 2)) ||
-        overlap(workspace, off, Ls[i].g, (size_t)4 * Ls[i].out_features) ||
-        overlap(workspace, off, Ls[i].h, (size_t)4 * in))
-      return RABIT_EINVAL;
+    if (overlaps_layer(workspace, off, &Ls[i])) return RABIT_EINVAL;
   return dev_status(launch_gemv_multi(segs, n, in, x, batch, nullptr, 0.f, (hipStream_t)stream));
 }
 
@@ -211,8 +216,8 @@ int rabit_gemv_reduce(const rabit_layer* L, int32_t batch, void* y, int32_t y_dt
   if (s) return s;
   if ((s = check_gemv_y(L, batch, y, y_dtype, nullptr))) return s;
   const size_t yb = (size_t)batch * L->out_features * (y_dtype == RABIT_OUT_F32 ? 4 : 2);
-  if (overlap(workspace, gemv_workspace_bytes(L->out_features, L->in_features, batch), y, yb))
-    return RABIT_EINVAL;
+  const size_t wsb = gemv_workspace_bytes(L->out_features, L->in_features, batch);
+  if (overlap(workspace, wsb, y, yb) || overlaps_layer(workspace, wsb, L)) return RABIT_EINVAL;
   return dev_status(launch_gemv_reduce(L->out_features, L->in_features, batch, y, y_dtype,
                                        workspace, (hipStream_t)stream));
 }
@@ -247,15 +252,6 @@ int rabit_gemm_ex(const rabit_layer* L, const uint16_t* X, int32_t m, void* Y, i
 // --------------------------------------------------------------------------
 // training side
 // --------------------------------------------------------------------------
-namespace {
-// does [p, p + n) overlap any buffer of the layer?
-bool overlaps_layer(const void* p, size_t n, const rabit_layer* L) {
-  const int P = L->n_paths, out = L->out_features, in = L->in_features;
-  return overlap(p, n, L->planes, rabit_planes_bytes(out, in, P)) ||
-         overlap(p, n, L->g, (size_t)2 * P * out) || overlap(p, n, L->h, (size_t)2 * P * in);
-}
-}  // namespace
-
 size_t rabit_grad_input_workspace_bytes(int32_t out, int32_t in, int32_t m) {
   if (check_dims(out, in) || m < 1 || m > RABIT_MAX_GEMM_M) return 0;
   return std::max(grad_input_workspace_bytes(out, in, m, 2), grad_input_workspace_bytes(out, in, m, 3));

@@ -38,9 +38,10 @@ Readings where the pages are silent:
 Pins (tests/test_oracle_*.py): brute-force argmin on 4x8 with Fraction (B_1,
 B_2), closed-form flip rule and flip statistic (B_2), Fraction means and an
 independent Fraction RNE (scales, fp16/bf16 rounding), exact rational sums on
-dyadic data and fsum bounds (canonical sums), L750-style word patterns and
-round trips (pack, device layout), two formulations agreeing exactly in
-Fraction (GEMV), unit-vector probes, the residual-norm identity (P7), and
+dyadic data and fsum bounds (canonical sums), word patterns that follow from
+the +1 -> 0, -1 -> 1 mapping of App. E.1 "Weight Packing" (all +1, all -1,
+alternating) and round trips (pack, device layout), two formulations agreeing exactly in
+Fraction (GEMV), unit-vector probes, the residual-norm identity, and
 closed forms for the decode glue ops.
 """
 from __future__ import annotations

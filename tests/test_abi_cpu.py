@@ -263,3 +263,36 @@ def test_gemm_ex_flags(lib):
     assert lib.rabit_gemm_ex(ctypes.byref(L), X, 0, Y, 0, 1, ws, 1 << 30, None) == rabit.RABIT_ESHAPE
     assert lib.rabit_grad_input_ex(ctypes.byref(L), X, 8, Y, 0, 4, ws, 1 << 30, None) == rabit.RABIT_EINVAL
     assert lib.rabit_grad_input_ex(ctypes.byref(L), X, 8, Y, 0, 1, ws, 16, None) == rabit.RABIT_EWORKSPACE
+
+
+def test_three_path_layer_aliasing(lib):
+    # A 3-path layer's third plane, g_3 and h_3 lie beyond what a 2-path layer
+    # of the same shape occupies; outputs and workspaces that overlap only
+    # them must still be rejected.
+    out, inp = 256, 512
+    pb2, pb3 = lib.rabit_planes_bytes(out, inp, 2), lib.rabit_planes_bytes(out, inp, 3)
+    assert pb3 > pb2
+    G, H = FAKE + (1 << 30), FAKE + (2 << 30)
+    L3 = fake_layer(out, inp, paths=3, planes=FAKE, g=G, h=H)
+    third_plane = FAKE + (pb2 + pb3) // 2 // 16 * 16
+    g3 = G + 2 * 2 * out          # g of path 3
+    h3 = H + 2 * 2 * inp          # h of path 3
+    x, ws = FAKE + (3 << 30), FAKE + (5 << 30)
+    big = 1 << 30
+    # rabit_gemv: y or the workspace on the third plane, g_3 or h_3
+    for y in (third_plane, g3, h3):
+        assert gemv(lib, L3, y=y) == rabit.RABIT_EINVAL, hex(y)
+        assert gemv(lib, L3, ws=y) == rabit.RABIT_EINVAL, hex(y)
+    # rabit_gemv_partial: the workspace on any of them
+    for w in (third_plane, g3, h3):
+        assert lib.rabit_gemv_partial(ctypes.byref(L3), x, 1, w, big, None) == rabit.RABIT_EINVAL
+    # rabit_gemv_reduce: y or the workspace on any of them
+    for p in (third_plane, g3, h3):
+        assert lib.rabit_gemv_reduce(ctypes.byref(L3), 1, p, 0, ws, big, None) == rabit.RABIT_EINVAL
+        assert lib.rabit_gemv_reduce(ctypes.byref(L3), 1, FAKE + (4 << 30), 0, p, big, None) == \
+            rabit.RABIT_EINVAL
+    # rabit_gemv_partial_multi: the workspace on the second layer's third plane or scales
+    a = fake_layer(out, inp, paths=3, planes=FAKE + (6 << 30), g=FAKE + (7 << 30), h=FAKE + (8 << 30))
+    for w in (third_plane, g3, h3):
+        arr = (rabit.RabitLayerC * 2)(a, L3)
+        assert lib.rabit_gemv_partial_multi(arr, 2, x, 1, w, big, None) == rabit.RABIT_EINVAL
