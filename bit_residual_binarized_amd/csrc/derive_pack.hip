@@ -205,11 +205,14 @@ __global__ __launch_bounds__(256) void k_derive_tile(
 // Ordered reduction of the partials and rounding to fp16.
 // One wave per workgroup: the column sums read 8 B x (rows / 64) per thread,
 // and small workgroups spread those reads over many CUs.
+// With tot != nullptr (normalized scales) the totals are also written to
+// tot[0 .. out + in) and h is left to k_norm_h.
 __global__ __launch_bounds__(64) void k_finalize(const double* __restrict__ rowpart,
                                                   const double* __restrict__ colpart, int out,
                                                   int in, int nct, int nrt,
                                                   uint16_t* __restrict__ g_out,
-                                                  uint16_t* __restrict__ h_out) {
+                                                  uint16_t* __restrict__ h_out,
+                                                  double* __restrict__ tot) {
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= out + in) return;
   const bool row = t < out;
@@ -230,8 +233,41 @@ __global__ __launch_bounds__(64) void k_finalize(const double* __restrict__ rowp
   }
   if (row)
     g_out[t] = f64_to_f16_rne(s / (double)in);
-  else
+  else if (!tot)
     h_out[t - out] = f64_to_f16_rne(s / (double)out);
+  if (tot) tot[t] = s;  // normalized scales: row then column totals for k_norm_h
+}
+
+// Normalized scales: h[j] = fp16((S_col[j] / out) / mu) with mu = T / (out in)
+// and T the canonical total of the row sums: lane l of one wave sums rows l,
+// l + 64, ... in ascending order, then the halving tree v[l] += v[l + s],
+// s = 32 .. 1 (a xor butterfly leaves the tree's value in lane 0). Every
+// workgroup computes T the same way and then its 1024 columns.
+__global__ __launch_bounds__(256) void k_norm_h(const double* __restrict__ tot, int out, int in,
+                                                uint16_t* __restrict__ h_out) {
+  __shared__ double s_mu;
+  if (threadIdx.x < 64) {
+    const int l = threadIdx.x;
+    double v = 0.0;
+    constexpr int kFly = 8;
+    for (int r0 = l; r0 < out; r0 += 64 * kFly) {
+      double t[kFly];
+#pragma unroll
+      for (int u = 0; u < kFly; ++u) t[u] = tot[min(r0 + 64 * u, out - 1)];
+#pragma unroll
+      for (int u = 0; u < kFly; ++u) v += r0 + 64 * u < out ? t[u] : 0.0;
+    }
+#pragma unroll
+    for (int sh = 32; sh >= 1; sh >>= 1) v += __shfl_xor(v, sh, 64);
+    if (l == 0) s_mu = v / ((double)out * (double)in);
+  }
+  __syncthreads();
+  const double mu = s_mu;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int j = blockIdx.x * 1024 + k * 256 + threadIdx.x;
+    if (j < in) h_out[j] = mu != 0.0 ? f64_to_f16_rne((tot[out + j] / (double)out) / mu) : (uint16_t)0;
+  }
 }
 
 // Device layout -> canonical words (test hook).
@@ -262,22 +298,27 @@ __global__ void k_test_f64_to_16(const double* __restrict__ in, uint16_t* __rest
 size_t pack_workspace_bytes(int out, int in) {
   const size_t nct = (size_t)(in + kTileCols - 1) / kTileCols;
   const size_t nrt = (size_t)(out + kTileRows - 1) / kTileRows;
-  return (nct * out + nrt * in) * sizeof(double);
+  // tile partials, then the row and column totals (normalized scales)
+  return (nct * out + nrt * in + (size_t)out + in) * sizeof(double);
 }
 
 hipError_t launch_pack(const float* W, int out, int in, int P, bool meanabs, uint16_t* g,
-                       uint16_t* h, uint4* planes, void* ws, hipStream_t st) {
+                       uint16_t* h, uint4* planes, void* ws, hipStream_t st, bool normalized) {
   if (P != 2 && P != 3) return hipErrorInvalidValue;
   const int nct = (in + kTileCols - 1) / kTileCols;
   const int nrt = (out + kTileRows - 1) / kTileRows;
   const int KG = col_groups(in);
   double* rowpart = (double*)ws;
   double* colpart = rowpart + (size_t)nct * out;
+  double* tot = normalized ? colpart + (size_t)nrt * in : nullptr;
   const dim3 grid(nct, nrt), block(256);
   const int fin_blocks = (out + in + 63) / 64;
   auto finalize = [&](int p) {
     hipLaunchKernelGGL(k_finalize, dim3(fin_blocks), dim3(64), 0, st, rowpart, colpart, out, in, nct,
-                       nrt, g + (size_t)p * out, h + (size_t)p * in);
+                       nrt, g + (size_t)p * out, h + (size_t)p * in, tot);
+    if (normalized)
+      hipLaunchKernelGGL(k_norm_h, dim3((in + 1023) / 1024), dim3(256), 0, st, tot, out, in,
+                         h + (size_t)p * in);
   };
   if (meanabs) {
     hipLaunchKernelGGL((k_derive_tile<0, true, 2>), grid, block, 0, st, W, out, in, nullptr,

@@ -95,7 +95,9 @@ size_t rabit_gemm_workspace_bytes(int32_t out, int32_t in, int32_t m) {
 int rabit_pack(const float* W, uint32_t scale_mode, const rabit_layer* L, void* workspace,
                size_t workspace_bytes, void* stream) {
   if (!L || !W) return RABIT_EINVAL;
-  if (scale_mode != RABIT_SCALES_GIVEN && scale_mode != RABIT_SCALES_MEANABS) return RABIT_EINVAL;
+  if (scale_mode != RABIT_SCALES_GIVEN && scale_mode != RABIT_SCALES_MEANABS &&
+      scale_mode != RABIT_SCALES_MEANABS_NORMALIZED)
+    return RABIT_EINVAL;
   int s = check_layer(L);
   if (s) return s;
   if (!aligned16(W)) return RABIT_EALIGN;
@@ -104,14 +106,14 @@ int rabit_pack(const float* W, uint32_t scale_mode, const rabit_layer* L, void* 
   if (overlap(W, wb, L->planes, rabit_planes_bytes(out, in, P)) ||
       overlap(W, wb, L->g, (size_t)2 * P * out) || overlap(W, wb, L->h, (size_t)2 * P * in))
     return RABIT_EINVAL;
-  const bool meanabs = scale_mode == RABIT_SCALES_MEANABS;
+  const bool meanabs = scale_mode != RABIT_SCALES_GIVEN;
   if (meanabs) {
     if (!workspace) return RABIT_EWORKSPACE;
     if (workspace_bytes < pack_workspace_bytes(out, in)) return RABIT_EWORKSPACE;
     if (!aligned16(workspace)) return RABIT_EALIGN;
   }
   return dev_status(launch_pack(W, out, in, P, meanabs, L->g, L->h, (uint4*)L->planes, workspace,
-                                (hipStream_t)stream));
+                                (hipStream_t)stream, scale_mode == RABIT_SCALES_MEANABS_NORMALIZED));
 }
 
 int rabit_unpack(const rabit_layer* L, uint32_t* words, void* stream) {

@@ -167,8 +167,9 @@ __host__ __device__ __forceinline__ size_t unit_index(int rg, int kg, int p, int
 // Host-side launchers (each returns hipSuccess or the launch error)
 // ---------------------------------------------------------------------------
 size_t pack_workspace_bytes(int out, int in);
+// normalized (with meanabs): h divided by the global mean |.| of the matrix
 hipError_t launch_pack(const float* W, int out, int in, int P, bool meanabs, uint16_t* g,
-                       uint16_t* h, uint4* planes, void* ws, hipStream_t st);
+                       uint16_t* h, uint4* planes, void* ws, hipStream_t st, bool normalized = false);
 hipError_t launch_unpack(const uint4* planes, int out, int in, int P, uint32_t* words, hipStream_t st);
 
 size_t gemv_workspace_bytes(int out, int in, int batch);

@@ -24,6 +24,7 @@ RABIT_EDEVICE = -5
 RABIT_EWORKSPACE = -6
 RABIT_SCALES_GIVEN = 0
 RABIT_SCALES_MEANABS = 1
+RABIT_SCALES_MEANABS_NORMALIZED = 2
 RABIT_OUT_F32 = 0
 RABIT_OUT_BF16 = 1
 RABIT_LAYOUT_V1 = 1
@@ -187,7 +188,7 @@ def pack(w: torch.Tensor, layer: PackedLayer, mode: int = RABIT_SCALES_MEANABS,
     lib = load()
     assert w.dtype == torch.float32 and w.is_contiguous()
     nb = lib.rabit_pack_workspace_bytes(layer.out_features, layer.in_features)
-    if workspace is None and mode == RABIT_SCALES_MEANABS:
+    if workspace is None and mode != RABIT_SCALES_GIVEN:
         workspace = _ws(nb, w.device)
     lc = layer.c()
     _check(lib.rabit_pack(_ptr(w), mode, ctypes.byref(lc), _ptr(workspace),

@@ -69,7 +69,10 @@ typedef enum {
 
 enum {
   RABIT_SCALES_GIVEN = 0,   /* g_1, h_1 are inputs; g_2, h_2 are not touched */
-  RABIT_SCALES_MEANABS = 1  /* all four scales written as mean |.| (see above) */
+  RABIT_SCALES_MEANABS = 1, /* all four scales written as mean |.| (see above) */
+  /* as MEANABS, with each h divided by the global mean |.| of the matrix
+     being binarised (see rabit_pack) */
+  RABIT_SCALES_MEANABS_NORMALIZED = 2
 };
 
 enum {
@@ -131,6 +134,15 @@ size_t rabit_gemm_workspace_bytes(int32_t out_features, int32_t in_features, int
  * scale_mode  RABIT_SCALES_MEANABS: writes g_1, h_1 = mean |W| per row/column,
  *             then g_2, h_2 = mean |R_1| (and g_3, h_3 = mean |R_2|), and the
  *             planes. W is read 2 times (3 with three paths).
+ *             RABIT_SCALES_MEANABS_NORMALIZED: as MEANABS with h[j] =
+ *             fp16((S_col(j) / out) / mu), mu = T / (out * in), where T is
+ *             the canonical total of the row sums S_row: lane l (0..63) adds
+ *             S_row(l), S_row(l+64), ... in ascending order from +0.0, then
+ *             v[l] += v[l+s] for s = 32,16,8,4,2,1 (result v[0]); each
+ *             division one IEEE float64 division (h = 0 where T = 0). Then
+ *             g_p h_p tracks |M| itself rather than mean|M|^2 (a reading that
+ *             fits paper App. B, Corollary 1: the second path approximates
+ *             the first path's residual).
  *             RABIT_SCALES_GIVEN: reads g_1, h_1 (and with three paths g_2,
  *             h_2) from layer->g, layer->h; writes only the planes (one read
  *             of W).

@@ -54,7 +54,7 @@ import numpy as np
 __all__ = [
     "TILE_ROWS", "SEG_ROWS", "TILE_COLS", "LANE_COLS",
     "f16_rne", "bf16_rne", "frac_round_to_format",
-    "canonical_row_sums", "canonical_col_sums", "meanabs_scales",
+    "canonical_row_sums", "canonical_col_sums", "canonical_total", "meanabs_scales",
     "derive", "Derived",
     "pack_words", "unpack_words", "device_planes", "device_planes_to_words",
     "planes_bytes", "weff", "gemv", "gemv_additions", "gemm",
@@ -196,12 +196,44 @@ def frac_round_to_format(x: Fraction, mant_bits: int, emin: int, emax: int) -> F
 # ---------------------------------------------------------------------------
 # Derivation of the two paths (paper §4.2, coupled forward pass)
 # ---------------------------------------------------------------------------
-def meanabs_scales(m_abs: np.ndarray):
-    """(g, h) = fp16 mean |M| per row and per column, canonical sums."""
+def canonical_total(row_sums: np.ndarray) -> float:
+    """Canonical float64 total of the (non-negative) row sums of a matrix:
+    lane l (0..63) sums rows l, l+64, l+128, ... in ascending order from +0.0,
+    then the 64 lane values are combined by the halving tree
+    v[l] += v[l + s], s = 32, 16, 8, 4, 2, 1 (result v[0])."""
+    s = np.asarray(row_sums, dtype=np.float64)
+    n = s.shape[0]
+    p = np.zeros(max(_ceil_to(n, 64), 64), dtype=np.float64)
+    p[:n] = s
+    blocks = p.reshape(-1, 64)        # block c holds rows 64c .. 64c+63, lane l = column l
+    v = np.zeros(64, dtype=np.float64)
+    for c in range(blocks.shape[0]):
+        v = v + blocks[c]
+    w = 32
+    while w >= 1:
+        v = v[:w] + v[w:2 * w]
+        w //= 2
+    return float(v[0])
+
+
+def meanabs_scales(m_abs: np.ndarray, normalized: bool = False):
+    """(g, h) = fp16 mean |M| per row and per column, canonical sums.
+
+    normalized: h is divided by the global mean mu = T / (rows cols) of |M|
+    (T = canonical_total of the row sums), so that g_i h_j tracks |M_ij|
+    itself rather than its square: h[j] = fp16((S_col[j] / rows) / mu), each
+    division one IEEE float64 division.
+    """
     rows, cols = m_abs.shape
-    g = f16_rne(canonical_row_sums(m_abs) / np.float64(cols))
-    h = f16_rne(canonical_col_sums(m_abs) / np.float64(rows))
-    return g, h
+    srow = canonical_row_sums(m_abs)
+    scol = canonical_col_sums(m_abs)
+    g = f16_rne(srow / np.float64(cols))
+    if not normalized:
+        return g, f16_rne(scol / np.float64(rows))
+    mu = canonical_total(srow) / (np.float64(rows) * np.float64(cols))
+    with np.errstate(divide="ignore", invalid="ignore"):
+        hn = (scol / np.float64(rows)) / mu if mu != 0.0 else np.zeros_like(scol)
+    return g, f16_rne(hn)
 
 
 class Derived:
@@ -242,16 +274,23 @@ def derive(w, mode: str = "meanabs", g1=None, h1=None, g2=None, h2=None, n_paths
     With n_paths = 3 the same step once more (each path corrects the residual
     of its predecessor, paper §1): R_2 = R_1 − g_2 ⊙ B_2 ⊙ h_2, B_3 = sign(R_2).
     mode "meanabs": g_p, h_p are the mean |.| of the matrix being binarised
-    (W for path 1, R_1 for path 2, R_2 for path 3). mode "given": the scales
-    are supplied by the caller (the last path's scales do not affect the bits).
+    (W for path 1, R_1 for path 2, R_2 for path 3). mode
+    "meanabs_normalized": the same with h_p divided by the matrix's global
+    mean |.| (``meanabs_scales``), so that g_p h_p tracks |M| (a reading
+    that fits the pages' App. B Corollary 1, W_hat_2 close to R_1). mode
+    "given": the scales are supplied by the caller (the last path's scales
+    do not affect the bits).
     """
     if n_paths not in (2, 3):
         raise ValueError(n_paths)
     w = np.asarray(w, dtype=np.float32)
     out, inp = w.shape
     s1 = w < 0
+    norm = mode == "meanabs_normalized"
+    if norm:
+        mode = "meanabs"
     if mode == "meanabs":
-        g1, h1 = meanabs_scales(np.abs(w).astype(np.float64))
+        g1, h1 = meanabs_scales(np.abs(w).astype(np.float64), norm)
     elif mode == "given":
         g1 = np.asarray(g1, dtype=np.float16)
         h1 = np.asarray(h1, dtype=np.float16)
@@ -265,7 +304,7 @@ def derive(w, mode: str = "meanabs", g1=None, h1=None, g2=None, h2=None, n_paths
     r = (w - b1e1).astype(np.float32)          # float32 subtraction: one rounding
     s2 = r < 0
     if mode == "meanabs":
-        g2, h2 = meanabs_scales(np.abs(r).astype(np.float64))
+        g2, h2 = meanabs_scales(np.abs(r).astype(np.float64), norm)
     else:
         g2 = np.asarray(g2 if g2 is not None else np.zeros(out), dtype=np.float16)
         h2 = np.asarray(h2 if h2 is not None else np.zeros(inp), dtype=np.float16)
@@ -277,7 +316,7 @@ def derive(w, mode: str = "meanabs", g1=None, h1=None, g2=None, h2=None, n_paths
     r2 = (r - b2e2).astype(np.float32)
     s3 = r2 < 0
     if mode == "meanabs":
-        g3, h3 = meanabs_scales(np.abs(r2).astype(np.float64))
+        g3, h3 = meanabs_scales(np.abs(r2).astype(np.float64), norm)
     else:
         g3 = np.asarray(g3 if g3 is not None else np.zeros(out), dtype=np.float16)
         h3 = np.asarray(h3 if h3 is not None else np.zeros(inp), dtype=np.float16)

@@ -121,6 +121,9 @@ def test_pack_argument_errors(lib):
         w, mode, ctypes.byref(layer), ws, wsb, None)
     assert pk(w=0) == rabit.RABIT_EINVAL
     assert pk(mode=5) == rabit.RABIT_EINVAL
+    assert pk(mode=3) == rabit.RABIT_EINVAL
+    # the normalized mean-|.| mode is accepted and needs the workspace
+    assert pk(mode=rabit.RABIT_SCALES_MEANABS_NORMALIZED, wsb=8) == rabit.RABIT_EWORKSPACE
     assert pk(w=w + 4) == rabit.RABIT_EALIGN
     assert pk(w=FAKE) == rabit.RABIT_EINVAL          # W aliases the planes it would write
     assert pk(ws=0) == rabit.RABIT_EWORKSPACE

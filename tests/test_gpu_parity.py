@@ -387,3 +387,35 @@ def test_stream_read_runs(gpu_lib):
     sink = gpu_lib.stream_read(t)
     torch.cuda.synchronize()
     assert sink.numel() == 4
+
+
+@pytest.mark.parametrize("shape", [(64, 256), (130, 1000), (1024, 4096), (11008, 4096)])
+def test_pack_meanabs_normalized_bit_exact(gpu_lib, shape):
+    # h divided by the matrix's global mean |.| (canonical total of the row sums)
+    out, inp = shape
+    say("pack meanabs normalized", shape)
+    w = weight_f32(out, inp, 1500 + out + inp)
+    layer = pack_gpu(gpu_lib, w, gpu_lib.RABIT_SCALES_MEANABS_NORMALIZED)
+    d = oracle.derive(w.numpy(), mode="meanabs_normalized")
+    check_pack(gpu_lib, layer, d, out, inp)
+    x = act_bf16(2, inp, 1600 + inp)
+    y = gpu_lib.gemv(layer, x.cuda()).cpu().numpy().astype(np.float64)
+    ref = oracle.gemv(d, bf16_values(x))
+    assert oracle.normwise_rel_err(y, ref) < TOL
+    check_fx(y, ref, d, bf16_values(x))
+
+
+def test_pack_meanabs_normalized_three_paths_and_zero(gpu_lib):
+    out, inp = 200, 700
+    say("pack meanabs normalized, three paths and a zero matrix")
+    w = weight_f32(out, inp, 1700)
+    layer = gpu_lib.PackedLayer.empty(out, inp, n_paths=3)
+    gpu_lib.pack(w.cuda(), layer, gpu_lib.RABIT_SCALES_MEANABS_NORMALIZED)
+    d = oracle.derive(w.numpy(), mode="meanabs_normalized", n_paths=3)
+    words = gpu_lib.unpack(layer).cpu().numpy().view(np.uint32)
+    for p, (s, g, h) in enumerate(d.paths):
+        assert np.array_equal(words[p], oracle.pack_words(s)), p
+        assert np.array_equal(layer.g[p].cpu().numpy().view(np.uint16), g.view(np.uint16)), p
+        assert np.array_equal(layer.h[p].cpu().numpy().view(np.uint16), h.view(np.uint16)), p
+    z = pack_gpu(gpu_lib, torch.zeros(64, 300), gpu_lib.RABIT_SCALES_MEANABS_NORMALIZED)
+    assert not z.g.any() and not z.h.any() and not z.planes.any()
