@@ -10,7 +10,10 @@ constexpr int kPerThread = 8;  // 16-byte loads in flight per thread
 
 // Workgroup b reads the 16-byte units [b * 2048, (b + 1) * 2048) (the last one
 // fewer): unit b * 2048 + i * 256 + tid for i < 8, so that each load
-// instruction covers 4 KiB of consecutive memory.
+// instruction covers 4 KiB of consecutive memory. Streaming (non-temporal)
+// loads, like the GEMV's plane loads: of the plain read patterns measured
+// (4, 8 or 16 loads per thread, persistent grids, 8 KiB per wave) this one
+// reads fastest (6.1 TB/s over 117 MB, 6.5 TB/s over 470 MB).
 __global__ __launch_bounds__(256) void k_stream_read(const uint4* __restrict__ src, size_t n16,
                                                      uint32_t* __restrict__ sink) {
   const size_t base = (size_t)blockIdx.x * 256 * kPerThread + threadIdx.x;
@@ -18,7 +21,7 @@ __global__ __launch_bounds__(256) void k_stream_read(const uint4* __restrict__ s
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i) {
     const size_t u = base + (size_t)i * 256;
-    v[i] = src[u < n16 ? u : n16 - 1];
+    v[i] = load_nt(src + (u < n16 ? u : n16 - 1));
   }
   uint32_t acc = 0;
 #pragma unroll
