@@ -2,6 +2,7 @@
 // carving and dispatch to the HIP launchers. Nothing here allocates device
 // memory; every call enqueues on the caller's stream.
 #include <algorithm>
+#include <mutex>
 
 #include "rabit_internal.h"
 
@@ -68,6 +69,7 @@ const char* rabit_status_string(int status) {
     case RABIT_EUNSUPPORTED: return "unsupported option";
     case RABIT_EDEVICE: return "HIP launch or runtime error";
     case RABIT_EWORKSPACE: return "workspace missing or too small";
+    case RABIT_ESCRATCH: return "call needs more than the fixed scratch buffer of rabit_gemv_noalloc";
     default: return "unknown status";
   }
 }
@@ -170,6 +172,51 @@ int rabit_gemv(const rabit_layer* L, const uint16_t* x, int32_t batch, void* y, 
   return dev_status(launch_gemv((const uint4*)L->planes, L->g, L->h, L->out_features,
                                 L->in_features, x, batch, y, y_dtype, workspace,
                                 (hipStream_t)stream, L->n_paths));
+}
+
+}  // extern "C"
+
+// ---- the allocation-free GEMV's scratch ------------------------------------
+// One file-scope device array per GPU the library runs on. Host code never
+// uses the name `scratch` as an address: its device address is looked up per
+// device (hipGetSymbolAddress, with that device current) on the first call
+// there and kept in scratch_dev[].
+namespace {
+constexpr int kScratchDevices = 64;
+__device__ __align__(256) unsigned char scratch[RABIT_NOALLOC_SCRATCH_BYTES];
+std::mutex scratch_mu;
+void* scratch_dev[kScratchDevices] = {};
+
+void* scratch_address() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_dev[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    scratch_dev[dev] = p;
+  }
+  return scratch_dev[dev];
+}
+}  // namespace
+
+extern "C" {
+
+int rabit_gemv_noalloc(const rabit_layer* L, const uint16_t* x, int32_t batch, void* y,
+                       int32_t y_dtype, void* stream) {
+  int s = check_layer(L);
+  if (s) return s;
+  if (!x || !y) return RABIT_EINVAL;
+  if (y_dtype != RABIT_OUT_F32 && y_dtype != RABIT_OUT_BF16) return RABIT_EINVAL;
+  if (batch < 1 || batch > RABIT_MAX_GEMV_BATCH) return RABIT_ESHAPE;
+  if ((s = check_gemv_x(L, x)) || (s = check_gemv_y(L, batch, y, y_dtype, x))) return s;
+  if (gemv_workspace_bytes(L->out_features, L->in_features, batch) > RABIT_NOALLOC_SCRATCH_BYTES)
+    return RABIT_ESCRATCH;
+  void* ws = scratch_address();
+  if (!ws) return RABIT_EDEVICE;
+  return dev_status(launch_gemv((const uint4*)L->planes, L->g, L->h, L->out_features,
+                                L->in_features, x, batch, y, y_dtype, ws, (hipStream_t)stream,
+                                L->n_paths));
 }
 
 int rabit_gemv_partial(const rabit_layer* L, const uint16_t* x, int32_t batch, void* workspace,

@@ -22,6 +22,8 @@ RABIT_EALIGN = -3
 RABIT_EUNSUPPORTED = -4
 RABIT_EDEVICE = -5
 RABIT_EWORKSPACE = -6
+RABIT_ESCRATCH = -7
+NOALLOC_SCRATCH_BYTES = 16 << 20
 RABIT_SCALES_GIVEN = 0
 RABIT_SCALES_MEANABS = 1
 RABIT_SCALES_MEANABS_NORMALIZED = 2
@@ -39,7 +41,7 @@ EXPORTS = [
     "rabit_gemv_partial_multi", "rabit_stream_read", "rabit_grad_input_workspace_bytes",
     "rabit_grad_weight_workspace_bytes", "rabit_transpose_planes", "rabit_grad_input",
     "rabit_grad_weight", "rabit_svid_workspace_bytes", "rabit_svid_init", "rabit_gemm_ex",
-    "rabit_grad_input_ex",
+    "rabit_grad_input_ex", "rabit_gemv_noalloc",
 ]
 
 
@@ -96,6 +98,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "rabit_pack": (ctypes.c_int, [vp, u32, lp, vp, sz, vp]),
         "rabit_unpack": (ctypes.c_int, [lp, vp, vp]),
         "rabit_gemv": (ctypes.c_int, [lp, vp, i32, vp, i32, vp, sz, vp]),
+        "rabit_gemv_noalloc": (ctypes.c_int, [lp, vp, i32, vp, i32, vp]),
         "rabit_gemm": (ctypes.c_int, [lp, vp, i32, vp, i32, vp, sz, vp]),
         "rabit_gemv_partial": (ctypes.c_int, [lp, vp, i32, vp, sz, vp]),
         "rabit_gemv_reduce": (ctypes.c_int, [lp, i32, vp, i32, vp, sz, vp]),
@@ -226,6 +229,17 @@ def gemv(layer: PackedLayer, x: torch.Tensor, y_dtype: int = RABIT_OUT_F32,
     lc = layer.c()
     _check(lib.rabit_gemv(ctypes.byref(lc), _ptr(x), batch, _ptr(y), y_dtype, _ptr(workspace),
                           workspace.numel(), _stream(stream)), "rabit_gemv")
+    return y
+
+
+def gemv_noalloc(layer: PackedLayer, x: torch.Tensor, y: torch.Tensor, y_dtype: int = RABIT_OUT_F32,
+                 stream=None) -> torch.Tensor:
+    """rabit_gemv_noalloc: the GEMV with the library's fixed scratch buffer
+    (no workspace); y must be preallocated [batch, out]."""
+    assert x.dtype == torch.bfloat16 and x.is_contiguous() and y.is_contiguous()
+    lc = layer.c()
+    _check(load().rabit_gemv_noalloc(ctypes.byref(lc), _ptr(x), x.shape[0], _ptr(y), y_dtype,
+                                     _stream(stream)), "rabit_gemv_noalloc")
     return y
 
 

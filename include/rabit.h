@@ -64,7 +64,9 @@ typedef enum {
   RABIT_EALIGN = -3,        /* device pointer not 16-byte aligned */
   RABIT_EUNSUPPORTED = -4,  /* n_paths != 2, or an unsupported option */
   RABIT_EDEVICE = -5,       /* a HIP launch or runtime call failed */
-  RABIT_EWORKSPACE = -6     /* workspace missing or too small */
+  RABIT_EWORKSPACE = -6,    /* workspace missing or too small */
+  RABIT_ESCRATCH = -7       /* rabit_gemv_noalloc: the call needs more than its
+                               fixed scratch buffer (RABIT_NOALLOC_SCRATCH_BYTES) */
 } rabit_status;
 
 enum {
@@ -180,6 +182,28 @@ int rabit_unpack(const rabit_layer *layer, uint32_t *words, void *stream);
 int rabit_gemv(const rabit_layer *layer, const uint16_t *x, int32_t batch,
                void *y, int32_t y_dtype, void *workspace, size_t workspace_bytes,
                void *stream);
+
+/*
+ * rabit_gemv without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). Same arithmetic, kernels and result bits as
+ * rabit_gemv; nothing is allocated. The per-range partials live in a fixed
+ * scratch array of RABIT_NOALLOC_SCRATCH_BYTES in device memory that the
+ * library holds on every GPU it runs on until the process ends (its address
+ * is looked up once per device, on the first call there).
+ * Limit: rabit_gemv_workspace_bytes(out, in, batch) <= RABIT_NOALLOC_SCRATCH_BYTES
+ * (e.g. a 28672 x 8192 or 8192 x 28672 layer up to batch 4), else
+ * RABIT_ESCRATCH before anything is enqueued.
+ * Every call on one GPU shares that GPU's scratch: calls that may overlap on
+ * one GPU (different streams without ordering between them, or several host
+ * threads) race and must be serialised by the caller. Each call overwrites
+ * every partial it reads, so nothing needs clearing between calls.
+ * Errors: as rabit_gemv (no workspace errors), RABIT_ESCRATCH, RABIT_EDEVICE
+ * (the scratch address could not be obtained).
+ */
+#define RABIT_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int rabit_gemv_noalloc(const rabit_layer *layer, const uint16_t *x, int32_t batch, void *y,
+                       int32_t y_dtype, void *stream);
 
 /*
  * The two halves of rabit_gemv, for callers that time or schedule them apart.

@@ -51,7 +51,7 @@ def test_sizes(lib):
     assert lib.rabit_gemv_workspace_bytes(4096, 4096, 33) == 0
     assert lib.rabit_gemm_workspace_bytes(4096, 4096, 512) > 0
     assert lib.rabit_layout_version() == 1
-    for code in range(-6, 1):
+    for code in range(-7, 1):
         assert rabit.status_string(code) != "unknown status"
 
 
@@ -299,3 +299,28 @@ def test_three_path_layer_aliasing(lib):
     for w in (third_plane, g3, h3):
         arr = (rabit.RabitLayerC * 2)(a, L3)
         assert lib.rabit_gemv_partial_multi(arr, 2, x, 1, w, big, None) == rabit.RABIT_EINVAL
+
+
+def test_gemv_noalloc_argument_errors(lib):
+    # every error is returned before the scratch address is looked up or
+    # anything is enqueued
+    def na(layer, x=FAKE + (3 << 30), batch=1, y=FAKE + (4 << 30), dtype=0):
+        return lib.rabit_gemv_noalloc(ctypes.byref(layer) if layer is not None else None, x, batch, y,
+                                      dtype, None)
+    L = fake_layer()
+    assert na(None) == rabit.RABIT_EINVAL
+    assert na(fake_layer(paths=4)) == rabit.RABIT_EUNSUPPORTED
+    assert na(L, x=0) == rabit.RABIT_EINVAL
+    assert na(L, dtype=5) == rabit.RABIT_EINVAL
+    assert na(L, batch=0) == rabit.RABIT_ESHAPE
+    assert na(L, batch=33) == rabit.RABIT_ESHAPE
+    assert na(L, y=FAKE + (3 << 30)) == rabit.RABIT_EINVAL            # y aliases x
+    assert na(L, y=FAKE + 8 + (4 << 30)) == rabit.RABIT_EALIGN
+    L3 = fake_layer(paths=3)
+    assert na(L3, y=FAKE + 32768) == rabit.RABIT_EINVAL               # y on the third plane
+    # partials beyond the fixed scratch buffer
+    big = fake_layer(28672, 8192, planes=FAKE, g=FAKE + (1 << 30), h=FAKE + (2 << 30))
+    need = lib.rabit_gemv_workspace_bytes(28672, 8192, 8)
+    assert need > rabit.NOALLOC_SCRATCH_BYTES
+    assert na(big, batch=8, x=FAKE + (3 << 32), y=FAKE + (4 << 32)) == rabit.RABIT_ESCRATCH
+    assert lib.rabit_gemv_workspace_bytes(28672, 8192, 4) <= rabit.NOALLOC_SCRATCH_BYTES
