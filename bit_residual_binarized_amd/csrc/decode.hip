@@ -65,13 +65,14 @@ __global__ void k_residual_add(const uint16_t* __restrict__ x, const float* __re
 }
 
 // ---- consumers of GEMV partials (fused with the ops that follow a layer) ----
-// part: float64 [batch][S][stride] with S = ceil(in/512) ranges of the
-// producing GEMV and stride = 64 ceil(n/64); sum_ranges adds the ranges in
-// ascending order, as rabit_gemv_reduce does.
+// part: the producing GEMV launch's partial buffer of the matrix (a header
+// with the slice count S, then float64 [batch][S][stride], stride =
+// 64 ceil(n/64); slices are 512-column ranges or chunks of them);
+// sum_ranges adds the slices in ascending order, as rabit_gemv_reduce does.
 // Block (i, b) covers elements [i span, (i + 1) span) of row b: x_out =
 // bf16(x + Σ part) (or x itself without part) and the sum of x_out^2 over
 // the block, combined in a fixed order, into stats[b][i].
-__global__ __launch_bounds__(256) void k_resid_stats(const double* __restrict__ part, int S,
+__global__ __launch_bounds__(256) void k_resid_stats(const double* __restrict__ part,
                                                      const uint16_t* x, uint16_t* x_out,
                                                      double* __restrict__ stats, int n) {
   const int i = blockIdx.x, b = blockIdx.y;
@@ -82,7 +83,7 @@ __global__ __launch_bounds__(256) void k_resid_stats(const double* __restrict__ 
   for (int e = e0 + (int)threadIdx.x; e < e1; e += 256) {
     double v = (double)bf16_bits_to_f32(x[(size_t)b * n + e]);
     if (part) {
-      const uint16_t o = f64_to_bf16_rne(v + sum_ranges(part, b, S, stride, e));
+      const uint16_t o = f64_to_bf16_rne(v + sum_ranges(part, b, stride, e));
       x_out[(size_t)b * n + e] = o;
       v = (double)bf16_bits_to_f32(o);
     }
@@ -96,54 +97,53 @@ __global__ __launch_bounds__(256) void k_resid_stats(const double* __restrict__ 
 }
 
 __global__ __launch_bounds__(256) void k_reduce_silu(const double* __restrict__ pg,
-                                                     const double* __restrict__ pu, int S,
+                                                     const double* __restrict__ pu,
                                                      uint16_t* __restrict__ a, int n) {
   const int i = blockIdx.x * 256 + threadIdx.x, b = blockIdx.y;
   if (i >= n) return;
   const int stride = 64 * ((n + 63) / 64);
-  const double g = sum_ranges(pg, b, S, stride, i), u = sum_ranges(pu, b, S, stride, i);
+  const double g = sum_ranges(pg, b, stride, i), u = sum_ranges(pu, b, stride, i);
   a[(size_t)b * n + i] = f64_to_bf16_rne(g / (1.0 + exp(-g)) * u);
 }
 
 // qk: [batch][n_q + kv] fp32 (q then k); attn: [batch][n_q] bf16
 __global__ __launch_bounds__(256) void k_reduce_attn(const double* __restrict__ pq,
                                                      const double* __restrict__ pk,
-                                                     const double* __restrict__ pv, int S,
+                                                     const double* __restrict__ pv,
                                                      float* __restrict__ qk,
                                                      uint16_t* __restrict__ attn, int n_q, int kv,
                                                      int rep, int head_dim) {
   const int i = blockIdx.x * 256 + threadIdx.x, b = blockIdx.y;
   const int sq = 64 * ((n_q + 63) / 64), skv = 64 * ((kv + 63) / 64);
   if (i < n_q) {
-    qk[(size_t)b * (n_q + kv) + i] = (float)sum_ranges(pq, b, S, sq, i);
+    qk[(size_t)b * (n_q + kv) + i] = (float)sum_ranges(pq, b, sq, i);
     const int h = i / head_dim, d = i - h * head_dim;
-    attn[(size_t)b * n_q + i] = f64_to_bf16_rne(sum_ranges(pv, b, S, skv, (h / rep) * head_dim + d));
+    attn[(size_t)b * n_q + i] = f64_to_bf16_rne(sum_ranges(pv, b, skv, (h / rep) * head_dim + d));
   }
-  if (i < kv) qk[(size_t)b * (n_q + kv) + n_q + i] = (float)sum_ranges(pk, b, S, skv, i);
+  if (i < kv) qk[(size_t)b * (n_q + kv) + n_q + i] = (float)sum_ranges(pk, b, skv, i);
 }
 
 }  // namespace
 
-hipError_t launch_resid_stats(const double* part, int in_of_part, const uint16_t* x, uint16_t* x_out,
+hipError_t launch_resid_stats(const double* part, const uint16_t* x, uint16_t* x_out,
                               double* stats, int batch, int n, hipStream_t st) {
-  hipLaunchKernelGGL(k_resid_stats, dim3(RABIT_STAT_PARTS, batch), dim3(256), 0, st, part,
-                     (in_of_part + 511) / 512, x, x_out, stats, n);
+  hipLaunchKernelGGL(k_resid_stats, dim3(RABIT_STAT_PARTS, batch), dim3(256), 0, st, part, x,
+                     x_out, stats, n);
   return hipGetLastError();
 }
 
-hipError_t launch_reduce_silu(const double* pg, const double* pu, int in_of_part, uint16_t* a,
+hipError_t launch_reduce_silu(const double* pg, const double* pu, uint16_t* a,
                               int batch, int n, hipStream_t st) {
-  hipLaunchKernelGGL(k_reduce_silu, dim3((n + 255) / 256, batch), dim3(256), 0, st, pg, pu,
-                     (in_of_part + 511) / 512, a, n);
+  hipLaunchKernelGGL(k_reduce_silu, dim3((n + 255) / 256, batch), dim3(256), 0, st, pg, pu, a, n);
   return hipGetLastError();
 }
 
 hipError_t launch_reduce_attn(const double* pq, const double* pk, const double* pv,
-                              int in_of_part, float* qk, uint16_t* attn, int batch, int n_heads,
+                              float* qk, uint16_t* attn, int batch, int n_heads,
                               int n_kv_heads, int head_dim, hipStream_t st) {
   const int n_q = n_heads * head_dim, kv = n_kv_heads * head_dim;
   hipLaunchKernelGGL(k_reduce_attn, dim3((std::max(n_q, kv) + 255) / 256, batch), dim3(256), 0, st,
-                     pq, pk, pv, (in_of_part + 511) / 512, qk, attn, n_q, kv, n_heads / n_kv_heads,
+                     pq, pk, pv, qk, attn, n_q, kv, n_heads / n_kv_heads,
                      head_dim);
   return hipGetLastError();
 }

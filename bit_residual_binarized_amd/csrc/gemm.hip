@@ -192,41 +192,6 @@ __global__ __launch_bounds__(256) void k_gemm_prep(const uint16_t* __restrict__ 
     prep_h(h, in, Kp, P, ws, blockIdx.x - nbx);
 }
 
-// Raw (untyped, unswizzled) buffer resource word 3.
-constexpr int kBufWord3 = 0x00020000;
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Direct buffer-to-LDS loads of 16 and 4 bytes per lane: lane l writes its
-// bytes at dst + size * l. (Plain device functions: inside a kernel template
-// the builtin keeps the host pass from emitting the kernel's launch handle.)
-__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, lds_void* dst, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
-}
-__device__ __forceinline__ void lds_load4(__amdgpu_buffer_rsrc_t r, lds_void* dst, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 4, voff, 0, 0, 0);
-}
-
-// s_waitcnt immediate: at most n vector-memory loads of this wave in flight
-// and (lgkm0) none of its LDS accesses; expcnt unconstrained
-__host__ __device__ constexpr int vmcnt_imm(int n, bool lgkm0 = false) {
-  return (n & 15) | ((n >> 4) << 14) | (7 << 4) | ((lgkm0 ? 0 : 15) << 8);
-}
-
-// Workgroup barrier after this wave's loads but the last N have landed in
-// LDS and its own LDS reads are done. A fence (__syncthreads) would wait for
-// every load in flight, direct-to-LDS ones included; the empty asm
-// statements keep the compiler from moving memory accesses across the
-// barrier instead.
-template <int N>
-__device__ __forceinline__ void ring_barrier() {
-  __builtin_amdgcn_sched_barrier(0);  // no instruction moves across a step boundary
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(N, true));
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
-
 // LDS bytes of one stage of the main loop's ring (X rows, plane words and h
 // pairs of one 64-column step), and the ring depth: four stages where two
 // workgroups fit a CU's 160 KiB of LDS, else three

@@ -64,7 +64,8 @@ struct Seg {
   const uint4* planes;
   const uint16_t* g;
   const uint16_t* h;
-  double* part;  // partials [batch][S][RG*64]
+  double* part;  // partial buffer: header (slice count), then [batch][slices][RG*64]
+  uint32_t* hp;  // fp16 path: the matrix's h pairs in the contraction order
   int out, RG, rb0;
 };
 
@@ -76,6 +77,9 @@ struct Args {
   const double* stats;    // norm mode: [batch][kStatParts] partial sums of x^2
   int nseg, in, KG, S, m, batch, norm;
   int items, ngrp;        // work items (row block, range); batch groups along x
+  int kr, nck;            // fp16 path: ranges per chunk, chunks per row block
+  uint16_t* xh;           // fp16 path: prepared x [batch][Kp] (contraction order)
+  int* rowexp;            // fp16 path: per token, the power of two applied to x
   float eps;
 };
 
@@ -91,8 +95,20 @@ struct Plan {
 
 
 __host__ inline size_t part_bytes(int out, int S, int batch) {
-  return align256((size_t)batch * S * row_groups(out) * 64 * sizeof(double));
+  return kPartHdrDoubles * sizeof(double) + align256((size_t)batch * S * row_groups(out) * 64 * sizeof(double));
 }
+
+// fp16 path (batches from RABIT_GEMV_FP16_MIN_BATCH on): after each matrix's
+// partial buffer, the launch's prepared x (used in the first matrix's area),
+// the per-token exponents and the matrix's h pairs (up to 3 paths).
+// The prepared rows span whole ranges, S = ceil(in / 512) of them, zero past
+// in: a range's columns past in meet zeros there, whatever weights the
+// clamped plane loads bring.
+__host__ inline int f16_cols(int in) { return (in + kChunk - 1) / kChunk * kChunk; }
+__host__ inline size_t xh_bytes(int in) { return align256((size_t)RABIT_MAX_GEMV_BATCH * f16_cols(in) * 2); }
+constexpr size_t kRowExpBytes = 256;
+__host__ inline size_t hp_bytes(int in) { return align256((size_t)3 * (f16_cols(in) / 32) * 64); }
+__host__ inline size_t prep_bytes(int in) { return xh_bytes(in) + kRowExpBytes + hp_bytes(in); }
 
 // 6 dwords of 32 fp6 fields, every field = code
 __device__ __forceinline__ void fill_code(uint32_t (&dw)[kImgDw], uint32_t code) {
@@ -166,6 +182,12 @@ __global__ __launch_bounds__(256) void k_gemv(Args A) {
   const int out = si == 2 ? A.seg[2].out : si == 1 ? A.seg[1].out : A.seg[0].out;
   const int RG = si == 2 ? A.seg[2].RG : si == 1 ? A.seg[1].RG : A.seg[0].RG;
   const int rb = rbg - (si == 2 ? A.seg[2].rb0 : si == 1 ? A.seg[1].rb0 : A.seg[0].rb0);
+  if (blockIdx.x == 0 && threadIdx.x < A.nseg) {
+    // the partial buffers' headers: one slice per range
+    double* hp = threadIdx.x == 2 ? A.seg[2].part : threadIdx.x == 1 ? A.seg[1].part : A.seg[0].part;
+    *(int*)hp = A.S;
+  }
+  part += kPartHdrDoubles;
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
@@ -514,13 +536,296 @@ __global__ __launch_bounds__(256) void k_gemv(Args A) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Batches from kF16MinBatch on: fp16 matrix cores, every weight decoded once
+// for all the batch's tokens.
+//
+// The digit path above spends its matrix and slice work per batch pair; from
+// a few pairs on, a dense fp16 contraction is cheaper. Per token, x is scaled
+// by a power of two and rounded to fp16 (k_gemv16_prep, below); the B operand
+// holds ±h_p (exact in fp16); the products are exact in fp32 and the matrix
+// cores accumulate them in fp32. A workgroup covers a chunk of kr consecutive
+// ranges of 512 columns and, per chunk and output, forms Σ_p g_p acc_p 2^-e in
+// float64 and leaves it as one partial (so the partials, written and read
+// again by the consumer, shrink kr-fold).
+//
+// Inside a 32-column block the contraction index is permuted so that dword c
+// of a lane's 8 fp16 values holds the columns (m, m + 16), m = 4 t + c, of
+// quarter t (paper App. E.1 packs 32 columns per word: the sign bits of that
+// dword are bits m and m + 16 of the stored word, moved to bits 15 and 31 by
+// one shift). A and B use the same order.
+//
+// Workgroup: 4 waves, one row group (64 rows) each, 4 consecutive row groups.
+// Lane (j, gl) holds, per range, the 16-byte unit (rg, 4 r + gl, p, 16 tau + j)
+// of each path and 16-row slice tau (as in k_gemv); matrix step s of a range
+// takes word s / 4, quarter s % 4 of that unit.
+// ---------------------------------------------------------------------------
+constexpr int kF16MinBatch = RABIT_GEMV_FP16_MIN_BATCH;
+constexpr int kXRow = 260;  // dwords per staged token row (256 + 4: conflict-free 16-byte reads)
+
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ uint32_t f16_pair(float lo, float hi) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
+}
+
+// The prepared input (k_gemv16_prep, one launch before the GEMV): token b's
+// x (RMSNorm applied when the launch has statistics) scaled by 2^e_b so that
+// the row's largest |value| lies in [2^14, 2^15) and rounded to fp16 (exact
+// for every value above 2^-32 of that largest one; the rest off by at most
+// 2^-25 2^-e_b), in the contraction order: dword m of each 32-column block
+// holds columns (m, m + 16); Kp = 512 ceil(in / 512) columns (whole ranges),
+// zero past in. Every matrix's h pairs in the same order.
+// Workgroup (b, s) for s < xs = ceil(Kp / 2048): token b's row maximum (each
+// of the row's workgroups reads the whole row), then columns [2048 s, 2048 s
+// + 2048): thread t writes dwords 4 q .. 4 q + 3 (q = t % 4) of block
+// 64 s + t / 4. Workgroups from hwg0 on: the h pairs.
+constexpr int kPrepCols = 2048;
+
+__global__ __launch_bounds__(256) void k_gemv16_prep(Args A, int P, int hwg0) {
+  const int Kp = A.S * kChunk, nblk = Kp / 32;
+  const int in = A.in, tid = threadIdx.x, l = tid & 63, w = tid >> 6;
+  if ((int)blockIdx.x >= hwg0) {
+    const int idx = ((int)blockIdx.x - hwg0) * 256 + tid;  // (segment, path, block, m)
+    const int per = P * nblk * 16;
+    const int sg = idx / per;
+    if (sg >= A.nseg) return;
+    const int rem = idx - sg * per, pth = rem / (nblk * 16), blk = (rem >> 4) % nblk, m = rem & 15;
+    const uint16_t* h = sg == 2 ? A.seg[2].h : sg == 1 ? A.seg[1].h : A.seg[0].h;
+    uint32_t* hp = sg == 2 ? A.seg[2].hp : sg == 1 ? A.seg[1].hp : A.seg[0].hp;
+    const int c0 = 32 * blk + m, c1 = c0 + 16;
+    const uint32_t lo = c0 < in ? h[(size_t)pth * in + c0] : 0u, hi = c1 < in ? h[(size_t)pth * in + c1] : 0u;
+    hp[(size_t)(pth * nblk + blk) * 16 + m] = lo | (hi << 16);
+    return;
+  }
+  const int xs = (Kp + kPrepCols - 1) / kPrepCols;
+  const int b = blockIdx.x / xs, sl = blockIdx.x % xs;
+  const uint16_t* xb = A.x + (size_t)b * in;
+  __shared__ double s_den;
+  __shared__ float s_m[4];
+  if (A.norm && w == 0) {
+    // the sum of x^2 from its kStatParts partials, by the digit path's DPP tree
+    const double v = A.stats[(size_t)b * kStatParts + (l & (kStatParts - 1))];
+    const double ss = wave_sum_f64(l < kStatParts ? v : 0.0);
+    if (l == 0) s_den = sqrt(ss / (double)in + (double)A.eps);
+  }
+  const bool vec = (in & 7) == 0;
+  float m = 0.0f;
+  if (vec) {
+    const int ng = in / 8;
+    for (int g0 = tid; g0 < ng; g0 += 256 * 8) {
+      uint4 v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = ((const uint4*)xb)[min(g0 + 256 * k, ng - 1)];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const uint32_t d[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+        float mk = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          mk = fmaxf(mk, fmaxf(fabsf(__uint_as_float(d[q] << 16)), fabsf(__uint_as_float(d[q] & 0xFFFF0000u))));
+        m = g0 + 256 * k < ng ? fmaxf(m, mk) : m;
+      }
+    }
+  } else {
+    for (int c = tid; c < in; c += 256) m = fmaxf(m, fabsf(bf16_bits_to_f32(xb[c])));
+  }
+#pragma unroll
+  for (int sh = 32; sh >= 1; sh >>= 1) m = fmaxf(m, __shfl_xor(m, sh, 64));
+  if (l == 0) s_m[w] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+  const double den = A.norm ? s_den : 1.0;
+  // with RMSNorm the largest input is the rounding of the largest |x| / den
+  // (both steps are monotonic)
+  if (A.norm && m > 0.0f) m = bf16_bits_to_f32(f64_to_bf16_rne_fast((double)m / den));
+  const int e = m > 0.0f ? 14 - ilogbf(m) : 0;
+  if (tid == 0 && sl == 0) A.rowexp[b] = e;
+  const int blk = sl * (kPrepCols / 32) + (tid >> 2), q = tid & 3;
+  if (blk >= nblk) return;
+  const int c0 = 32 * blk + 4 * q;  // columns c0 + c and c0 + c + 16, c < 4
+  uint32_t lo[4], hi[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    lo[c] = c0 + c < in ? xb[c0 + c] : 0u;
+    hi[c] = c0 + c + 16 < in ? xb[c0 + c + 16] : 0u;
+  }
+  auto val = [&](uint32_t v) -> float {
+    return A.norm ? bf16_bits_to_f32(f64_to_bf16_rne_fast((double)bf16_bits_to_f32((uint16_t)v) / den))
+                  : bf16_bits_to_f32((uint16_t)v);
+  };
+  uint32_t o[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) o[c] = f16_pair(ldexpf(val(lo[c]), e), ldexpf(val(hi[c]), e));
+  *(uint4*)(A.xh + (size_t)b * Kp + 32 * blk + 8 * q) = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// The contraction: the prepared x and h pairs of a range reach LDS by direct
+// buffer-to-LDS loads into a ring of two stages, issued one range ahead
+// together with that range's weights (no staging registers, one barrier per
+// range).
+template <int MT, int P>
+__global__ __launch_bounds__(256, P == 3 && MT == 2 ? 1 : 2) void k_gemv16(Args A) {
+  constexpr int NB = 16 * MT;   // token rows held (batch <= NB)
+  const int ck = blockIdx.x % A.nck, rbg = blockIdx.x / A.nck;
+  const int si = (A.nseg > 2 && rbg >= A.seg[2].rb0) ? 2 : (A.nseg > 1 && rbg >= A.seg[1].rb0) ? 1 : 0;
+  const uint4* planes = si == 2 ? A.seg[2].planes : si == 1 ? A.seg[1].planes : A.seg[0].planes;
+  const uint16_t* gsc = si == 2 ? A.seg[2].g : si == 1 ? A.seg[1].g : A.seg[0].g;
+  const uint32_t* hps = si == 2 ? A.seg[2].hp : si == 1 ? A.seg[1].hp : A.seg[0].hp;
+  double* part = si == 2 ? A.seg[2].part : si == 1 ? A.seg[1].part : A.seg[0].part;
+  const int out = si == 2 ? A.seg[2].out : si == 1 ? A.seg[1].out : A.seg[0].out;
+  const int RG = si == 2 ? A.seg[2].RG : si == 1 ? A.seg[1].RG : A.seg[0].RG;
+  const int rb = rbg - (si == 2 ? A.seg[2].rb0 : si == 1 ? A.seg[1].rb0 : A.seg[0].rb0);
+  if (blockIdx.x == 0 && threadIdx.x < A.nseg) {
+    // the partial buffers' headers: one slice per chunk
+    double* hp = threadIdx.x == 2 ? A.seg[2].part : threadIdx.x == 1 ? A.seg[1].part : A.seg[0].part;
+    *(int*)hp = A.nck;
+  }
+  part += kPartHdrDoubles;
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
+  const int j = l & 15, gl = l >> 4;
+  const int batch = A.batch;
+  const int Kp = A.S * kChunk, nblk = Kp / 32;  // the prepared rows (whole ranges)
+  const int r0 = ck * A.kr, r1 = min(A.S, r0 + A.kr);
+  const int rg = 4 * rb + w;            // this wave's row group
+  const int rgc = min(rg, RG - 1);      // clamped: loads stay in bounds, results unused
+
+  __shared__ __align__(16) uint32_t s_x[2][NB * kXRow];
+  __shared__ __align__(16) uint32_t s_h[2][P][256];
+
+  auto load_w = [&](uint4 (&wt)[4 * P], int r) {
+    const int kg = min(A.KG - 1, 4 * r + gl);
+#pragma unroll
+    for (int tau = 0; tau < 4; ++tau)
+#pragma unroll
+      for (int p = 0; p < P; ++p) wt[tau * P + p] = load_nt(planes + unit_index(rgc, kg, p, 16 * tau + j, A.KG, P));
+  };
+  // range r's x (wave w: tokens w, w + 4, ...) and h pairs (path w % P) into
+  // stage u: every wave issues NB / 4 + 1 loads of 1 KiB
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)A.xh, (short)0, (int)((size_t)batch * Kp * 2), kBufWord3);
+  const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)hps, (short)0, (int)((size_t)P * nblk * 64), kBufWord3);
+  auto issue = [&](int r, auto U) {
+    constexpr int u = decltype(U)::value;
+#pragma unroll
+    for (int k = 0; k < NB / 4; ++k) {
+      const int b = w + 4 * k;
+      lds_load16(rx, (lds_void*)(s_x[u] + b * kXRow),
+                 (uint32_t)(((size_t)min(b, batch - 1) * Kp + (size_t)r * kChunk) * 2) + 16u * l);
+    }
+    const int hpth = w % P;
+    lds_load16(rh, (lds_void*)(s_h[u][hpth]), (uint32_t)((hpth * nblk + 16 * r) * 64) + 16u * l);
+  };
+
+  v4f acc[P][4][MT];
+#pragma unroll
+  for (int p = 0; p < P; ++p)
+#pragma unroll
+    for (int tau = 0; tau < 4; ++tau)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[p][tau][mt] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+  // the matrix ops of stage u with the range's weights wt
+  auto compute = [&](const uint4 (&wt)[4 * P], auto U) {
+    constexpr int u = decltype(U)::value;
+#pragma unroll
+    for (int st = 0; st < 16; ++st) {
+      // one word's four steps at a time, so that the scheduler does not hoist
+      // every step's LDS reads
+      if ((st & 3) == 0) __builtin_amdgcn_sched_barrier(0);
+      const int q = st >> 2, t4 = st & 3, sh = 15 - 4 * t4;
+      const int off = 16 * (4 * gl + q) + 4 * t4;
+      v8h fa[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) fa[mt] = *(const v8h*)(s_x[u] + (16 * mt + j) * kXRow + off);
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        const uint4 hh = *(const uint4*)(s_h[u][p] + off);
+#pragma unroll
+        for (int tau = 0; tau < 4; ++tau) {
+          const uint4 wv = wt[tau * P + p];
+          const uint32_t wd = q == 0 ? wv.x : q == 1 ? wv.y : q == 2 ? wv.z : wv.w;
+          uint4 e;
+          e.x = hh.x ^ ((wd << sh) & 0x80008000u);
+          e.y = hh.y ^ ((wd << (sh - 1)) & 0x80008000u);
+          e.z = hh.z ^ ((wd << (sh - 2)) & 0x80008000u);
+          e.w = hh.w ^ ((wd << (sh - 3)) & 0x80008000u);
+          const v8h fb = __builtin_bit_cast(v8h, e);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            acc[p][tau][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[mt], fb, acc[p][tau][mt], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  // ranges in pairs (stages 0 and 1, weight buffers wa and wb). Before the
+  // matrix ops of range r: this wave's stage loads of r have landed (only
+  // r's NB/4... weight loads, issued after them, may still be in flight) and
+  // every wave is done with range r - 1, whose stage the loads of r + 1 reuse
+  uint4 wa[4 * P], wb[4 * P];
+  issue(r0, std::integral_constant<int, 0>());
+  load_w(wa, r0);
+#pragma unroll 1
+  for (int r = r0; r < r1; r += 2) {
+    ring_barrier<4 * P>();
+    const bool n1 = r + 1 < r1;
+    if (n1) {
+      issue(r + 1, std::integral_constant<int, 1>());
+      load_w(wb, r + 1);
+    }
+    compute(wa, std::integral_constant<int, 0>());
+    if (!n1) break;
+    ring_barrier<4 * P>();
+    const bool n2 = r + 2 < r1;
+    if (n2) {
+      issue(r + 2, std::integral_constant<int, 0>());
+      load_w(wa, r + 2);
+    }
+    compute(wb, std::integral_constant<int, 1>());
+    if (!n2) break;
+  }
+
+  // tokens 16 mt + 4 gl + i of row 16 tau + j: Σ_p g_p acc_p 2^-e_b in float64
+  if (rg < RG) {
+    int eb[MT][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) eb[mt][i] = A.rowexp[min(16 * mt + 4 * gl + i, batch - 1)];
+#pragma unroll
+    for (int tau = 0; tau < 4; ++tau) {
+      const int row = rg * 64 + 16 * tau + j;
+      double gp[P];
+#pragma unroll
+      for (int p = 0; p < P; ++p) gp[p] = (double)f16_bits_to_f32(gsc[(size_t)p * out + min(row, out - 1)]);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int b = 16 * mt + 4 * gl + i;
+          if (b >= batch || row >= out) continue;
+          double v = gp[0] * (double)acc[0][tau][mt][i];
+#pragma unroll
+          for (int p = 1; p < P; ++p) v += gp[p] * (double)acc[p][tau][mt][i];
+          part[((size_t)b * A.nck + ck) * RG * 64 + row] = ldexp(v, -eb[mt][i]);
+        }
+    }
+  }
+}
+
 // y = Σ_r part (ascending r)
 __global__ __launch_bounds__(256) void k_gemv_reduce(const double* __restrict__ part, int out,
-                                                     int RG, int S, void* y, int y_dtype) {
+                                                     int RG, void* y, int y_dtype) {
   const int row = blockIdx.x * 256 + threadIdx.x, b = blockIdx.y;
   if (row >= out) return;
+  const int S = part_slices(part);
   // many ranges (wide layers): 32 loads in flight per round trip
-  const double* pp = part + (size_t)b * S * RG * 64 + row;
+  const double* pp = part_data(part) + (size_t)b * S * RG * 64 + row;
   const double v = S <= 8 ? sum_ranges_by<8>(pp, S, RG * 64) : sum_ranges_by<32>(pp, S, RG * 64);
   if (y_dtype == RABIT_OUT_F32)
     ((float*)y)[(size_t)b * out + row] = (float)v;
@@ -548,6 +853,60 @@ int resident_wgs(bool ring, int paths) {
     slot.store(c, std::memory_order_relaxed);
   }
   return c;
+}
+
+// Workgroups of k_gemv16<MT, P> resident at once (runtime occupancy query,
+// once per device and variant).
+int resident_wgs16(int mt, int paths) {
+  static std::atomic<int> cache[kMaxDevices][2][2];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
+  std::atomic<int>& slot = cache[dev][mt == 2 ? 1 : 0][paths == 3 ? 1 : 0];
+  int c = slot.load(std::memory_order_relaxed);
+  if (c == 0) {
+    int cus = 0, per = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+      cus = 256;
+    const void* fn = paths == 3 ? (mt == 2 ? (const void*)k_gemv16<2, 3> : (const void*)k_gemv16<1, 3>)
+                                : (mt == 2 ? (const void*)k_gemv16<2, 2> : (const void*)k_gemv16<1, 2>);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fn, 256, 0) != hipSuccess || per < 1) per = 1;
+    c = cus * per;
+    slot.store(c, std::memory_order_relaxed);
+  }
+  return c;
+}
+
+// The fp16 path's launch: row blocks of 4 row groups, chunks of kr ranges.
+// Cost model as for the digit path: passes x (kr ranges + one for staging),
+// ties to the larger kr (fewer partials to write and read back).
+struct Plan16 {
+  int S, kr, nck, mt, paths;
+  int RB[kMaxSeg];
+};
+
+__host__ inline Plan16 make_plan16(const int* outs, int nseg, int in, int batch, int paths) {
+  Plan16 P;
+  P.paths = paths;
+  P.mt = batch > 16 ? 2 : 1;
+  P.S = (in + kChunk - 1) / kChunk;
+  long rbs = 0;
+  for (int s = 0; s < nseg; ++s) {
+    P.RB[s] = (row_groups(outs[s]) + 3) / 4;
+    rbs += P.RB[s];
+  }
+  const long cap = resident_wgs16(P.mt, paths);
+  long best = -1;
+  P.kr = P.S;
+  for (int kr = P.S; kr >= 1; --kr) {
+    const long nck = (P.S + kr - 1) / kr;
+    const long cost = (rbs * nck + cap - 1) / cap * (kr + 1);
+    if (best < 0 || cost < best) {
+      best = cost;
+      P.kr = kr;
+    }
+  }
+  P.nck = (P.S + P.kr - 1) / P.kr;
+  return P;
 }
 
 // Rows per workgroup (4 m row groups). A workgroup builds the digit operand
@@ -637,29 +996,61 @@ Args make_args(const Plan& P, const uint4* planes, const uint16_t* g, const uint
 
 size_t gemv_workspace_bytes(int out, int in, int batch) {
   const int S = (in + kChunk - 1) / kChunk;
-  return part_bytes(out, S, batch);
+  return part_bytes(out, S, batch) + (batch >= kF16MinBatch ? prep_bytes(in) : 0);
+}
+
+hipError_t launch_16(const Plan16& P, Args A, int batch, hipStream_t st) {
+  int nrb = 0;
+  for (int s = 0; s < A.nseg; ++s) {
+    A.seg[s].rb0 = nrb;
+    nrb += P.RB[s];
+    // the fp16 path's area after the matrix's partial buffer
+    char* prep = (char*)A.seg[s].part + part_bytes(A.seg[s].out, P.S, batch);
+    A.seg[s].hp = (uint32_t*)(prep + xh_bytes(A.in) + kRowExpBytes);
+    if (s == 0) {
+      A.xh = (uint16_t*)prep;
+      A.rowexp = (int*)(prep + xh_bytes(A.in));
+    }
+  }
+  A.kr = P.kr;
+  A.nck = P.nck;
+  const int hthreads = A.nseg * P.paths * (P.S * kChunk / 32) * 16;
+  const int xwgs = batch * ((P.S * kChunk + kPrepCols - 1) / kPrepCols);
+  hipLaunchKernelGGL(k_gemv16_prep, dim3(xwgs + (hthreads + 255) / 256), dim3(256), 0, st, A, P.paths,
+                     xwgs);
+  const dim3 grid(nrb * P.nck);
+  if (P.paths == 3) {
+    if (P.mt == 2)
+      hipLaunchKernelGGL((k_gemv16<2, 3>), grid, dim3(256), 0, st, A);
+    else
+      hipLaunchKernelGGL((k_gemv16<1, 3>), grid, dim3(256), 0, st, A);
+  } else {
+    if (P.mt == 2)
+      hipLaunchKernelGGL((k_gemv16<2, 2>), grid, dim3(256), 0, st, A);
+    else
+      hipLaunchKernelGGL((k_gemv16<1, 2>), grid, dim3(256), 0, st, A);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_gemv_partial(const uint4* planes, const uint16_t* g, const uint16_t* h, int out,
                                int in, const uint16_t* x, int batch, void* ws, hipStream_t st,
                                int paths) {
   if (paths != 2 && paths != 3) return hipErrorInvalidValue;
-  const Plan P = make_plan(&out, 1, in, batch, paths);
-  const Args A = make_args(P, planes, g, h, out, in, x, batch, ws);
-  return launch_main(P, A, batch, st);
+  const LinSeg seg{planes, g, h, out, (double*)ws, paths};
+  return launch_gemv_multi(&seg, 1, in, x, batch, nullptr, 0.f, st);
 }
 
 hipError_t launch_gemv_reduce(int out, int in, int batch, void* y, int y_dtype, const void* ws,
-                              hipStream_t st) {
-  const int S = (in + kChunk - 1) / kChunk;
+                              hipStream_t st, int paths) {
+  (void)in;
+  (void)paths;
   hipLaunchKernelGGL(k_gemv_reduce, dim3((out + 255) / 256, batch), dim3(256), 0, st,
-                     (const double*)ws, out, row_groups(out), S, y, y_dtype);
+                     (const double*)ws, out, row_groups(out), y, y_dtype);
   return hipGetLastError();
 }
 
-size_t gemv_part_bytes(int out, int in, int batch) {
-  return part_bytes(out, (in + kChunk - 1) / kChunk, batch);
-}
+size_t gemv_part_bytes(int out, int in, int batch) { return gemv_workspace_bytes(out, in, batch); }
 
 hipError_t launch_gemv_multi(const LinSeg* segs, int nseg, int in, const uint16_t* x, int batch,
                              const double* stats, float eps, hipStream_t st) {
@@ -670,6 +1061,28 @@ hipError_t launch_gemv_multi(const LinSeg* segs, int nseg, int in, const uint16_
     if (segs[s].paths != segs[0].paths) return hipErrorInvalidValue;
   }
   if (segs[0].paths != 2 && segs[0].paths != 3) return hipErrorInvalidValue;
+  if (batch >= kF16MinBatch) {
+    const Plan16 P = make_plan16(outs, nseg, in, batch, segs[0].paths);
+    Args A = {};
+    for (int s = 0; s < nseg; ++s) {
+      A.seg[s].planes = segs[s].planes;
+      A.seg[s].g = segs[s].g;
+      A.seg[s].h = segs[s].h;
+      A.seg[s].part = segs[s].part;
+      A.seg[s].out = segs[s].out;
+      A.seg[s].RG = row_groups(segs[s].out);
+    }
+    A.x = x;
+    A.stats = stats;
+    A.nseg = nseg;
+    A.in = in;
+    A.KG = col_groups(in);
+    A.S = P.S;
+    A.batch = batch;
+    A.norm = stats ? 1 : 0;
+    A.eps = eps;
+    return launch_16(P, A, batch, st);
+  }
   const Plan P = make_plan(outs, nseg, in, batch, segs[0].paths);
   Args A = {};
   int rb0 = 0;
@@ -701,7 +1114,7 @@ hipError_t launch_gemv(const uint4* planes, const uint16_t* g, const uint16_t* h
                        hipStream_t st, int paths) {
   hipError_t e = launch_gemv_partial(planes, g, h, out, in, x, batch, ws, st, paths);
   if (e != hipSuccess) return e;
-  return launch_gemv_reduce(out, in, batch, y, y_dtype, ws, st);
+  return launch_gemv_reduce(out, in, batch, y, y_dtype, ws, st, paths);
 }
 
 }  // namespace rabit

@@ -268,7 +268,7 @@ int rabit_gemv_reduce(const rabit_layer* L, int32_t batch, void* y, int32_t y_dt
   const size_t wsb = gemv_workspace_bytes(L->out_features, L->in_features, batch);
   if (overlap(workspace, wsb, y, yb) || overlaps_layer(workspace, wsb, L)) return RABIT_EINVAL;
   return dev_status(launch_gemv_reduce(L->out_features, L->in_features, batch, y, y_dtype,
-                                       workspace, (hipStream_t)stream));
+                                       workspace, (hipStream_t)stream, L->n_paths));
 }
 
 int rabit_gemm(const rabit_layer* L, const uint16_t* X, int32_t m, void* Y, int32_t y_dtype,
@@ -515,7 +515,7 @@ hipError_t decode_gemv_path(const rabit_decoder_cfg* cfg, const rabit_layer* lay
                             const uint16_t* x, int batch, uint16_t* out, const DecodeWs& w,
                             hipStream_t st) {
   const int H = cfg->hidden, F = cfg->ffn;
-  hipError_t e = launch_resid_stats(nullptr, 0, x, nullptr, w.stats, batch, H, st);
+  hipError_t e = launch_resid_stats(nullptr, x, nullptr, w.stats, batch, H, st);
   const uint16_t* cur = x;
   for (int l = 0; l < cfg->n_layers && e == hipSuccess; ++l) {
     const rabit_layer* Ls = layers + l * 7;
@@ -523,20 +523,20 @@ hipError_t decode_gemv_path(const rabit_decoder_cfg* cfg, const rabit_layer* lay
     if (!cfg->mlp_only) {
       const LinSeg qkv[3] = {seg_of(Ls[0], w.pq), seg_of(Ls[1], w.pk), seg_of(Ls[2], w.pv)};
       if (!e) e = launch_gemv_multi(qkv, 3, H, cur, batch, w.stats, cfg->rms_eps, st);
-      if (!e) e = launch_reduce_attn(w.pq, w.pk, w.pv, H, w.qk, w.attn, batch, cfg->n_heads,
+      if (!e) e = launch_reduce_attn(w.pq, w.pk, w.pv, w.qk, w.attn, batch, cfg->n_heads,
                                      cfg->n_kv_heads, cfg->head_dim, st);
       const LinSeg o = seg_of(Ls[3], w.po);
       if (!e) e = launch_gemv_multi(&o, 1, H, w.attn, batch, nullptr, 0.f, st);
-      if (!e) e = launch_resid_stats(w.po, H, cur, nxt, w.stats, batch, H, st);
+      if (!e) e = launch_resid_stats(w.po, cur, nxt, w.stats, batch, H, st);
       cur = nxt;
     }
     const LinSeg gu[2] = {seg_of(Ls[4], w.pg), seg_of(Ls[5], w.pu)};
     if (!e) e = launch_gemv_multi(gu, 2, H, cur, batch, w.stats, cfg->rms_eps, st);
-    if (!e) e = launch_reduce_silu(w.pg, w.pu, H, w.z, batch, F, st);
+    if (!e) e = launch_reduce_silu(w.pg, w.pu, w.z, batch, F, st);
     const LinSeg dn = seg_of(Ls[6], w.pd);
     if (!e) e = launch_gemv_multi(&dn, 1, F, w.z, batch, nullptr, 0.f, st);
     // x + down may be written in place (cur == nxt when attention ran)
-    if (!e) e = launch_resid_stats(w.pd, F, cur, nxt, w.stats, batch, H, st);
+    if (!e) e = launch_resid_stats(w.pd, cur, nxt, w.stats, batch, H, st);
     cur = nxt;
   }
   return e;

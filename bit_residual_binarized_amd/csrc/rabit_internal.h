@@ -154,6 +154,44 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 }
 
 // ---------------------------------------------------------------------------
+// Direct buffer-to-LDS loads
+// ---------------------------------------------------------------------------
+// Raw (untyped, unswizzled) buffer resource word 3.
+constexpr int kBufWord3 = 0x00020000;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Direct buffer-to-LDS loads of 16 and 4 bytes per lane: lane l writes its
+// bytes at dst + size * l. (Plain device functions: inside a kernel template
+// the builtin keeps the host pass from emitting the kernel's launch handle.)
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, lds_void* dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void lds_load4(__amdgpu_buffer_rsrc_t r, lds_void* dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 4, voff, 0, 0, 0);
+}
+
+// s_waitcnt immediate: at most n vector-memory loads of this wave in flight
+// and (lgkm0) none of its LDS accesses; expcnt unconstrained
+__host__ __device__ constexpr int vmcnt_imm(int n, bool lgkm0 = false) {
+  return (n & 15) | ((n >> 4) << 14) | (7 << 4) | ((lgkm0 ? 0 : 15) << 8);
+}
+
+// Workgroup barrier after this wave's loads but the last N have landed in
+// LDS and its own LDS reads are done. A fence (__syncthreads) would wait for
+// every load in flight, direct-to-LDS ones included; the empty asm
+// statements keep the compiler from moving memory accesses across the
+// barrier instead.
+template <int N>
+__device__ __forceinline__ void ring_barrier() {
+  __builtin_amdgcn_sched_barrier(0);  // no instruction moves across a step boundary
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(N, true));
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// ---------------------------------------------------------------------------
 // Geometry of the V1 plane layout
 // ---------------------------------------------------------------------------
 __host__ __device__ __forceinline__ int row_groups(int out) { return (out + 63) / 64; }
@@ -181,10 +219,12 @@ hipError_t launch_gemv_partial(const uint4* planes, const uint16_t* g, const uin
                                int in, const uint16_t* x, int batch, void* ws, hipStream_t st,
                                int paths = 2);
 hipError_t launch_gemv_reduce(int out, int in, int batch, void* y, int y_dtype, const void* ws,
-                              hipStream_t st);
+                              hipStream_t st, int paths = 2);
+
 
 // Several matrices that read the same input in one launch (q/k/v, gate/up):
-// each leaves float64 partials [batch][ceil(in/512)][64*ceil(out/64)] in part.
+// each leaves its partial buffer (header, then float64 partials
+// [batch][slices][64*ceil(out/64)], slices at most ceil(in/512)) in part.
 // With stats != nullptr the input is RMSNorm(x) (unit weight, eps), rounded to
 // bfloat16, with stats[b][RABIT_STAT_PARTS] the partial sums of x^2 of row b.
 struct LinSeg {
@@ -196,6 +236,13 @@ struct LinSeg {
   int paths = 2;  // every segment of a launch has the same number of paths
 };
 #define RABIT_STAT_PARTS 32
+
+// A GEMV launch's partial buffer for one matrix: a 256-byte header whose
+// first int32 is the number of partial slices per output row, then the
+// float64 partials [batch][slices][64*ceil(out/64)].
+constexpr int kPartHdrDoubles = 32;
+__host__ __device__ __forceinline__ int part_slices(const double* part) { return *(const int*)part; }
+__host__ __device__ __forceinline__ const double* part_data(const double* part) { return part + kPartHdrDoubles; }
 
 // Σ_r part[b][r][i] over the S ranges of a GEMV's float64 partials (row
 // stride `stride`), added in ascending r, with the loads of C ranges in flight
@@ -213,9 +260,10 @@ __device__ __forceinline__ double sum_ranges_by(const double* __restrict__ pp, i
   }
   return v;
 }
-__device__ __forceinline__ double sum_ranges(const double* __restrict__ part, int b, int S,
-                                             int stride, int i) {
-  return sum_ranges_by<8>(part + (size_t)b * S * stride + i, S, stride);
+// (part: the matrix's whole partial buffer, header included)
+__device__ __forceinline__ double sum_ranges(const double* __restrict__ part, int b, int stride, int i) {
+  const int S = part_slices(part);
+  return sum_ranges_by<8>(part_data(part) + (size_t)b * S * stride + i, S, stride);
 }
 size_t gemv_part_bytes(int out, int in, int batch);
 hipError_t launch_gemv_multi(const LinSeg* segs, int nseg, int in, const uint16_t* x, int batch,
@@ -254,18 +302,18 @@ hipError_t launch_silu_mul(const float* gate, const float* up, uint16_t* z, int 
                            hipStream_t st);
 hipError_t launch_residual_add(const uint16_t* x, const float* d, uint16_t* out, int batch, int n,
                                hipStream_t st);
-// fused consumers of GEMV partials (S = ceil(in/512) ranges, row stride 64*ceil(out/64))
+// fused consumers of GEMV partial buffers (header with the slice count, row stride 64*ceil(out/64))
 // x_out = bf16(x + Σ part) (part == nullptr: x_out unused, x itself), and the
 // RABIT_STAT_PARTS partial sums of x_out^2 per row
-hipError_t launch_resid_stats(const double* part, int in_of_part, const uint16_t* x, uint16_t* x_out,
+hipError_t launch_resid_stats(const double* part, const uint16_t* x, uint16_t* x_out,
                               double* stats, int batch, int n, hipStream_t st);
 // a = bf16(silu(Σ gate part) * Σ up part)
-hipError_t launch_reduce_silu(const double* pg, const double* pu, int in_of_part, uint16_t* a,
+hipError_t launch_reduce_silu(const double* pg, const double* pu, uint16_t* a,
                               int batch, int n, hipStream_t st);
 // q, k: fp32 sums (kept in qk); v = bf16(Σ part); attention over a one-token
 // context returns, per head, its key/value group's v
 hipError_t launch_reduce_attn(const double* pq, const double* pk, const double* pv,
-                              int in_of_part, float* qk, uint16_t* attn, int batch, int n_heads,
+                              float* qk, uint16_t* attn, int batch, int n_heads,
                               int n_kv_heads, int head_dim, hipStream_t st);
 hipError_t launch_test_f64_to_16(const double* in, uint16_t* out, int n, int bf16, hipStream_t st);
 hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t st);

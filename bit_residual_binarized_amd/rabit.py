@@ -31,6 +31,7 @@ RABIT_OUT_F32 = 0
 RABIT_OUT_BF16 = 1
 RABIT_LAYOUT_V1 = 1
 MAX_GEMV_BATCH = 32
+GEMV_FP16_MIN_BATCH = 8   # RABIT_GEMV_FP16_MIN_BATCH: batches from here on use the fp16 matrix-core path
 
 # every symbol include/rabit.h declares
 EXPORTS = [

@@ -85,6 +85,9 @@ enum {
 /* Largest supported dimensions (out_features, in_features, batch, M). */
 #define RABIT_MAX_FEATURES (1 << 19)
 #define RABIT_MAX_GEMV_BATCH 32
+/* Batches from this size on run the decode GEMV on fp16 matrix cores (see
+   rabit_gemv); smaller ones on the exact fixed-point path. */
+#define RABIT_GEMV_FP16_MIN_BATCH 8
 #define RABIT_MAX_GEMM_M (1 << 20)
 
 /*
@@ -170,13 +173,25 @@ int rabit_unpack(const rabit_layer *layer, uint32_t *words, void *stream);
  * batch   1 .. RABIT_MAX_GEMV_BATCH.
  * y       device [batch][out], float32 (RABIT_OUT_F32) or bfloat16
  *         (RABIT_OUT_BF16), written entirely.
- * Arithmetic: h_p*x is formed exactly and held as a fixed-point integer per
- * (batch row, path, range of 512 input columns), scaled by a power of two so
- * that the range's largest |h_p*x| maps into [2^18, 2^19) (per-element error
- * <= 2^-19 of that largest value); the signed sums are exact integers; each
- * range's g_1 S_1 + g_2 S_2 is formed in float64, the ranges are summed in
- * float64 in ascending order and the result is rounded once.
- * Result is bitwise repeatable (no order-dependent arithmetic).
+ * Arithmetic, batch < RABIT_GEMV_FP16_MIN_BATCH: h_p*x is formed exactly and
+ * held as a fixed-point integer per (batch row, path, range of 512 input
+ * columns), scaled by a power of two so that the range's largest |h_p*x| maps
+ * into [2^18, 2^19) (per-element error <= 2^-19 of that largest value); the
+ * signed sums are exact integers; each range's g_1 S_1 + g_2 S_2 is formed in
+ * float64, the ranges are summed in float64 in ascending order and the result
+ * is rounded once.
+ * Arithmetic, batch >= RABIT_GEMV_FP16_MIN_BATCH: each token row of x is
+ * scaled by a power of two 2^e so that its largest |x| lies in [2^14, 2^15)
+ * and rounded to fp16 (exact for values above 2^-32 of that largest one, the
+ * rest off by at most 2^-25 2^-e); the products with ±h_p are exact and
+ * summed in fp32 over chunks of consecutive 512-column ranges (at most
+ * in_features + 16 ceil(in/512) roundings, each within 2^-24 of a running sum
+ * bounded by Σ_j |h_p[j] x[j]|); per chunk Σ_p g_p acc_p 2^-e is formed in
+ * float64, the chunks are summed in float64 in ascending order and the result
+ * is rounded once.
+ * Result is bitwise repeatable (no order-dependent arithmetic); a batch row's
+ * result depends only on that row, for batches of the same arithmetic and
+ * token tile (up to 16 rows, or 17 to 32).
  * workspace must not overlap x or y.
  */
 int rabit_gemv(const rabit_layer *layer, const uint16_t *x, int32_t batch,

@@ -74,10 +74,36 @@ def fx_bound(d, xv):
     return bound
 
 
+def f16_bound(d, xv):
+    """Elementwise error bound of the fp16 matrix-core path (batches from
+    RABIT_GEMV_FP16_MIN_BATCH on), as rabit.h states it.
+
+    Per (token, chunk of ranges) x is scaled by a power of two, 2^-e at most
+    max|x| / 2^14, and rounded to fp16 (exact above 2^-32 of the chunk's
+    largest |x|; below that off by at most 2^-25 2^-e); the products with
+    ±h_p are exact and summed in fp32 over the chunk (at most in + 16 S
+    roundings, each within 2^-24 of a running sum bounded by Σ|h_p x|); g_p is
+    applied in float64."""
+    xb = np.atleast_2d(xv)
+    B, K = xb.shape
+    S = -(-K // 512)
+    bound = np.zeros((B, d.g1.shape[0]))
+    xmax = np.abs(xb).max(axis=1)
+    for s_, g, h in d.paths:
+        ha = np.abs(h.astype(np.float64))
+        acc = (K + 16 * S) * 2.0 ** -24 * (np.abs(xb) @ ha) + ha.sum() * 2.0 ** -25 * xmax * 2.0 ** -14
+        bound += np.abs(g.astype(np.float64))[None, :] * acc[:, None]
+    return bound
+
+
 def check_fx(y, ref, d, xv):
-    bound = fx_bound(d, xv) + 2.0 ** -23 * np.abs(ref) + 1e-300
+    """The elementwise bound of the arithmetic the batch size selects."""
+    from bit_residual_binarized_amd import rabit
+    xb = np.atleast_2d(xv)
+    fx = f16_bound(d, xb) if xb.shape[0] >= rabit.GEMV_FP16_MIN_BATCH else fx_bound(d, xb)
+    bound = fx + 2.0 ** -23 * np.abs(ref) + 1e-300
     bad = np.argwhere(np.abs(y - ref) > bound)
-    assert bad.size == 0, f"{len(bad)} outputs outside the fixed-point bound, first {bad[:3].tolist()}"
+    assert bad.size == 0, f"{len(bad)} outputs outside the bound, first {bad[:3].tolist()}"
 
 
 PACK_SHAPES = [(4, 8), (64, 256), (100, 300), (130, 1000), (1, 1), (65, 129), (256, 4096),
@@ -228,7 +254,7 @@ def test_gemv_partial_reduce_equals_gemv(gpu_lib, shape):
     out, inp = shape
     say("gemv partial/reduce", shape)
     layer = pack_gpu(gpu_lib, weight_f32(out, inp, 8))
-    for batch in (1, 3):
+    for batch in (1, 3, 12):
         x = act_bf16(batch, inp, 9 + batch).cuda()
         ws = gpu_lib.gemv_workspace(layer, batch)
         y = torch.empty(batch, out, device="cuda")
@@ -241,7 +267,7 @@ def test_gemv_partial_multi_equals_gemv(gpu_lib):
     say("gemv partial multi")
     inp = 1100
     layers = [pack_gpu(gpu_lib, weight_f32(o, inp, 20 + o)) for o in (300, 64, 130)]
-    for batch in (1, 2, 5):
+    for batch in (1, 2, 5, 9, 32):
         x = act_bf16(batch, inp, 30 + batch).cuda()
         ws = gpu_lib.gemv_multi_workspace(layers, batch)
         views = gpu_lib.gemv_partial_multi(layers, x, ws)
@@ -419,3 +445,64 @@ def test_pack_meanabs_normalized_three_paths_and_zero(gpu_lib):
         assert np.array_equal(layer.h[p].cpu().numpy().view(np.uint16), h.view(np.uint16)), p
     z = pack_gpu(gpu_lib, torch.zeros(64, 300), gpu_lib.RABIT_SCALES_MEANABS_NORMALIZED)
     assert not z.g.any() and not z.h.any() and not z.planes.any()
+
+
+# The fp16 matrix-core path (batches 8 .. 32): ragged shapes, a chunk that
+# ends inside the last range, three paths, bf16 output, outlier and tiny
+# activations, zero token rows.
+F16_CASES = [(65, 129, 8), (300, 1100, 31), (1024, 4096, 16), (130, 5000, 17), (4096, 14336, 32), (256, 4100, 12),
+             (2048, 8192, 24)]
+
+
+@pytest.mark.parametrize("case", F16_CASES)
+def test_gemv_fp16_path(gpu_lib, case):
+    out, inp, batch = case
+    say("gemv fp16 path", case)
+    w = weight_f32(out, inp, 8000 + out + batch)
+    layer = pack_gpu(gpu_lib, w)
+    d = oracle.derive(w.numpy())
+    x = act_bf16(batch, inp, 8100 + batch)
+    x[0, inp // 3] = 2000.0                 # an outlier sets token 0's exponent
+    x[1, :] = 0.0                           # a zero token row
+    x[2, : min(inp, 700)] = 1e-30           # tiny values in the first ranges
+    xv = bf16_values(x)
+    y = gpu_lib.gemv(layer, x.cuda()).cpu().numpy().astype(np.float64)
+    ref = oracle.gemv(d, xv)
+    err = oracle.normwise_rel_err(np.delete(y, 1, 0), np.delete(ref, 1, 0))
+    say("  normwise err", err)
+    assert err < TOL
+    assert not y[1].any()
+    check_fx(y, ref, d, xv)
+    yb = gpu_lib.gemv(layer, x.cuda(), y_dtype=gpu_lib.RABIT_OUT_BF16).cpu().to(torch.float32).numpy()
+    assert oracle.normwise_rel_err(np.delete(yb.astype(np.float64), 1, 0), np.delete(ref, 1, 0)) < 2 ** -8
+
+
+def test_gemv_fp16_path_three_paths(gpu_lib):
+    out, inp, batch = 500, 3000, 20
+    say("gemv fp16 path, three paths")
+    w = weight_f32(out, inp, 8200)
+    layer = gpu_lib.PackedLayer.empty(out, inp, n_paths=3)
+    gpu_lib.pack(w.cuda(), layer)
+    d = oracle.derive(w.numpy(), n_paths=3)
+    x = act_bf16(batch, inp, 8201)
+    xv = bf16_values(x)
+    y = gpu_lib.gemv(layer, x.cuda()).cpu().numpy().astype(np.float64)
+    ref = oracle.gemv(d, xv)
+    assert oracle.normwise_rel_err(y, ref) < TOL
+    bound = f16_bound(d, xv) + 2.0 ** -23 * np.abs(ref)
+    assert (np.abs(y - ref) <= bound).all()
+
+
+def test_gemv_rows_same_for_every_batch_on_fp16_path(gpu_lib):
+    # a token's result does not depend on the other tokens of the batch
+    # (exponents per token, no cross-token arithmetic): batches that share a
+    # launch plan (token tiles of 16 up to batch 16, of 32 above) agree bit
+    # for bit
+    out, inp = 1024, 4096
+    say("gemv fp16 path: rows independent of the batch")
+    layer = pack_gpu(gpu_lib, weight_f32(out, inp, 8300))
+    x = act_bf16(32, inp, 8301).cuda()
+    for lo, hi in ((9, 16), (17, 32)):
+        yhi = gpu_lib.gemv(layer, x[:hi].contiguous())
+        ylo = gpu_lib.gemv(layer, x[:lo].contiguous())
+        assert torch.equal(yhi[:lo], ylo), (lo, hi)

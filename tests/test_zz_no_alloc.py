@@ -28,7 +28,8 @@ def _layer(rabit, out, inp, seed, n_paths=2):
 
 def test_gemv_noalloc_matches_gemv(gpu_lib):
     rabit = gpu_lib
-    cases = [(4096, 11008, 4, 2), (1000, 3000, 1, 2), (8192, 28672, 1, 2), (300, 1100, 3, 3)]
+    cases = [(4096, 11008, 4, 2), (1000, 3000, 1, 2), (8192, 28672, 1, 2), (300, 1100, 3, 3),
+             (2048, 4096, 12, 2), (300, 1100, 3, 2)]
     prev = None
     for out, inp, batch, P in cases:
         say("gemv_noalloc", out, inp, "batch", batch, "paths", P)
