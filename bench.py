@@ -460,6 +460,86 @@ def _line(metric, value, unit, config, higher=True, **kw):
     return d
 
 
+def _blas_info():
+    try:
+        from threadpoolctl import threadpool_info
+        return [(t.get("internal_api"), t.get("num_threads")) for t in threadpool_info()]
+    except Exception:  # pragma: no cover
+        return []
+
+
+def cpu_baseline_layers(rabit, shapes, cfg_id, batches=(1,)):
+    """The oracle (float64 numpy) on the host over whole matrices: derive with
+    mean-|.| scales and pack each matrix (timed), then its GEMV (W_eff
+    reconstruction + product) at each batch. value = plane bytes / GEMV time
+    at batch 1 (all matrices)."""
+    import numpy as np
+    import oracle
+    from synth.inputs import act_bf16, bf16_values, seed_w, seed_x, weight_f32
+    t_derive, t_gemv = 0.0, {b: 0.0 for b in batches}
+    weights = 0
+    for k, (name, (o, i)) in enumerate(shapes.items()):
+        w = weight_f32(o, i, seed_w(cfg_id, 0, name)).numpy()
+        t0 = time.perf_counter()
+        d = oracle.derive(w)
+        oracle.pack_words(d.s1), oracle.pack_words(d.s2)
+        t_derive += time.perf_counter() - t0
+        d.r = None
+        weights += o * i
+        del w
+        for b in batches:
+            x = bf16_values(act_bf16(b, i, seed_x(cfg_id, b)))
+            t0 = time.perf_counter()
+            oracle.gemv(d, x)
+            t_gemv[b] += time.perf_counter() - t0
+        del d
+    planes = sum(rabit.planes_bytes(o, i) for o, i in shapes.values())
+    return {
+        "value": round(planes / t_gemv[batches[0]] / 1e9, 5), "unit": "GB/s",
+        "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+        "sample": (f"the whole workload ({weights / 1e6:.0f} M weights): oracle mean-|.| derive + pack of every "
+                   "matrix, then its float64 GEMV (W_eff reconstruction + product) at batch "
+                   + ", ".join(str(b) for b in batches) + "; GB/s of packed-plane bytes at batch "
+                   + str(batches[0])),
+        "derive_pack_s": round(t_derive, 3),
+        "gemv_s": {str(b): round(v, 3) for b, v in t_gemv.items()},
+        "blas_threads": _blas_info(),
+    }
+
+
+def cpu_baseline_gemm(rabit, NK, Ms=(512, 2048, 8192), rows=256):
+    """The oracle's prefill GEMM (W_eff in float64, then X W_eff^T): M = 512 in
+    full, larger M on `rows` token rows, extrapolated linearly in M."""
+    import oracle
+    from synth.inputs import act_bf16, bf16_values, seed_w, seed_x, weight_f32
+    res, tot_flop, tot_s = {}, 0.0, 0.0
+    for (N, K) in NK:
+        w = weight_f32(N, K, seed_w(4, 0, "gate" if N > K else "down")).numpy()
+        t0 = time.perf_counter()
+        d = oracle.derive(w)
+        t_derive = time.perf_counter() - t0
+        d.r = None
+        del w
+        for M in Ms:
+            xm = bf16_values(act_bf16(M, K, seed_x(4, M)))
+            sub = None if M <= 512 else list(range(0, M, max(1, M // rows)))[:rows]
+            n = M if sub is None else len(sub)
+            t0 = time.perf_counter()
+            oracle.gemm(d, xm, rows=sub)
+            dt = time.perf_counter() - t0
+            full = dt * M / n
+            res[f"{N}x{K}_M{M}"] = {"s": round(full, 3), "extrapolated": sub is not None,
+                                    "tflops": round(4.0 * M * N * K / full / 1e12, 5)}
+            tot_flop += 4.0 * M * N * K
+            tot_s += full
+        res[f"{N}x{K}_derive_s"] = round(t_derive, 3)
+    return {"value": round(tot_flop / tot_s / 1e12, 5), "unit": "TFLOP/s", "cores": len(os.sched_getaffinity(0)),
+            "kind": "oracle",
+            "sample": (f"Llama-3-8B MLP shapes, M = 512 whole and {rows} token rows at M = 2048, 8192 "
+                       "(extrapolated linearly in M, labelled): oracle W_eff reconstruction + float64 product"),
+            "runs": res, "blas_threads": _blas_info()}
+
+
 def bench_layer4096(args, rabit, torch):
     """One 4096x4096 layer: derive+pack then batch-1 GEMV, over 128 cold copies."""
     from synth.inputs import act_bf16, seed_w, seed_x
@@ -479,6 +559,7 @@ def bench_layer4096(args, rabit, torch):
     pb = rabit.planes_bytes(4096, 4096)
     pk = sorted(packs[2:])[len(packs[2:]) // 2]
     alg = gemv_alg_bytes(4096, 4096)
+    cpu = None if args.no_cpu_baseline else cpu_baseline_layers(rabit, {"q": (4096, 4096)}, 1)
     return _line("4096x4096 residual-binary GEMV packed-weight GB/s (batch 1, cold)",
                  round(pb / (full * 1e-3) / 1e9, 1), "GB/s",
                  {"workload": "single-layer-4096x4096-b1", "copies": n}, dtype="fp4xfp6",
@@ -487,7 +568,8 @@ def bench_layer4096(args, rabit, torch):
                            "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(alg / (part * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                            "kernel": "k_gemv<1>"},
-                 derive_pack={"ms": round(pk, 4), "gbs": round(8.25 * 4096 * 4096 / (pk * 1e-3) / 1e9, 1)})
+                 derive_pack={"ms": round(pk, 4), "gbs": round(8.25 * 4096 * 4096 / (pk * 1e-3) / 1e9, 1)},
+                 cpu_baseline=cpu)
 
 
 def bench_table7(args, rabit, torch):
@@ -650,10 +732,14 @@ def bench_llama3_8b(args, rabit, torch):
         sweep[b] = {"ms_per_step": round(ms, 4), "plane_gbs": round(planes / (ms * 1e-3) / 1e9, 1),
                     "tokens_per_s": round(b * 1e3 / ms, 1)}
         log(f"llama3-8b batch {b}: {ms:.3f} ms/step, {sweep[b]['plane_gbs']} GB/s")
+    cpu = None if args.no_cpu_baseline else cpu_baseline_layers(
+        rabit, layer_shapes(H, F, kv), 3, batches=(1,))
     return _line("Llama-3-8B decode step, packed-weight GB/s at batch 1 (sweep 1..16)",
                  sweep[1]["plane_gbs"], "GB/s",
                  {"workload": "llama3-8b-decode-32-layers", "batch": [1, 2, 4, 8, 16],
-                  "plane_bytes_per_step": planes}, dtype="fp4xfp6", sweep=sweep)
+                  "plane_bytes_per_step": planes}, dtype="fp4xfp6", sweep=sweep,
+                 cpu_baseline=cpu, cpu_baseline_note="the oracle over one layer's seven matrices (the step "
+                 "repeats them 32 times)")
 
 
 def bench_gemm(args, rabit, torch):
@@ -709,9 +795,10 @@ def bench_gemm(args, rabit, torch):
                 log(f"gemm weff P={P} {N}x{K} M={M}: {ms:.3f} ms {tf:.1f} dense-equivalent TFLOP/s")
                 del X, ws, Y
     best = max(v["tflops"] for v in res.values())
+    cpu = None if args.no_cpu_baseline else cpu_baseline_gemm(rabit, ((14336, 4096), (4096, 14336)))
     return _line("Residual-binary prefill GEMM TFLOP/s (4 M N K, fp16 MFMA)", best, "TFLOP/s",
                  {"workload": "llama3-8b-mlp-gemm", "M": [512, 2048, 8192]}, dtype="fp16",
-                 runs=res, runs_3bit=res3, runs_weff=resw,
+                 runs=res, runs_3bit=res3, runs_weff=resw, cpu_baseline=cpu,
                  roofline={"bound": "mfma", "peak": 2500.0, "unit": "TFLOP/s",
                                      "achieved": best, "frac": round(best / 2500.0, 4)})
 
