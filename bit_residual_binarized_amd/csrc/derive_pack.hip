@@ -290,7 +290,7 @@ __global__ __launch_bounds__(256) void k_unpack(const uint4* __restrict__ planes
 __global__ void k_test_f64_to_16(const double* __restrict__ in, uint16_t* __restrict__ out, int n,
                                  int bf16) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) out[i] = bf16 ? f64_to_bf16_rne(in[i]) : f64_to_f16_rne(in[i]);
+  if (i < n) out[i] = bf16 == 2 ? f64_to_bf16_rne_fast(in[i]) : bf16 ? f64_to_bf16_rne(in[i]) : f64_to_f16_rne(in[i]);
 }
 
 }  // namespace

@@ -139,7 +139,7 @@ __device__ __forceinline__ uint16_t f64_to_bf16_rne_fast(double d) {
   const uint32_t e = (uint32_t)(b >> 52) & 0x7FFu;
   if (e >= 897u && e <= 1150u) {
     const uint64_t r = (b & 0x7FFFFFFFFFFFFFFFull) - ((uint64_t)896 << 52);
-    const uint64_t q = (r + 0x1FFFFFFFFFFFull + ((r >> 45) & 1)) >> 45;
+    const uint64_t q = (r + 0xFFFFFFFFFFFull + ((r >> 45) & 1)) >> 45;  // + 2^44 - 1 + lsb: half to even
     return (uint16_t)(((b >> 63) << 15) | q);
   }
   return f64_to_bf16_rne_slow(d);

@@ -486,7 +486,8 @@ def stream_read(t: torch.Tensor, sink: torch.Tensor | None = None, stream=None) 
     return sink
 
 
-def test_f64_to_16(v: torch.Tensor, bf16: bool, stream=None) -> torch.Tensor:
+def test_f64_to_16(v: torch.Tensor, bf16: int, stream=None) -> torch.Tensor:
+    """bf16: 0 fp16, 1 bfloat16, 2 the short bfloat16 path of the RMSNorm prologues."""
     lib = load()
     assert v.dtype == torch.float64 and v.is_cuda
     out = torch.empty(v.numel(), dtype=torch.int16, device=v.device)

@@ -437,7 +437,8 @@ int32_t rabit_layout_version(void);
 
 /*
  * Test hook: the library's float64 -> fp16 (bf16 = 0) or -> bfloat16
- * (bf16 = 1) round-to-nearest-even, as used for the scales and outputs.
+ * (bf16 = 1) round-to-nearest-even, as used for the scales and outputs;
+ * bf16 = 2: the short bfloat16 path the RMSNorm prologues use (same result).
  * in: device float64 [n]; out: device uint16 [n].
  */
 int rabit_test_f64_to_16(const double *in, uint16_t *out, int32_t n, int32_t bf16, void *stream);

@@ -178,6 +178,17 @@ def test_f64_to_f16_and_bf16_rounding(gpu_lib):
     gotb = gpu_lib.test_f64_to_16(torch.from_numpy(vb).cuda(), bf16=True).cpu().numpy().view(np.uint16)
     refb = oracle.bf16_rne(vb).astype(np.float32).view(np.uint32) >> 16
     assert np.array_equal(gotb, refb.astype(np.uint16))
+    # the short path of the RMSNorm prologues: halfway cases of every binade's
+    # mantissa pattern both ways, random values, the carry into the exponent
+    # and the edges of its range (outside it: the general conversion)
+    mant = rng.integers(0, 128, 50000)
+    ex = rng.integers(-130, 128, 50000)
+    half = (1.0 + mant / 128.0 + 2.0 ** -8) * np.exp2(ex.astype(np.float64))  # exactly halfway
+    vf = np.concatenate([vb, half, -half, np.nextafter(half, 0), np.nextafter(half, np.inf),
+                         [2.0 ** -126, 2.0 ** -127, 2.0 ** 127 * (2 - 2.0 ** -9), 2.0 ** 128, 1.0 - 2.0 ** -10]])
+    gotf = gpu_lib.test_f64_to_16(torch.from_numpy(vf).cuda(), bf16=2).cpu().numpy().view(np.uint16)
+    reff = oracle.bf16_rne(vf).astype(np.float32).view(np.uint32) >> 16
+    assert np.array_equal(gotf, reff.astype(np.uint16))
 
 
 GEMV_SHAPES = [(4, 8), (64, 256), (100, 300), (130, 1000), (65, 129), (1, 4096), (4096, 4096),
