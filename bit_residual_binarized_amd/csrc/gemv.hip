@@ -81,6 +81,7 @@ struct Args {
   uint16_t* xh;           // fp16 path: prepared x [batch][Kp] (contraction order)
   int* rowexp;            // fp16 path: per token, the power of two applied to x
   float eps;
+  GemvXSrc xs;            // digit path: input formed from partial buffers
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -157,7 +158,7 @@ __device__ __forceinline__ void deposit_digits(uint32_t (&dw)[kImgDw], const int
 // group 4 m rb + 4 k + w. Lane l = j + 16 g loads, per tile tau and path p,
 // the 16-byte unit (rg, 4 r + g, p, 16 tau + j): 128 columns of row
 // 16 tau + j, bit 4e + t of dword q being column 32 q + 4 e + t of the group.
-template <int NBP, bool RING, bool GROUPED, int P>
+template <int NBP, bool RING, bool GROUPED, int P, int XM = XSRC_X>
 __global__ __launch_bounds__(256) void k_gemv(Args A) {
   // Work item (row block, range) and batch group of this workgroup. With
   // several batch groups (GROUPED), the groups of one item are adjacent in
@@ -218,6 +219,69 @@ __global__ __launch_bounds__(256) void k_gemv(Args A) {
   __shared__ int s_sh[NBP][2][P];
   __shared__ int s_U[NBP][2][P];
 
+  // ---- input formed from the previous launch's partials (batch 1) ----------
+  // Their loads go out first, ahead of h and the weights, so that they do not
+  // queue behind the weight stream: 16 slices of each of the NS sums (2
+  // columns per thread, and gate and up for SiLU), and for the attention
+  // input this workgroup's share of the q and k sums (kept in fp32).
+  constexpr int NS = XM == XSRC_ATTN ? 2 : XM == XSRC_SILU ? 4 : 1;
+  constexpr int kFormC = XM == XSRC_X ? 1 : 32 / NS;  // slices per chunk: 32 loads in flight
+  double ft[NS][kFormC], acc[NS];
+  const double* fsrc[NS];
+  int fS = 0, fstride = 1;
+  double sq[XM == XSRC_ATTN ? kFormC : 1];
+  int sq_row = -1, sq_S = 0, sq_stride = 1;
+  const double* sq_src = nullptr;
+  if constexpr (XM != XSRC_X) {
+    fS = part_slices(A.xs.pa);
+    fstride = 64 * (((XM == XSRC_ATTN ? A.xs.kv : A.in) + 63) / 64);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int cc = min(col0 + tid + 256 * k, A.in - 1);
+      if constexpr (XM == XSRC_ATTN) {
+        const int hd = A.xs.head_dim, hh = cc / hd, d = cc - hh * hd;
+        fsrc[k] = part_data(A.xs.pa) + (hh / A.xs.rep) * hd + d;
+      } else {
+        fsrc[k] = part_data(A.xs.pa) + cc;
+        fsrc[k + 2] = part_data(A.xs.pb) + cc;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NS; ++i)
+#pragma unroll
+      for (int u = 0; u < kFormC; ++u) ft[i][u] = fsrc[i][(size_t)min(u, fS - 1) * fstride];
+    if constexpr (XM == XSRC_SILU) {
+      // gate and up: the first 8 slices are added before the next 8 go out
+      // (with h and the weights), to bound the registers held
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        acc[i] = 0.0;
+#pragma unroll
+        for (int u = 0; u < kFormC; ++u) acc[i] += u < fS ? ft[i][u] : 0.0;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < NS; ++i)
+#pragma unroll
+        for (int u = 0; u < kFormC; ++u) ft[i][u] = fsrc[i][(size_t)min(kFormC + u, fS - 1) * fstride];
+    }
+    if constexpr (XM == XSRC_ATTN) {
+      // rows [wid per, wid per + per) of q then k: the first 256 preloaded
+      // here, one per thread (any further ones after the rounds)
+      const int rows = A.xs.n_q + A.xs.kv, per = (rows + A.items - 1) / A.items;
+      const int row = wid * per + tid;
+      if (grp == 0 && tid < per && row < rows) {
+        const bool isq = row < A.xs.n_q;
+        sq_row = row;
+        sq_src = part_data(isq ? A.xs.pq : A.xs.pk) + (isq ? row : row - A.xs.n_q);
+        sq_S = part_slices(isq ? A.xs.pq : A.xs.pk);
+        sq_stride = 64 * (((isq ? A.xs.n_q : A.xs.kv) + 63) / 64);
+#pragma unroll
+        for (int u = 0; u < kFormC; ++u) sq[u] = sq_src[(size_t)min(u, sq_S - 1) * sq_stride];
+      }
+    }
+  }
+
   // ---- digit operand of this range, pair by pair ---------------------------
   // element e = tid + 256 k (k = 0, 1) of the range: column col0 + e
   // loads are unconditional (clamped indices) and masked afterwards, so that
@@ -229,13 +293,14 @@ __global__ __launch_bounds__(256) void k_gemv(Args A) {
     const int cc = min(col, in - 1);
 #pragma unroll
     for (int p = 0; p < P; ++p) hv[p][k] = hsc[(size_t)p * in + cc];
+    if constexpr (XM == XSRC_X)
 #pragma unroll
-    for (int q = 0; q < NBP; ++q)
+      for (int q = 0; q < NBP; ++q)
 #pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        const int b = 2 * (bp0 + q) + hb;
-        xv[q][hb][k] = A.x[(size_t)min(b, batch - 1) * in + cc];
-      }
+        for (int hb = 0; hb < 2; ++hb) {
+          const int b = 2 * (bp0 + q) + hb;
+          xv[q][hb][k] = A.x[(size_t)min(b, batch - 1) * in + cc];
+        }
   }
   // RMSNorm input: lane l < kStatParts holds partial sum l of x^2 of each
   // batch row (added by a fixed DPP tree below)
@@ -254,6 +319,35 @@ __global__ __launch_bounds__(256) void k_gemv(Args A) {
   __builtin_amdgcn_sched_barrier(0);
   load_round(w0, g0, 0);
   __builtin_amdgcn_sched_barrier(0);  // keep every load above the first use of x and h
+  if constexpr (XM != XSRC_X) {
+    // the formed input: each sum's slices added in ascending order (the
+    // chunks in flight, then any further ones)
+    const int r_in_flight = XM == XSRC_SILU ? kFormC : 0;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      if (XM != XSRC_SILU) acc[i] = 0.0;
+#pragma unroll
+      for (int u = 0; u < kFormC; ++u) acc[i] += r_in_flight + u < fS ? ft[i][u] : 0.0;
+    }
+    for (int r = r_in_flight + kFormC; r < fS; r += kFormC) {
+#pragma unroll
+      for (int i = 0; i < NS; ++i)
+#pragma unroll
+        for (int u = 0; u < kFormC; ++u) ft[i][u] = fsrc[i][(size_t)min(r + u, fS - 1) * fstride];
+#pragma unroll
+      for (int i = 0; i < NS; ++i)
+#pragma unroll
+        for (int u = 0; u < kFormC; ++u) acc[i] += r + u < fS ? ft[i][u] : 0.0;
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      if constexpr (XM == XSRC_ATTN)
+        xv[0][0][k] = f64_to_bf16_rne(acc[k]);
+      else
+        xv[0][0][k] = f64_to_bf16_rne(acc[k] / (1.0 + exp(-acc[k])) * acc[k + 2]);
+      xv[0][1][k] = 0;
+    }
+  }
   if (A.norm) {
     // x <- bf16(x / sqrt(mean(x^2) + eps)), the partial sums added in order
 #pragma unroll
@@ -513,6 +607,18 @@ __global__ __launch_bounds__(256) void k_gemv(Args A) {
     }
   };
 
+  if constexpr (XM == XSRC_ATTN) {
+    // this thread's q or k row (batch 1), slices in ascending order
+    if (sq_row >= 0) {
+      double v = 0.0;
+#pragma unroll
+      for (int u = 0; u < kFormC; ++u) v += u < sq_S ? sq[u] : 0.0;
+      for (int r = kFormC; r < sq_S; r += kFormC)
+        for (int u = 0; u < kFormC && r + u < sq_S; ++u) v += sq_src[(size_t)(r + u) * sq_stride];
+      A.xs.qk[sq_row] = (float)v;
+    }
+  }
+
   // rounds in pairs, so that each ring buffer is a fixed register array
 #pragma unroll 1
   for (int k = 0; k < m; k += 2) {
@@ -533,6 +639,19 @@ __global__ __launch_bounds__(256) void k_gemv(Args A) {
       if (k + 2 < m) load_round(w0, g0, k + 2);
       round(w1, g1, k + 1);
     }
+  }
+
+  if constexpr (XM == XSRC_ATTN) {
+    // rows of this work item's q/k share beyond the first 256 (small launches)
+    const int rows = A.xs.n_q + A.xs.kv, per = (rows + A.items - 1) / A.items;
+    if (grp == 0)
+      for (int e = 256 + tid; e < per; e += 256) {
+        const int row = wid * per + e;
+        if (row >= rows) break;
+        const bool isq = row < A.xs.n_q;
+        const int stride = 64 * (((isq ? A.xs.n_q : A.xs.kv) + 63) / 64);
+        A.xs.qk[row] = (float)sum_ranges(isq ? A.xs.pq : A.xs.pk, 0, stride, isq ? row : row - A.xs.n_q);
+      }
   }
 }
 
@@ -835,19 +954,24 @@ __global__ __launch_bounds__(256) void k_gemv_reduce(const double* __restrict__ 
 
 // Workgroups of one variant that fit on the device at once (occupancy from
 // the runtime, queried once per device and variant).
-int resident_wgs(bool ring, int paths) {
-  static std::atomic<int> cache[kMaxDevices][2][2];
+template <int XM>
+const void* gemv_fn(bool ring, int paths) {
+  return paths == 3 ? (ring ? (const void*)k_gemv<1, true, false, 3, XM> : (const void*)k_gemv<1, false, false, 3, XM>)
+                    : (ring ? (const void*)k_gemv<1, true, false, 2, XM> : (const void*)k_gemv<1, false, false, 2, XM>);
+}
+
+int resident_wgs(bool ring, int paths, int xm) {
+  static std::atomic<int> cache[kMaxDevices][2][2][3];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
-  std::atomic<int>& slot = cache[dev][ring ? 1 : 0][paths == 3 ? 1 : 0];
+  std::atomic<int>& slot = cache[dev][ring ? 1 : 0][paths == 3 ? 1 : 0][xm];
   int c = slot.load(std::memory_order_relaxed);
   if (c == 0) {
     int cus = 0, per = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
       cus = 256;
-    const void* fn = paths == 3
-        ? (ring ? (const void*)k_gemv<1, true, false, 3> : (const void*)k_gemv<1, false, false, 3>)
-        : (ring ? (const void*)k_gemv<1, true, false, 2> : (const void*)k_gemv<1, false, false, 2>);
+    const void* fn = xm == XSRC_ATTN ? gemv_fn<XSRC_ATTN>(ring, paths)
+                   : xm == XSRC_SILU ? gemv_fn<XSRC_SILU>(ring, paths) : gemv_fn<XSRC_X>(ring, paths);
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fn, 256, 0) != hipSuccess || per < 1) per = 1;
     c = cus * per;
     slot.store(c, std::memory_order_relaxed);
@@ -917,7 +1041,7 @@ __host__ inline Plan16 make_plan16(const int* outs, int nseg, int in, int batch,
 // passes x (m rounds + one for the digit build), ties to the smaller m (more
 // workgroups). With more batch pairs (one buffer, rounds not overlapped) the
 // rounds stay short: enough workgroups to fill the device a few times over.
-__host__ inline Plan make_plan(const int* outs, int nseg, int in, int batch, int paths) {
+__host__ inline Plan make_plan(const int* outs, int nseg, int in, int batch, int paths, int xm = XSRC_X) {
   Plan P;
   P.paths = paths;
   P.KG = col_groups(in);
@@ -929,7 +1053,7 @@ __host__ inline Plan make_plan(const int* outs, int nseg, int in, int batch, int
     long wgs = 0;
     for (int s = 0; s < nseg; ++s) wgs += (row_groups(outs[s]) + 4 * m - 1) / (4 * m);
     wgs *= (long)P.S * groups;
-    const long cap = resident_wgs(m > 1, paths);
+    const long cap = resident_wgs(m > 1, paths, xm);
     const long cost = (wgs + cap - 1) / cap * (m + 1);
     if (best < 0 || cost < best) {
       best = cost;
@@ -948,24 +1072,32 @@ hipError_t launch_main(const Plan& P, const Args& A, int batch, hipStream_t st) 
   Args B = A;
   B.items = nrb * P.S;
   B.ngrp = groups;
-  auto go = [&](auto paths_tag) {
-    constexpr int NP = decltype(paths_tag)::value;
+  auto go = [&](auto paths_tag, auto xm_tag) {
+    constexpr int NP = decltype(paths_tag)::value, XM = decltype(xm_tag)::value;
     if (groups > 1) {
       if (A.m > 1)
-        hipLaunchKernelGGL((k_gemv<1, true, true, NP>), grid, dim3(256), 0, st, B);
+        hipLaunchKernelGGL((k_gemv<1, true, true, NP, XM>), grid, dim3(256), 0, st, B);
       else
-        hipLaunchKernelGGL((k_gemv<1, false, true, NP>), grid, dim3(256), 0, st, B);
+        hipLaunchKernelGGL((k_gemv<1, false, true, NP, XM>), grid, dim3(256), 0, st, B);
     } else {
       if (A.m > 1)
-        hipLaunchKernelGGL((k_gemv<1, true, false, NP>), grid, dim3(256), 0, st, B);
+        hipLaunchKernelGGL((k_gemv<1, true, false, NP, XM>), grid, dim3(256), 0, st, B);
       else
-        hipLaunchKernelGGL((k_gemv<1, false, false, NP>), grid, dim3(256), 0, st, B);
+        hipLaunchKernelGGL((k_gemv<1, false, false, NP, XM>), grid, dim3(256), 0, st, B);
     }
   };
-  if (P.paths == 3)
-    go(std::integral_constant<int, 3>());
+  auto go_p = [&](auto xm_tag) {
+    if (P.paths == 3)
+      go(std::integral_constant<int, 3>(), xm_tag);
+    else
+      go(std::integral_constant<int, 2>(), xm_tag);
+  };
+  if (A.xs.mode == XSRC_ATTN)
+    go_p(std::integral_constant<int, XSRC_ATTN>());
+  else if (A.xs.mode == XSRC_SILU)
+    go_p(std::integral_constant<int, XSRC_SILU>());
   else
-    go(std::integral_constant<int, 2>());
+    go_p(std::integral_constant<int, XSRC_X>());
   return hipGetLastError();
 }
 
@@ -1053,8 +1185,17 @@ hipError_t launch_gemv_reduce(int out, int in, int batch, void* y, int y_dtype, 
 size_t gemv_part_bytes(int out, int in, int batch) { return gemv_workspace_bytes(out, in, batch); }
 
 hipError_t launch_gemv_multi(const LinSeg* segs, int nseg, int in, const uint16_t* x, int batch,
-                             const double* stats, float eps, hipStream_t st) {
+                             const double* stats, float eps, hipStream_t st, const GemvXSrc* xs) {
   if (nseg < 1 || nseg > kMaxSeg) return hipErrorInvalidValue;
+  if (xs && xs->mode != XSRC_X) {
+    // formed inputs: digit path only, no RMSNorm, the partial buffers they read
+    if (batch != 1 || stats || !xs->pa) return hipErrorInvalidValue;
+    if (xs->mode == XSRC_ATTN &&
+        (xs->head_dim < 1 || xs->rep < 1 || !xs->pq || !xs->pk || !xs->qk || xs->n_q != in || xs->kv < 1 ||
+         xs->kv != in / xs->rep || in % (xs->rep * xs->head_dim)))
+      return hipErrorInvalidValue;
+    if (xs->mode == XSRC_SILU && !xs->pb) return hipErrorInvalidValue;
+  }
   int outs[kMaxSeg];
   for (int s = 0; s < nseg; ++s) {
     outs[s] = segs[s].out;
@@ -1083,7 +1224,7 @@ hipError_t launch_gemv_multi(const LinSeg* segs, int nseg, int in, const uint16_
     A.eps = eps;
     return launch_16(P, A, batch, st);
   }
-  const Plan P = make_plan(outs, nseg, in, batch, segs[0].paths);
+  const Plan P = make_plan(outs, nseg, in, batch, segs[0].paths, xs ? xs->mode : XSRC_X);
   Args A = {};
   int rb0 = 0;
   for (int s = 0; s < nseg; ++s) {
@@ -1097,6 +1238,7 @@ hipError_t launch_gemv_multi(const LinSeg* segs, int nseg, int in, const uint16_
     rb0 += P.RB[s];
   }
   A.x = x;
+  if (xs) A.xs = *xs;
   A.stats = stats;
   A.nseg = nseg;
   A.in = in;

@@ -509,12 +509,15 @@ extern "C++" LinSeg seg_of(const rabit_layer& L, double* part) {
 // One decode step at batch <= RABIT_MAX_GEMV_BATCH. Per layer: [q,k,v] GEMV
 // on RMSNorm(x) -> q/k/v sums + attention -> o GEMV -> x + o and its x^2
 // sums -> [gate,up] GEMV on RMSNorm -> SiLU(gate)*up -> down GEMV -> x + down
-// and its x^2 sums: 8 launches (4 without attention), plus one for the
-// statistics of the step input.
+// and its x^2 sums, plus one launch for the statistics of the step input.
+// At batch 1 the o and down GEMVs form their inputs (attention, SiLU(gate)*up)
+// from the previous launch's partials themselves: 6 launches per layer (3
+// without attention); otherwise 8 (4).
 hipError_t decode_gemv_path(const rabit_decoder_cfg* cfg, const rabit_layer* layers,
                             const uint16_t* x, int batch, uint16_t* out, const DecodeWs& w,
                             hipStream_t st) {
   const int H = cfg->hidden, F = cfg->ffn;
+  const bool formed = batch == 1;
   hipError_t e = launch_resid_stats(nullptr, x, nullptr, w.stats, batch, H, st);
   const uint16_t* cur = x;
   for (int l = 0; l < cfg->n_layers && e == hipSuccess; ++l) {
@@ -523,18 +526,40 @@ hipError_t decode_gemv_path(const rabit_decoder_cfg* cfg, const rabit_layer* lay
     if (!cfg->mlp_only) {
       const LinSeg qkv[3] = {seg_of(Ls[0], w.pq), seg_of(Ls[1], w.pk), seg_of(Ls[2], w.pv)};
       if (!e) e = launch_gemv_multi(qkv, 3, H, cur, batch, w.stats, cfg->rms_eps, st);
-      if (!e) e = launch_reduce_attn(w.pq, w.pk, w.pv, w.qk, w.attn, batch, cfg->n_heads,
-                                     cfg->n_kv_heads, cfg->head_dim, st);
       const LinSeg o = seg_of(Ls[3], w.po);
-      if (!e) e = launch_gemv_multi(&o, 1, H, w.attn, batch, nullptr, 0.f, st);
+      if (formed) {
+        GemvXSrc xs;
+        xs.mode = XSRC_ATTN;
+        xs.pa = w.pv;
+        xs.head_dim = cfg->head_dim;
+        xs.rep = cfg->n_heads / cfg->n_kv_heads;
+        xs.pq = w.pq;
+        xs.pk = w.pk;
+        xs.qk = w.qk;
+        xs.n_q = H;
+        xs.kv = cfg->n_kv_heads * cfg->head_dim;
+        if (!e) e = launch_gemv_multi(&o, 1, H, nullptr, batch, nullptr, 0.f, st, &xs);
+      } else {
+        if (!e) e = launch_reduce_attn(w.pq, w.pk, w.pv, w.qk, w.attn, batch, cfg->n_heads,
+                                       cfg->n_kv_heads, cfg->head_dim, st);
+        if (!e) e = launch_gemv_multi(&o, 1, H, w.attn, batch, nullptr, 0.f, st);
+      }
       if (!e) e = launch_resid_stats(w.po, cur, nxt, w.stats, batch, H, st);
       cur = nxt;
     }
     const LinSeg gu[2] = {seg_of(Ls[4], w.pg), seg_of(Ls[5], w.pu)};
     if (!e) e = launch_gemv_multi(gu, 2, H, cur, batch, w.stats, cfg->rms_eps, st);
-    if (!e) e = launch_reduce_silu(w.pg, w.pu, w.z, batch, F, st);
     const LinSeg dn = seg_of(Ls[6], w.pd);
-    if (!e) e = launch_gemv_multi(&dn, 1, F, w.z, batch, nullptr, 0.f, st);
+    if (formed) {
+      GemvXSrc xs;
+      xs.mode = XSRC_SILU;
+      xs.pa = w.pg;
+      xs.pb = w.pu;
+      if (!e) e = launch_gemv_multi(&dn, 1, F, nullptr, batch, nullptr, 0.f, st, &xs);
+    } else {
+      if (!e) e = launch_reduce_silu(w.pg, w.pu, w.z, batch, F, st);
+      if (!e) e = launch_gemv_multi(&dn, 1, F, w.z, batch, nullptr, 0.f, st);
+    }
     // x + down may be written in place (cur == nxt when attention ran)
     if (!e) e = launch_resid_stats(w.pd, cur, nxt, w.stats, batch, H, st);
     cur = nxt;

@@ -266,8 +266,30 @@ __device__ __forceinline__ double sum_ranges(const double* __restrict__ part, in
   return sum_ranges_by<8>(part_data(part) + (size_t)b * S * stride + i, S, stride);
 }
 size_t gemv_part_bytes(int out, int in, int batch);
+
+// Where a decode GEMV launch takes its input from (batch 1): the op between
+// two linear layers is formed per column inside the second one, from the
+// first one's partial buffers (slices summed in ascending order, as
+// rabit_gemv_reduce does), instead of in a launch of its own.
+enum GemvXMode { XSRC_X = 0, XSRC_ATTN = 1, XSRC_SILU = 2 };
+struct GemvXSrc {
+  int mode = XSRC_X;
+  // XSRC_ATTN: column c = head h, dim d is bf16(v[(h / rep) head_dim + d])
+  // (one-token attention), v = Σ of pa's slices; XSRC_SILU: column c is
+  // bf16(silu(Σ pa) Σ pb) (gate, up)
+  const double* pa = nullptr;
+  const double* pb = nullptr;
+  int head_dim = 1, rep = 1;
+  // XSRC_ATTN: the q and k sums, fp32 into qk [n_q + kv], spread over the
+  // launch's workgroups
+  const double* pq = nullptr;
+  const double* pk = nullptr;
+  float* qk = nullptr;
+  int n_q = 0, kv = 0;
+};
 hipError_t launch_gemv_multi(const LinSeg* segs, int nseg, int in, const uint16_t* x, int batch,
-                             const double* stats, float eps, hipStream_t st);
+                             const double* stats, float eps, hipStream_t st,
+                             const GemvXSrc* xs = nullptr);
 
 size_t gemm_workspace_bytes(int out, int in, int m);
 // weff: form the effective weight per tile in fp16 (one matrix op per tile

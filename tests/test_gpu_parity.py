@@ -321,7 +321,7 @@ def test_gemm_rows_match_gemv(gpu_lib):
         assert oracle.normwise_rel_err(ym[r:r + 1], yv) < 1e-5
 
 
-def _decode_case(gpu_lib, cfg, mlp_only, batch, seed):
+def _decode_case(gpu_lib, cfg, mlp_only, batch, seed, repeats=1):
     H, F = cfg.hidden, cfg.ffn
     kv = cfg.n_kv_heads * cfg.head_dim
     shapes = {"q": (H, H), "k": (kv, H), "v": (kv, H), "o": (H, H), "gate": (F, H), "up": (F, H), "down": (H, F)}
@@ -336,7 +336,9 @@ def _decode_case(gpu_lib, cfg, mlp_only, batch, seed):
         layers.append(ld)
         dmats.append(dd)
     x = act_bf16(batch, H, seed + 99)
-    y = gpu_lib.decode_step(cfg, layers, x.cuda()).cpu().to(torch.float32).numpy().astype(np.float64)
+    ys = [gpu_lib.decode_step(cfg, layers, x.cuda()).cpu().to(torch.float32).numpy().astype(np.float64)
+          for _ in range(repeats)]
+    y = ys[0] if repeats == 1 else ys
     ref = bf16_values(x)
     ocfg = {"n_heads": cfg.n_heads, "n_kv_heads": cfg.n_kv_heads, "head_dim": cfg.head_dim, "rms_eps": cfg.rms_eps}
     for dd in dmats:
@@ -415,6 +417,49 @@ def test_decode_attention_block(gpu_lib, batch):
     ok, nbad = bf16_close(y, ref)
     say("  normwise err", err, "elements outside bound", nbad)
     assert ok
+
+
+@pytest.mark.parametrize("batch", [1, 3, 7, 9])
+def test_decode_steps_repeatable(gpu_lib, batch):
+    # ragged shapes (hidden 768, 128 rows of k and v, ffn 1100), batch groups
+    # of 1, 2 and 4 workgroups per range and the fp16 path: three steps on
+    # the same input give the same bits, close to the oracle
+    say("decode repeatable batch", batch)
+    cfg = gpu_lib.DecoderCfg(hidden=768, ffn=1100, n_heads=6, n_kv_heads=1, head_dim=128, n_layers=3)
+    ys, ref = _decode_case(gpu_lib, cfg, False, batch, 1300 + batch, repeats=3)
+    assert np.array_equal(ys[0], ys[1]) and np.array_equal(ys[0], ys[2])
+    ok, nbad = bf16_close(ys[0], ref)
+    say("  normwise err", oracle.normwise_rel_err(ys[0], ref), "elements outside bound", nbad)
+    assert ok
+
+
+@pytest.mark.parametrize("hidden,n_heads,n_kv", [(1024, 8, 2), (512, 8, 2), (4608, 36, 4)])
+def test_decode_qk_sums_batch1(gpu_lib, hidden, n_heads, n_kv):
+    # at batch 1 the o launch also sums the q and k partials of the layer
+    # (rows spread over its work items, more than 256 per item at hidden 512);
+    # the workspace keeps the last layer's q and k in fp32 after x, x, the
+    # attention output, z and the x^2 statistics (256-byte aligned areas)
+    say("decode q/k sums at batch 1, hidden", hidden)
+    hd = hidden // n_heads
+    cfg = gpu_lib.DecoderCfg(hidden=hidden, ffn=768, n_heads=n_heads, n_kv_heads=n_kv, head_dim=hd, n_layers=1)
+    H, F, kv = hidden, cfg.ffn, n_kv * hd
+    shapes = {"q": (H, H), "k": (kv, H), "v": (kv, H), "o": (H, H), "gate": (F, H), "up": (F, H), "down": (H, F)}
+    ws_, d = {}, {}
+    for i, (n, sh) in enumerate(shapes.items()):
+        w = weight_f32(*sh, 1400 + i)
+        ws_[n] = pack_gpu(gpu_lib, w)
+        d[n] = oracle.derive(w.numpy())
+    x = act_bf16(1, H, 1499)
+    work = gpu_lib.decode_workspace(cfg, 1)
+    gpu_lib.decode_step(cfg, [ws_], x.cuda(), workspace=work)
+    torch.cuda.synchronize()
+    a = lambda n: (n + 255) // 256 * 256
+    off = 3 * a(2 * H) + a(2 * F) + a(8 * 32)
+    qk = work[off:off + 4 * (H + kv)].view(torch.float32).cpu().numpy().astype(np.float64)
+    n = oracle.rmsnorm_bf16(bf16_values(x))
+    for name, got in (("q", qk[:H]), ("k", qk[H:])):
+        ref = oracle.gemv(d[name], n)[0]
+        check_fx(got[None, :], ref[None, :], d[name], n)
 
 
 def test_stream_read_runs(gpu_lib):
