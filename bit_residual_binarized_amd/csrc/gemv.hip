@@ -672,7 +672,8 @@ __global__ __launch_bounds__(256) void k_gemv(Args A) {
 // of a lane's 8 fp16 values holds the columns (m, m + 16), m = 4 t + c, of
 // quarter t (paper App. E.1 packs 32 columns per word: the sign bits of that
 // dword are bits m and m + 16 of the stored word, moved to bits 15 and 31 by
-// one shift). A and B use the same order.
+// one shift, which serves two words at once as a 64-bit shift). A and B use
+// the same order.
 //
 // Workgroup: 4 waves, one row group (64 rows) each, 4 consecutive row groups.
 // Lane (j, gl) holds, per range, the 16-byte unit (rg, 4 r + gl, p, 16 tau + j)
@@ -683,6 +684,14 @@ constexpr int kF16MinBatch = RABIT_GEMV_FP16_MIN_BATCH;
 constexpr int kXRow = 260;  // dwords per staged token row (256 + 4: conflict-free 16-byte reads)
 
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+
+// v << n as one V_LSHLREV_B64 (full rate here); the compiler otherwise splits
+// a 64-bit shift into a 32-bit shift and an align, two instructions
+__device__ __forceinline__ uint64_t shl64(uint64_t v, int n) {
+  uint64_t r;
+  asm volatile("v_lshlrev_b64 %0, %1, %2" : "=v"(r) : "v"(n), "v"(v));
+  return r;
+}
 
 __device__ __forceinline__ uint32_t f16_pair(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
@@ -851,35 +860,53 @@ __global__ __launch_bounds__(256, P == 3 && MT == 2 ? 1 : 2) void k_gemv16(Args 
   // the matrix ops of stage u with the range's weights wt
   auto compute = [&](const uint4 (&wt)[4 * P], auto U) {
     constexpr int u = decltype(U)::value;
+    // steps (q, t4) and (q + 1, t4) together: words q and q + 1 of a unit sit
+    // in adjacent registers, and one 64-bit shift by 15 - 4 t4 - c brings the
+    // sign bits of dword c of both steps to bits 15 and 31 of each half (no
+    // bit of the low word reaches those positions of the high word)
 #pragma unroll
-    for (int st = 0; st < 16; ++st) {
-      // one word's four steps at a time, so that the scheduler does not hoist
-      // every step's LDS reads
-      if ((st & 3) == 0) __builtin_amdgcn_sched_barrier(0);
-      const int q = st >> 2, t4 = st & 3, sh = 15 - 4 * t4;
-      const int off = 16 * (4 * gl + q) + 4 * t4;
-      v8h fa[MT];
+    for (int qq = 0; qq < 4; qq += 2)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) fa[mt] = *(const v8h*)(s_x[u] + (16 * mt + j) * kXRow + off);
+      for (int t4 = 0; t4 < 4; ++t4) {
+        // one step pair at a time, so that the scheduler does not hoist every
+        // step's LDS reads
+        __builtin_amdgcn_sched_barrier(0);
+        const int sh = 15 - 4 * t4;
+        const int off0 = 16 * (4 * gl + qq) + 4 * t4, off1 = off0 + 16;
+        v8h fa0[MT], fa1[MT];
 #pragma unroll
-      for (int p = 0; p < P; ++p) {
-        const uint4 hh = *(const uint4*)(s_h[u][p] + off);
+        for (int mt = 0; mt < MT; ++mt) {
+          fa0[mt] = *(const v8h*)(s_x[u] + (16 * mt + j) * kXRow + off0);
+          fa1[mt] = *(const v8h*)(s_x[u] + (16 * mt + j) * kXRow + off1);
+        }
 #pragma unroll
-        for (int tau = 0; tau < 4; ++tau) {
-          const uint4 wv = wt[tau * P + p];
-          const uint32_t wd = q == 0 ? wv.x : q == 1 ? wv.y : q == 2 ? wv.z : wv.w;
-          uint4 e;
-          e.x = hh.x ^ ((wd << sh) & 0x80008000u);
-          e.y = hh.y ^ ((wd << (sh - 1)) & 0x80008000u);
-          e.z = hh.z ^ ((wd << (sh - 2)) & 0x80008000u);
-          e.w = hh.w ^ ((wd << (sh - 3)) & 0x80008000u);
-          const v8h fb = __builtin_bit_cast(v8h, e);
+        for (int p = 0; p < P; ++p) {
+          const uint4 h0 = *(const uint4*)(s_h[u][p] + off0);
+          const uint4 h1 = *(const uint4*)(s_h[u][p] + off1);
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
-            acc[p][tau][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[mt], fb, acc[p][tau][mt], 0, 0, 0);
+          for (int tau = 0; tau < 4; ++tau) {
+            const uint4 wv = wt[tau * P + p];
+            const uint64_t pr = qq == 0 ? (((uint64_t)wv.y << 32) | wv.x) : (((uint64_t)wv.w << 32) | wv.z);
+            const uint64_t s0 = shl64(pr, sh), s1 = shl64(pr, sh - 1), s2 = shl64(pr, sh - 2),
+                           s3 = shl64(pr, sh - 3);
+            uint4 e0, e1;
+            e0.x = h0.x ^ ((uint32_t)s0 & 0x80008000u);
+            e0.y = h0.y ^ ((uint32_t)s1 & 0x80008000u);
+            e0.z = h0.z ^ ((uint32_t)s2 & 0x80008000u);
+            e0.w = h0.w ^ ((uint32_t)s3 & 0x80008000u);
+            e1.x = h1.x ^ ((uint32_t)(s0 >> 32) & 0x80008000u);
+            e1.y = h1.y ^ ((uint32_t)(s1 >> 32) & 0x80008000u);
+            e1.z = h1.z ^ ((uint32_t)(s2 >> 32) & 0x80008000u);
+            e1.w = h1.w ^ ((uint32_t)(s3 >> 32) & 0x80008000u);
+            const v8h fb0 = __builtin_bit_cast(v8h, e0), fb1 = __builtin_bit_cast(v8h, e1);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+              acc[p][tau][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa0[mt], fb0, acc[p][tau][mt], 0, 0, 0);
+              acc[p][tau][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa1[mt], fb1, acc[p][tau][mt], 0, 0, 0);
+            }
+          }
         }
       }
-    }
   };
 
   // ranges in pairs (stages 0 and 1, weight buffers wa and wb). Before the
