@@ -883,6 +883,42 @@ __global__ __launch_bounds__(256, P == 3 && MT == 2 ? 1 : 2) void k_gemv16(Args 
         for (int p = 0; p < P; ++p) {
           const uint4 h0 = *(const uint4*)(s_h[u][p] + off0);
           const uint4 h1 = *(const uint4*)(s_h[u][p] + off1);
+          if constexpr (MT == 2) {
+            // all four slices' operands first, then the low step's matrix
+            // ops, then the high step's: the two ops on one accumulator are
+            // eight apart (same accumulation order as below; 24 more registers,
+            // which cost occupancy with one token tile)
+            v8h fb0[4], fb1[4];
+#pragma unroll
+            for (int tau = 0; tau < 4; ++tau) {
+              const uint4 wv = wt[tau * P + p];
+              const uint64_t pr = qq == 0 ? (((uint64_t)wv.y << 32) | wv.x) : (((uint64_t)wv.w << 32) | wv.z);
+              const uint64_t s0 = shl64(pr, sh), s1 = shl64(pr, sh - 1), s2 = shl64(pr, sh - 2),
+                             s3 = shl64(pr, sh - 3);
+              uint4 e0, e1;
+              e0.x = h0.x ^ ((uint32_t)s0 & 0x80008000u);
+              e0.y = h0.y ^ ((uint32_t)s1 & 0x80008000u);
+              e0.z = h0.z ^ ((uint32_t)s2 & 0x80008000u);
+              e0.w = h0.w ^ ((uint32_t)s3 & 0x80008000u);
+              e1.x = h1.x ^ ((uint32_t)(s0 >> 32) & 0x80008000u);
+              e1.y = h1.y ^ ((uint32_t)(s1 >> 32) & 0x80008000u);
+              e1.z = h1.z ^ ((uint32_t)(s2 >> 32) & 0x80008000u);
+              e1.w = h1.w ^ ((uint32_t)(s3 >> 32) & 0x80008000u);
+              fb0[tau] = __builtin_bit_cast(v8h, e0);
+              fb1[tau] = __builtin_bit_cast(v8h, e1);
+            }
+#pragma unroll
+            for (int tau = 0; tau < 4; ++tau)
+#pragma unroll
+              for (int mt = 0; mt < MT; ++mt)
+                acc[p][tau][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa0[mt], fb0[tau], acc[p][tau][mt], 0, 0, 0);
+#pragma unroll
+            for (int tau = 0; tau < 4; ++tau)
+#pragma unroll
+              for (int mt = 0; mt < MT; ++mt)
+                acc[p][tau][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa1[mt], fb1[tau], acc[p][tau][mt], 0, 0, 0);
+            continue;
+          }
 #pragma unroll
           for (int tau = 0; tau < 4; ++tau) {
             const uint4 wv = wt[tau * P + p];
