@@ -917,6 +917,15 @@ __global__ __launch_bounds__(256, P == 3 && MT == 2 ? 1 : 2) void k_gemv16(Args 
 #pragma unroll
               for (int mt = 0; mt < MT; ++mt)
                 acc[p][tau][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa1[mt], fb1[tau], acc[p][tau][mt], 0, 0, 0);
+            // issue order: the first slice's operands (6 VALU), then one
+            // matrix op and two VALU instructions at a time, so that the
+            // operand builds run beside the matrix ops
+            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+            }
             continue;
           }
 #pragma unroll
