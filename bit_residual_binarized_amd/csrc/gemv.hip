@@ -184,9 +184,10 @@ __global__ __launch_bounds__(256) void k_gemv(Args A) {
   const int RG = si == 2 ? A.seg[2].RG : si == 1 ? A.seg[1].RG : A.seg[0].RG;
   const int rb = rbg - (si == 2 ? A.seg[2].rb0 : si == 1 ? A.seg[1].rb0 : A.seg[0].rb0);
   if (blockIdx.x == 0 && threadIdx.x < A.nseg) {
-    // the partial buffers' headers: one slice per range
+    // the partial buffers' headers: one float64 slice per range
     double* hp = threadIdx.x == 2 ? A.seg[2].part : threadIdx.x == 1 ? A.seg[1].part : A.seg[0].part;
-    *(int*)hp = A.S;
+    ((int*)hp)[0] = A.S;
+    ((int*)hp)[1] = 8;
   }
   part += kPartHdrDoubles;
 
@@ -665,8 +666,9 @@ __global__ __launch_bounds__(256) void k_gemv(Args A) {
 // holds ±h_p (exact in fp16); the products are exact in fp32 and the matrix
 // cores accumulate them in fp32. A workgroup covers a chunk of kr consecutive
 // ranges of 512 columns and, per chunk and output, forms Σ_p g_p acc_p 2^-e in
-// float64 and leaves it as one partial (so the partials, written and read
-// again by the consumer, shrink kr-fold).
+// float64 and leaves it as one float32 partial (so the partials, written and
+// read again by the consumer, shrink kr-fold, and are half the bytes of the
+// digit path's).
 //
 // Inside a 32-column block the contraction index is permuted so that dword c
 // of a lane's 8 fp16 values holds the columns (m, m + 16), m = 4 t + c, of
@@ -806,9 +808,10 @@ __global__ __launch_bounds__(256, P == 3 && MT == 2 ? 1 : 2) void k_gemv16(Args 
   const int RG = si == 2 ? A.seg[2].RG : si == 1 ? A.seg[1].RG : A.seg[0].RG;
   const int rb = rbg - (si == 2 ? A.seg[2].rb0 : si == 1 ? A.seg[1].rb0 : A.seg[0].rb0);
   if (blockIdx.x == 0 && threadIdx.x < A.nseg) {
-    // the partial buffers' headers: one slice per chunk
+    // the partial buffers' headers: one float32 slice per chunk
     double* hp = threadIdx.x == 2 ? A.seg[2].part : threadIdx.x == 1 ? A.seg[1].part : A.seg[0].part;
-    *(int*)hp = A.nck;
+    ((int*)hp)[0] = A.nck;
+    ((int*)hp)[1] = 4;
   }
   part += kPartHdrDoubles;
 
@@ -981,7 +984,8 @@ __global__ __launch_bounds__(256, P == 3 && MT == 2 ? 1 : 2) void k_gemv16(Args 
     if (!n2) break;
   }
 
-  // tokens 16 mt + 4 gl + i of row 16 tau + j: Σ_p g_p acc_p 2^-e_b in float64
+  // tokens 16 mt + 4 gl + i of row 16 tau + j: Σ_p g_p acc_p 2^-e_b in float64,
+  // stored rounded to float32
   if (rg < RG) {
     int eb[MT][4];
 #pragma unroll
@@ -1003,7 +1007,7 @@ __global__ __launch_bounds__(256, P == 3 && MT == 2 ? 1 : 2) void k_gemv16(Args 
           double v = gp[0] * (double)acc[0][tau][mt][i];
 #pragma unroll
           for (int p = 1; p < P; ++p) v += gp[p] * (double)acc[p][tau][mt][i];
-          part[((size_t)b * A.nck + ck) * RG * 64 + row] = ldexp(v, -eb[mt][i]);
+          ((float*)part)[((size_t)b * A.nck + ck) * RG * 64 + row] = (float)ldexp(v, -eb[mt][i]);
         }
     }
   }
@@ -1016,8 +1020,15 @@ __global__ __launch_bounds__(256) void k_gemv_reduce(const double* __restrict__ 
   if (row >= out) return;
   const int S = part_slices(part);
   // many ranges (wide layers): 32 loads in flight per round trip
-  const double* pp = part_data(part) + (size_t)b * S * RG * 64 + row;
-  const double v = S <= 8 ? sum_ranges_by<8>(pp, S, RG * 64) : sum_ranges_by<32>(pp, S, RG * 64);
+  const size_t at = (size_t)b * S * RG * 64 + row;
+  double v;
+  if (part_elem_bytes(part) == 4) {
+    const float* pp = (const float*)part_data(part) + at;
+    v = S <= 8 ? sum_ranges_by<8>(pp, S, RG * 64) : sum_ranges_by<32>(pp, S, RG * 64);
+  } else {
+    const double* pp = part_data(part) + at;
+    v = S <= 8 ? sum_ranges_by<8>(pp, S, RG * 64) : sum_ranges_by<32>(pp, S, RG * 64);
+  }
   if (y_dtype == RABIT_OUT_F32)
     ((float*)y)[(size_t)b * out + row] = (float)v;
   else

@@ -238,23 +238,26 @@ struct LinSeg {
 #define RABIT_STAT_PARTS 32
 
 // A GEMV launch's partial buffer for one matrix: a 256-byte header whose
-// first int32 is the number of partial slices per output row, then the
-// float64 partials [batch][slices][64*ceil(out/64)].
+// first int32 is the number of partial slices per output row and whose
+// second is the bytes per partial (8: float64, written by the digit path; 4:
+// float32, the fp16 path's chunk partials), then the partials
+// [batch][slices][64*ceil(out/64)].
 constexpr int kPartHdrDoubles = 32;
 __host__ __device__ __forceinline__ int part_slices(const double* part) { return *(const int*)part; }
+__host__ __device__ __forceinline__ int part_elem_bytes(const double* part) { return ((const int*)part)[1]; }
 __host__ __device__ __forceinline__ const double* part_data(const double* part) { return part + kPartHdrDoubles; }
 
 // Σ_r part[b][r][i] over the S ranges of a GEMV's float64 partials (row
 // stride `stride`), added in ascending r, with the loads of C ranges in flight
 // together (clamped index, masked). The decode consumers use C = 8: a wider
 // chunk makes these small kernels slower to start than the round trips it saves.
-template <int C>
-__device__ __forceinline__ double sum_ranges_by(const double* __restrict__ pp, int S, int stride) {
+template <int C, typename T = double>
+__device__ __forceinline__ double sum_ranges_by(const T* __restrict__ pp, int S, int stride) {
   double v = 0.0;
   for (int r = 0; r < S; r += C) {
     double t[C];
 #pragma unroll
-    for (int u = 0; u < C; ++u) t[u] = pp[(size_t)min(r + u, S - 1) * stride];
+    for (int u = 0; u < C; ++u) t[u] = (double)pp[(size_t)min(r + u, S - 1) * stride];
 #pragma unroll
     for (int u = 0; u < C; ++u) v += r + u < S ? t[u] : 0.0;
   }
@@ -263,7 +266,9 @@ __device__ __forceinline__ double sum_ranges_by(const double* __restrict__ pp, i
 // (part: the matrix's whole partial buffer, header included)
 __device__ __forceinline__ double sum_ranges(const double* __restrict__ part, int b, int stride, int i) {
   const int S = part_slices(part);
-  return sum_ranges_by<8>(part_data(part) + (size_t)b * S * stride + i, S, stride);
+  const size_t at = (size_t)b * S * stride + i;
+  if (part_elem_bytes(part) == 4) return sum_ranges_by<8>((const float*)part_data(part) + at, S, stride);
+  return sum_ranges_by<8>(part_data(part) + at, S, stride);
 }
 size_t gemv_part_bytes(int out, int in, int batch);
 

@@ -187,8 +187,9 @@ int rabit_unpack(const rabit_layer *layer, uint32_t *words, void *stream);
  * summed in fp32 over chunks of consecutive 512-column ranges (at most
  * in_features + 16 ceil(in/512) roundings, each within 2^-24 of a running sum
  * bounded by Σ_j |h_p[j] x[j]|); per chunk Σ_p g_p acc_p 2^-e is formed in
- * float64, the chunks are summed in float64 in ascending order and the result
- * is rounded once.
+ * float64 and rounded to float32 (one more rounding per chunk, within 2^-24
+ * of Σ_p |g_p| Σ_j |h_p[j] x[j]|), the chunks are summed in float64 in
+ * ascending order and the result is rounded once.
  * Result is bitwise repeatable (no order-dependent arithmetic); a batch row's
  * result depends only on that row, for batches of the same arithmetic and
  * token tile (up to 16 rows, or 17 to 32).
@@ -223,8 +224,10 @@ int rabit_gemv_noalloc(const rabit_layer *layer, const uint16_t *x, int32_t batc
 /*
  * The two halves of rabit_gemv, for callers that time or schedule them apart.
  * rabit_gemv_partial streams every plane byte in one kernel launch and leaves
- * in the workspace the float64 partial result of each range of 512 input
- * columns; rabit_gemv_reduce sums those partials (ascending range) into y.
+ * in the workspace the partial result of each range of 512 input columns
+ * (float64; from RABIT_GEMV_FP16_MIN_BATCH on, of each chunk of ranges, in
+ * float32), after a header that records their count and width;
+ * rabit_gemv_reduce sums those partials (ascending order) into y.
  * A reduce consumes the workspace of the last partial for the same layer and
  * batch; the pair gives the same bits as rabit_gemv. Errors as rabit_gemv.
  */

@@ -83,7 +83,8 @@ def f16_bound(d, xv):
     largest |x|; below that off by at most 2^-25 2^-e); the products with
     ±h_p are exact and summed in fp32 over the chunk (at most in + 16 S
     roundings, each within 2^-24 of a running sum bounded by Σ|h_p x|); g_p is
-    applied in float64."""
+    applied in float64 and each chunk's partial rounded to float32 (one more
+    rounding per chunk, at most S of them)."""
     xb = np.atleast_2d(xv)
     B, K = xb.shape
     S = -(-K // 512)
@@ -91,7 +92,7 @@ def f16_bound(d, xv):
     xmax = np.abs(xb).max(axis=1)
     for s_, g, h in d.paths:
         ha = np.abs(h.astype(np.float64))
-        acc = (K + 16 * S) * 2.0 ** -24 * (np.abs(xb) @ ha) + ha.sum() * 2.0 ** -25 * xmax * 2.0 ** -14
+        acc = (K + 17 * S) * 2.0 ** -24 * (np.abs(xb) @ ha) + ha.sum() * 2.0 ** -25 * xmax * 2.0 ** -14
         bound += np.abs(g.astype(np.float64))[None, :] * acc[:, None]
     return bound
 
