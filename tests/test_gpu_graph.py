@@ -49,7 +49,7 @@ def same_bits(a, b):
                        b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32))
 
 
-@pytest.mark.parametrize("mlp_only,batch", [(True, 1), (False, 1), (False, 4), (True, 40)])
+@pytest.mark.parametrize("mlp_only,batch", [(True, 1), (False, 1), (False, 4), (False, 12), (True, 9), (True, 40)])
 def test_decode_step_graph_replays(gpu_lib, mlp_only, batch):
     say("decode step graph replay, mlp_only", mlp_only, "batch", batch)
     cfg = gpu_lib.DecoderCfg(hidden=1024, ffn=2752, n_heads=8, n_kv_heads=2, head_dim=128, n_layers=2,
