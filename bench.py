@@ -184,6 +184,37 @@ def graph_ms(torch, fn, reps):
     return e0.elapsed_time(e1) / reps
 
 
+def dist_summary(vals):
+    """Median, p10 and p90 of a list of timings (nearest-rank percentiles)."""
+    v = sorted(vals)
+    pick = lambda q: v[min(len(v) - 1, max(0, int(round(q * (len(v) - 1)))))]
+    return {"median": pick(0.5), "p10": pick(0.1), "p90": pick(0.9), "n": len(v)}
+
+
+def graph_ms_dist(torch, fn, reps):
+    """As graph_ms, but one event after every replay: the list of per-replay
+    times (ms), for the distribution over repetitions."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    g.replay()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record()
+    for k in range(reps):
+        g.replay()
+        ev[k + 1].record()
+    torch.cuda.synchronize()
+    del g
+    return [ev[k].elapsed_time(ev[k + 1]) for k in range(reps)]
+
+
 def stream_read_ms(rabit, torch, nbytes, reps=8):
     """Practical ceiling: a plain read-only stream of nbytes (rabit_stream_read,
     16-byte loads like the GEMV's plane loads) over rotating cold buffers
@@ -918,7 +949,7 @@ def bench_init(args, rabit, torch):
                            "achieved": round(best, 1), "frac": round(best / 8000.0, 4)})
 
 
-def _timed_decode(rabit, torch, cfg, arr, batch, steps, warmup, use_graph, xseed):
+def _timed_decode(rabit, torch, cfg, arr, batch, steps, warmup, use_graph, xseed, dist=0):
     """ms per decode step at `batch`: `warmup` untimed steps, then exactly
     `steps` steps between two HIP events on the launch stream, bracketed by
     device synchronisations. Steps ping-pong between two activation buffers
@@ -973,6 +1004,19 @@ def _timed_decode(rabit, torch, cfg, arr, batch, steps, warmup, use_graph, xseed
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
+    if dist:
+        # after the timed region: `dist` more steps, one event after each,
+        # for the per-step distribution
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(dist + 1)]
+        ev[0].record()
+        k = nxt + steps
+        for i in range(dist):
+            k = run(1, k)
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        per_step = [ev[i].elapsed_time(ev[i + 1]) for i in range(dist)]
+        del graphs, ws
+        return ms, per_step
     del graphs, ws
     return ms
 
@@ -1089,7 +1133,9 @@ def bench_llama70b(args, rabit, torch):
     arr = rabit.layer_array(cfg, layers)
     use_graph = not args.no_graph
 
-    ms1 = _timed_decode(rabit, torch, cfg, arr, 1, args.steps, args.warmup, use_graph, seed_x(5, 1))
+    ms1, steps1 = _timed_decode(rabit, torch, cfg, arr, 1, args.steps, args.warmup, use_graph, seed_x(5, 1),
+                                dist=20)
+    step_dist = {k: (round(v, 4) if k != "n" else v) for k, v in dist_summary(steps1).items()}
     gbs1 = planes / (ms1 * 1e-3) / 1e9
     log(f"batch 1: {args.steps} steps, {ms1:.3f} ms/step, {1e3 / ms1:.1f} tokens/s, {gbs1:.1f} GB/s of planes")
     steps32 = max(2, args.steps // 5)
@@ -1102,6 +1148,12 @@ def bench_llama70b(args, rabit, torch):
         lin[b] = (per, step_ms, alg)
         log(f"linear only, batch {b}: {step_ms:.3f} ms/step; per launch (us): "
             + ", ".join(f"{k} {v * 1e3:.2f}" for k, v in per.items()))
+    kinds1 = _stack_kinds(rabit, layers, H, F, 1)
+    launch_dist = {}
+    for k, f in kinds1.items():
+        d = dist_summary([t / L for t in graph_ms_dist(torch, lambda: [f(Lr) for Lr in layers], 20)])
+        launch_dist[k] = {q: (round(v * 1e3, 3) if q != "n" else v) for q, v in d.items()}
+    log(f"per-launch distribution over 20 replays (us): {launch_dist}")
     per1, lin_ms1, alg1 = lin[1]
     per32, lin_ms32, _ = lin[32]
     tot_alg = sum(alg1.values())
@@ -1155,13 +1207,15 @@ def bench_llama70b(args, rabit, torch):
                    "batch": 1, "graph_replay": use_graph, "plane_bytes_per_step": planes},
         "pct_hbm_peak": round(100.0 * gbs1 / HBM_PEAK_GBS, 2),
         "decode_tokens_per_s": round(1e3 / ms1, 2),
+        "step_ms_dist": step_dist,
         "batch32": {"ms_per_step": round(ms32, 4), "tokens_per_s": round(32e3 / ms32, 1),
                     "plane_gbs": round(planes / (ms32 * 1e-3) / 1e9, 1), "steps": steps32},
         "linear_only": {
             "b1": {"ms_per_step": round(lin_ms1, 4), "tokens_per_s": round(1e3 / lin_ms1, 2),
                    "plane_gbs": round(planes / (lin_ms1 * 1e-3) / 1e9, 1),
                    "pct_hbm_peak": round(100.0 * planes / (lin_ms1 * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
-                   "launch_us": {k: round(v * 1e3, 3) for k, v in per1.items()}},
+                   "launch_us": {k: round(v * 1e3, 3) for k, v in per1.items()},
+                   "launch_us_dist": launch_dist},
             "b32": {"ms_per_step": round(lin_ms32, 4), "tokens_per_s": round(32e3 / lin_ms32, 1),
                     "plane_gbs": round(planes / (lin_ms32 * 1e-3) / 1e9, 1),
                     "launch_us": {k: round(v * 1e3, 3) for k, v in per32.items()}},

@@ -121,12 +121,20 @@ __global__ __launch_bounds__(256, kTO == 256 ? 1 : 2) void k_grad_w(const uint16
                                                    const uint16_t* __restrict__ h, float* dW,
                                                    int accumulate, GradWs ws) {
   const int nbx = (in + kTI - 1) / kTI, nby = (out + kTO - 1) / kTO;
-  // tiles in i-fastest order; each XCD (workgroup id mod 8) takes a
-  // contiguous run of tiles when the count divides by 8
+  // Tile order: bands of G tile rows, column-major inside a band; each XCD
+  // (workgroup id mod 8, each with its own L2) takes a contiguous run of that
+  // order when the count divides by 8. An XCD's run then spans about G rows
+  // by T / (8 G) columns of tiles, which read G dY panels (128 rows each) and
+  // T / (8 G) X panels (256 columns, twice the bytes per token): G near
+  // sqrt(T / 4) keeps that union smallest, and the tiles an XCD runs at once
+  // (a few columns of one band) share their panels in its L2.
   const int T = nbx * nby;
-  int tile = blockIdx.x;
-  if ((T & 7) == 0) tile = (blockIdx.x & 7) * (T >> 3) + (blockIdx.x >> 3);
-  const int bx = tile % nbx, by = tile / nbx;
+  int o = blockIdx.x;
+  if ((T & 7) == 0) o = (blockIdx.x & 7) * (T >> 3) + (blockIdx.x >> 3);
+  const int G = max(1, min(nby, (int)sqrtf((float)T * 0.25f)));
+  const int band = o / (G * nbx), rem = o - band * G * nbx;
+  const int gb = min(G, nby - band * G);
+  const int bx = rem / gb, by = band * G + rem % gb;
   const int i0 = bx * kTI, o0 = by * kTO;
   const int tid = threadIdx.x, l = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
