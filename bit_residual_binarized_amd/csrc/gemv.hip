@@ -1007,7 +1007,10 @@ __global__ __launch_bounds__(256, P == 3 && MT == 2 ? 1 : 2) void k_gemv16(Args 
           double v = gp[0] * (double)acc[0][tau][mt][i];
 #pragma unroll
           for (int p = 1; p < P; ++p) v += gp[p] * (double)acc[p][tau][mt][i];
-          ((float*)part)[((size_t)b * A.nck + ck) * RG * 64 + row] = (float)ldexp(v, -eb[mt][i]);
+          // streaming (nontemporal) store: measured 1-2 us shorter [q,k,v], o
+          // and down launches at batch 16-32; on the digit path (batch 1) the
+          // same stores made the decode step slower, so it keeps plain ones
+          __builtin_nontemporal_store((float)ldexp(v, -eb[mt][i]), &((float*)part)[((size_t)b * A.nck + ck) * RG * 64 + row]);
         }
     }
   }
