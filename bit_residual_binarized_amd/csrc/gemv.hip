@@ -30,9 +30,11 @@
 //    and h (no separate activation pass), then its 4 waves stream 64-row
 //    groups of planes through the matrix cores (one 8 KiB slab per wave and
 //    row group, prefetched one row group ahead).
-//  * Per range, g_1 S_1 + g_2 S_2 is formed in float64 from exact integers;
-//    the ranges' partials are summed in a fixed order by the consumer (a
-//    small reduce kernel, or the fused op that follows the layer), so the
+//  * Per range, g_1 S_1 + g_2 S_2 is formed in float64 from exact integers
+//    and stored as one float32 partial (half the bytes of a float64 one for
+//    the launch that reads it next); the ranges' partials are summed in
+//    float64 in a fixed order by the consumer (a small reduce kernel, the op
+//    that follows the layer, or the next GEMV forming its input), so the
 //    output is bitwise repeatable. No atomics, no fences.
 #include <algorithm>
 #include <atomic>
@@ -96,7 +98,7 @@ struct Plan {
 
 
 __host__ inline size_t part_bytes(int out, int S, int batch) {
-  return kPartHdrDoubles * sizeof(double) + align256((size_t)batch * S * row_groups(out) * 64 * sizeof(double));
+  return kPartHdrDoubles * sizeof(double) + align256((size_t)batch * S * row_groups(out) * 64 * sizeof(float));
 }
 
 // fp16 path (batches from RABIT_GEMV_FP16_MIN_BATCH on): after each matrix's
@@ -184,10 +186,9 @@ __global__ __launch_bounds__(256) void k_gemv(Args A) {
   const int RG = si == 2 ? A.seg[2].RG : si == 1 ? A.seg[1].RG : A.seg[0].RG;
   const int rb = rbg - (si == 2 ? A.seg[2].rb0 : si == 1 ? A.seg[1].rb0 : A.seg[0].rb0);
   if (blockIdx.x == 0 && threadIdx.x < A.nseg) {
-    // the partial buffers' headers: one float64 slice per range
+    // the partial buffers' headers: one slice per range
     double* hp = threadIdx.x == 2 ? A.seg[2].part : threadIdx.x == 1 ? A.seg[1].part : A.seg[0].part;
     ((int*)hp)[0] = A.S;
-    ((int*)hp)[1] = 8;
   }
   part += kPartHdrDoubles;
 
@@ -224,15 +225,18 @@ __global__ __launch_bounds__(256) void k_gemv(Args A) {
   // Their loads go out first, ahead of h and the weights, so that they do not
   // queue behind the weight stream: 16 slices of each of the NS sums (2
   // columns per thread, and gate and up for SiLU), and for the attention
-  // input this workgroup's share of the q and k sums (kept in fp32).
+  // input this workgroup's share of the q and k sums (kept in fp32). The
+  // partials are this path's float32 ranges (the launches that form their
+  // inputs follow digit-path launches of the same step).
   constexpr int NS = XM == XSRC_ATTN ? 2 : XM == XSRC_SILU ? 4 : 1;
-  constexpr int kFormC = XM == XSRC_X ? 1 : 32 / NS;  // slices per chunk: 32 loads in flight
-  double ft[NS][kFormC], acc[NS];
-  const double* fsrc[NS];
+  constexpr int kFormC = XM == XSRC_X ? 1 : 16;  // slices per batch of loads
+  float ft[NS][kFormC];
+  double acc[NS];
+  const float* fsrc[NS];
   int fS = 0, fstride = 1;
-  double sq[XM == XSRC_ATTN ? kFormC : 1];
+  float sq[XM == XSRC_ATTN ? kFormC : 1];
   int sq_row = -1, sq_S = 0, sq_stride = 1;
-  const double* sq_src = nullptr;
+  const float* sq_src = nullptr;
   if constexpr (XM != XSRC_X) {
     fS = part_slices(A.xs.pa);
     fstride = 64 * (((XM == XSRC_ATTN ? A.xs.kv : A.in) + 63) / 64);
@@ -251,21 +255,6 @@ __global__ __launch_bounds__(256) void k_gemv(Args A) {
     for (int i = 0; i < NS; ++i)
 #pragma unroll
       for (int u = 0; u < kFormC; ++u) ft[i][u] = fsrc[i][(size_t)min(u, fS - 1) * fstride];
-    if constexpr (XM == XSRC_SILU) {
-      // gate and up: the first 8 slices are added before the next 8 go out
-      // (with h and the weights), to bound the registers held
-#pragma unroll
-      for (int i = 0; i < NS; ++i) {
-        acc[i] = 0.0;
-#pragma unroll
-        for (int u = 0; u < kFormC; ++u) acc[i] += u < fS ? ft[i][u] : 0.0;
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < NS; ++i)
-#pragma unroll
-        for (int u = 0; u < kFormC; ++u) ft[i][u] = fsrc[i][(size_t)min(kFormC + u, fS - 1) * fstride];
-    }
     if constexpr (XM == XSRC_ATTN) {
       // rows [wid per, wid per + per) of q then k: the first 256 preloaded
       // here, one per thread (any further ones after the rounds)
@@ -322,15 +311,14 @@ __global__ __launch_bounds__(256) void k_gemv(Args A) {
   __builtin_amdgcn_sched_barrier(0);  // keep every load above the first use of x and h
   if constexpr (XM != XSRC_X) {
     // the formed input: each sum's slices added in ascending order (the
-    // chunks in flight, then any further ones)
-    const int r_in_flight = XM == XSRC_SILU ? kFormC : 0;
+    // batch in flight, then any further ones)
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
-      if (XM != XSRC_SILU) acc[i] = 0.0;
+      acc[i] = 0.0;
 #pragma unroll
-      for (int u = 0; u < kFormC; ++u) acc[i] += r_in_flight + u < fS ? ft[i][u] : 0.0;
+      for (int u = 0; u < kFormC; ++u) acc[i] += u < fS ? (double)ft[i][u] : 0.0;
     }
-    for (int r = r_in_flight + kFormC; r < fS; r += kFormC) {
+    for (int r = kFormC; r < fS; r += kFormC) {
 #pragma unroll
       for (int i = 0; i < NS; ++i)
 #pragma unroll
@@ -338,7 +326,7 @@ __global__ __launch_bounds__(256) void k_gemv(Args A) {
 #pragma unroll
       for (int i = 0; i < NS; ++i)
 #pragma unroll
-        for (int u = 0; u < kFormC; ++u) acc[i] += r + u < fS ? ft[i][u] : 0.0;
+        for (int u = 0; u < kFormC; ++u) acc[i] += r + u < fS ? (double)ft[i][u] : 0.0;
     }
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
@@ -602,7 +590,7 @@ __global__ __launch_bounds__(256) void k_gemv(Args A) {
         for (int tau = 0; tau < 4; ++tau) {
           const int row = rg * 64 + 16 * tau + j;
           if (row >= out) continue;
-            part[((size_t)b * A.S + r) * RG * 64 + row] = res[q][tau];
+            ((float*)part)[((size_t)b * A.S + r) * RG * 64 + row] = (float)res[q][tau];
         }
       }
     }
@@ -613,9 +601,9 @@ __global__ __launch_bounds__(256) void k_gemv(Args A) {
     if (sq_row >= 0) {
       double v = 0.0;
 #pragma unroll
-      for (int u = 0; u < kFormC; ++u) v += u < sq_S ? sq[u] : 0.0;
+      for (int u = 0; u < kFormC; ++u) v += u < sq_S ? (double)sq[u] : 0.0;
       for (int r = kFormC; r < sq_S; r += kFormC)
-        for (int u = 0; u < kFormC && r + u < sq_S; ++u) v += sq_src[(size_t)(r + u) * sq_stride];
+        for (int u = 0; u < kFormC && r + u < sq_S; ++u) v += (double)sq_src[(size_t)(r + u) * sq_stride];
       A.xs.qk[sq_row] = (float)v;
     }
   }
@@ -808,10 +796,9 @@ __global__ __launch_bounds__(256, P == 3 && MT == 2 ? 1 : 2) void k_gemv16(Args 
   const int RG = si == 2 ? A.seg[2].RG : si == 1 ? A.seg[1].RG : A.seg[0].RG;
   const int rb = rbg - (si == 2 ? A.seg[2].rb0 : si == 1 ? A.seg[1].rb0 : A.seg[0].rb0);
   if (blockIdx.x == 0 && threadIdx.x < A.nseg) {
-    // the partial buffers' headers: one float32 slice per chunk
+    // the partial buffers' headers: one slice per chunk of ranges
     double* hp = threadIdx.x == 2 ? A.seg[2].part : threadIdx.x == 1 ? A.seg[1].part : A.seg[0].part;
     ((int*)hp)[0] = A.nck;
-    ((int*)hp)[1] = 4;
   }
   part += kPartHdrDoubles;
 
@@ -1024,14 +1011,8 @@ __global__ __launch_bounds__(256) void k_gemv_reduce(const double* __restrict__ 
   const int S = part_slices(part);
   // many ranges (wide layers): 32 loads in flight per round trip
   const size_t at = (size_t)b * S * RG * 64 + row;
-  double v;
-  if (part_elem_bytes(part) == 4) {
-    const float* pp = (const float*)part_data(part) + at;
-    v = S <= 8 ? sum_ranges_by<8>(pp, S, RG * 64) : sum_ranges_by<32>(pp, S, RG * 64);
-  } else {
-    const double* pp = part_data(part) + at;
-    v = S <= 8 ? sum_ranges_by<8>(pp, S, RG * 64) : sum_ranges_by<32>(pp, S, RG * 64);
-  }
+  const float* pp = part_data(part) + at;
+  const double v = S <= 8 ? sum_ranges_by<8>(pp, S, RG * 64) : sum_ranges_by<32>(pp, S, RG * 64);
   if (y_dtype == RABIT_OUT_F32)
     ((float*)y)[(size_t)b * out + row] = (float)v;
   else

@@ -223,7 +223,7 @@ hipError_t launch_gemv_reduce(int out, int in, int batch, void* y, int y_dtype, 
 
 
 // Several matrices that read the same input in one launch (q/k/v, gate/up):
-// each leaves its partial buffer (header, then float64 partials
+// each leaves its partial buffer (header, then float32 partials
 // [batch][slices][64*ceil(out/64)], slices at most ceil(in/512)) in part.
 // With stats != nullptr the input is RMSNorm(x) (unit weight, eps), rounded to
 // bfloat16, with stats[b][RABIT_STAT_PARTS] the partial sums of x^2 of row b.
@@ -238,21 +238,21 @@ struct LinSeg {
 #define RABIT_STAT_PARTS 32
 
 // A GEMV launch's partial buffer for one matrix: a 256-byte header whose
-// first int32 is the number of partial slices per output row and whose
-// second is the bytes per partial (8: float64, written by the digit path; 4:
-// float32, the fp16 path's chunk partials), then the partials
-// [batch][slices][64*ceil(out/64)].
+// first int32 is the number of partial slices per output row, then the
+// float32 partials [batch][slices][64*ceil(out/64)] (the digit path writes one
+// slice per range of 512 columns, the fp16 path one per chunk of ranges).
 constexpr int kPartHdrDoubles = 32;
 __host__ __device__ __forceinline__ int part_slices(const double* part) { return *(const int*)part; }
-__host__ __device__ __forceinline__ int part_elem_bytes(const double* part) { return ((const int*)part)[1]; }
-__host__ __device__ __forceinline__ const double* part_data(const double* part) { return part + kPartHdrDoubles; }
+__host__ __device__ __forceinline__ const float* part_data(const double* part) {
+  return (const float*)(part + kPartHdrDoubles);
+}
 
-// Σ_r part[b][r][i] over the S ranges of a GEMV's float64 partials (row
+// Σ_r part[b][r][i] over the S slices of a GEMV's partials (row
 // stride `stride`), added in ascending r, with the loads of C ranges in flight
 // together (clamped index, masked). The decode consumers use C = 8: a wider
 // chunk makes these small kernels slower to start than the round trips it saves.
-template <int C, typename T = double>
-__device__ __forceinline__ double sum_ranges_by(const T* __restrict__ pp, int S, int stride) {
+template <int C>
+__device__ __forceinline__ double sum_ranges_by(const float* __restrict__ pp, int S, int stride) {
   double v = 0.0;
   for (int r = 0; r < S; r += C) {
     double t[C];
@@ -267,7 +267,6 @@ __device__ __forceinline__ double sum_ranges_by(const T* __restrict__ pp, int S,
 __device__ __forceinline__ double sum_ranges(const double* __restrict__ part, int b, int stride, int i) {
   const int S = part_slices(part);
   const size_t at = (size_t)b * S * stride + i;
-  if (part_elem_bytes(part) == 4) return sum_ranges_by<8>((const float*)part_data(part) + at, S, stride);
   return sum_ranges_by<8>(part_data(part) + at, S, stride);
 }
 size_t gemv_part_bytes(int out, int in, int batch);

@@ -178,8 +178,9 @@ int rabit_unpack(const rabit_layer *layer, uint32_t *words, void *stream);
  * columns), scaled by a power of two so that the range's largest |h_p*x| maps
  * into [2^18, 2^19) (per-element error <= 2^-19 of that largest value); the
  * signed sums are exact integers; each range's g_1 S_1 + g_2 S_2 is formed in
- * float64, the ranges are summed in float64 in ascending order and the result
- * is rounded once.
+ * float64 and rounded to float32 (within 2^-24 of Σ_p |g_p| Σ_range |h_p x|
+ * plus the grid error), the ranges are summed in float64 in ascending order
+ * and the result is rounded once.
  * Arithmetic, batch >= RABIT_GEMV_FP16_MIN_BATCH: each token row of x is
  * scaled by a power of two 2^e so that its largest |x| lies in [2^14, 2^15)
  * and rounded to fp16 (exact for values above 2^-32 of that largest one, the
@@ -208,7 +209,7 @@ int rabit_gemv(const rabit_layer *layer, const uint16_t *x, int32_t batch,
  * library holds on every GPU it runs on until the process ends (its address
  * is looked up once per device, on the first call there).
  * Limit: rabit_gemv_workspace_bytes(out, in, batch) <= RABIT_NOALLOC_SCRATCH_BYTES
- * (e.g. a 28672 x 8192 or 8192 x 28672 layer up to batch 4), else
+ * (e.g. a 28672 x 8192 or 8192 x 28672 layer up to batch 8), else
  * RABIT_ESCRATCH before anything is enqueued.
  * Every call on one GPU shares that GPU's scratch: calls that may overlap on
  * one GPU (different streams without ordering between them, or several host
@@ -224,9 +225,9 @@ int rabit_gemv_noalloc(const rabit_layer *layer, const uint16_t *x, int32_t batc
 /*
  * The two halves of rabit_gemv, for callers that time or schedule them apart.
  * rabit_gemv_partial streams every plane byte in one kernel launch and leaves
- * in the workspace the partial result of each range of 512 input columns
- * (float64; from RABIT_GEMV_FP16_MIN_BATCH on, of each chunk of ranges, in
- * float32), after a header that records their count and width;
+ * in the workspace the partial result, in float32, of each range of 512
+ * input columns (from RABIT_GEMV_FP16_MIN_BATCH on, of each chunk of
+ * ranges), after a header that records their count;
  * rabit_gemv_reduce sums those partials (ascending order) into y.
  * A reduce consumes the workspace of the last partial for the same layer and
  * batch; the pair gives the same bits as rabit_gemv. Errors as rabit_gemv.

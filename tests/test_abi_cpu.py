@@ -320,7 +320,7 @@ def test_gemv_noalloc_argument_errors(lib):
     assert na(L3, y=FAKE + 32768) == rabit.RABIT_EINVAL               # y on the third plane
     # partials beyond the fixed scratch buffer
     big = fake_layer(28672, 8192, planes=FAKE, g=FAKE + (1 << 30), h=FAKE + (2 << 30))
-    need = lib.rabit_gemv_workspace_bytes(28672, 8192, 8)
+    need = lib.rabit_gemv_workspace_bytes(28672, 8192, 9)
     assert need > rabit.NOALLOC_SCRATCH_BYTES
-    assert na(big, batch=8, x=FAKE + (3 << 32), y=FAKE + (4 << 32)) == rabit.RABIT_ESCRATCH
-    assert lib.rabit_gemv_workspace_bytes(28672, 8192, 4) <= rabit.NOALLOC_SCRATCH_BYTES
+    assert na(big, batch=9, x=FAKE + (3 << 32), y=FAKE + (4 << 32)) == rabit.RABIT_ESCRATCH
+    assert lib.rabit_gemv_workspace_bytes(28672, 8192, 8) <= rabit.NOALLOC_SCRATCH_BYTES

@@ -58,8 +58,10 @@ def fx_bound(d, xv):
 
     Per (batch row, path, range of 512 columns) h_p*x is rounded to a grid of
     step 2^(ilogb(max |h_p*x|) - 18), so each element is off by at most half a
-    step; the signed sums are exact and g_p is applied in float64. The fp32
-    output rounding is covered separately (2^-23 |y|)."""
+    step; the signed sums are exact and g_p is applied in float64; each
+    range's partial is rounded to float32 (within 2^-24 of Σ_p |g_p| Σ_range
+    |rounded h_p*x|). The fp32 output rounding is covered separately
+    (2^-23 |y|)."""
     xb = np.atleast_2d(xv)
     B, K = xb.shape
     bound = np.zeros((B, d.g1.shape[0]))
@@ -70,7 +72,9 @@ def fx_bound(d, xv):
             mr = u[:, c0:c0 + 512].max(axis=1)
             _, e = np.frexp(mr)  # mr = f 2^e, f in [0.5, 1): ilogb = e - 1
             tot += np.where(mr > 0, min(512, K - c0) * np.exp2(e - 1.0 - 19.0), 0.0)
-        bound += np.abs(g.astype(np.float64))[None, :] * tot[:, None]
+        # the float32 rounding of every range's partial
+        part = 2.0 ** -24 * (u.sum(axis=1) + tot)
+        bound += np.abs(g.astype(np.float64))[None, :] * (tot + part)[:, None]
     return bound
 
 

@@ -111,7 +111,8 @@ TOL = 2e-3
 def fx_bound(d, xv):
     """Elementwise bound of the GEMV arithmetic (rabit.h): per (batch row, path,
     512-column range) h_p*x on a grid of step 2^(ilogb(max |h_p*x|) - 18),
-    exact signed sums, g_p in float64; summed over the paths."""
+    exact signed sums, g_p in float64, each range's partial rounded to
+    float32; summed over the paths."""
     xb = np.atleast_2d(xv)
     B, K = xb.shape
     bound = np.zeros((B, d.g1.shape[0]))
@@ -122,7 +123,9 @@ def fx_bound(d, xv):
             mr = u[:, c0:c0 + 512].max(axis=1)
             _, e = np.frexp(mr)
             tot += np.where(mr > 0, min(512, K - c0) * np.exp2(e - 1.0 - 19.0), 0.0)
-        bound += np.abs(g.astype(np.float64))[None, :] * tot[:, None]
+        # the float32 rounding of every range's partial
+        part = 2.0 ** -24 * (u.sum(axis=1) + tot)
+        bound += np.abs(g.astype(np.float64))[None, :] * (tot + part)[:, None]
     return bound
 
 

@@ -59,13 +59,13 @@ def test_gemv_noalloc_matches_gemv(gpu_lib):
 def test_gemv_noalloc_too_large_is_rejected(gpu_lib):
     rabit = gpu_lib
     L = _layer(rabit, 28672, 8192, 11)
-    x = act_bf16(8, 8192, 12).cuda()
-    y = torch.empty(8, 28672, device="cuda")
+    x = act_bf16(9, 8192, 12).cuda()
+    y = torch.empty(9, 28672, device="cuda")
     with pytest.raises(rabit.RabitError) as e:
         rabit.gemv_noalloc(L, x, y)
     assert e.value.code == rabit.RABIT_ESCRATCH
     # at the limit's largest batch it runs and matches
-    x4 = x[:4].contiguous()
-    y4 = torch.empty(4, 28672, device="cuda")
-    rabit.gemv_noalloc(L, x4, y4)
-    assert torch.equal(y4, rabit.gemv(L, x4))
+    x8 = x[:8].contiguous()
+    y8 = torch.empty(8, 28672, device="cuda")
+    rabit.gemv_noalloc(L, x8, y8)
+    assert torch.equal(y8, rabit.gemv(L, x8))
