@@ -1076,12 +1076,13 @@ def _linear_only(rabit, torch, layers, H, F, KV, batch, reps=3):
 
 def cpu_baseline_70b(rabit, budget_s, frac=8):
     """The oracle (float64 numpy) on the host over a bounded sample of the
-    Llama-2-70B step: for layers {0, 39, 79}, the first out/frac output rows
+    Llama-2-70B step: for layers {0, 39, 79}, blocks of out/frac output rows
     of each of the seven matrices (given fp16 scales of the mean-|.|
     magnitude; the derivation is set-up and not timed), the oracle's GEMV
     (W_eff reconstruction in float64, then the product with x) at batch 1.
-    Extrapolated to the whole step: x (rows / sampled rows) per matrix and
-    x 80/3 over the layers."""
+    Row blocks are added, all 21 matrices at a time, until the timed GEMVs
+    reach budget_s seconds (or every row is done). Extrapolated to the whole
+    step: x (rows / sampled rows) per matrix and x 80/3 over the layers."""
     import numpy as np
     import oracle
     from synth.inputs import act_bf16, bf16_values, random_f16_scales, weight_f32
@@ -1093,32 +1094,42 @@ def cpu_baseline_70b(rabit, budget_s, frac=8):
     c = L70
     H, F, KV = c["H"], c["F"], c["KV"]
     shapes = layer_shapes(H, F, KV)
-    t_step, t_sample, w_sample = 0.0, 0.0, 0
-    for li in (0, 39, 79):
-        for k, (name, (o, i)) in enumerate(shapes.items()):
-            R = max(64, o // frac)
-            w = weight_f32(R, i, 5000 + 10 * li + k).numpy()
-            g1, g2 = random_f16_scales(R, 1, 0.010, 0.022), random_f16_scales(R, 2, 0.008, 0.018)
-            h1, h2 = random_f16_scales(i, 3, 0.010, 0.022), random_f16_scales(i, 4, 0.008, 0.018)
-            d = oracle.derive(w, mode="given", g1=g1, h1=h1, g2=g2, h2=h2)
-            d.r = None
-            del w
-            x = bf16_values(act_bf16(1, i, 7 + k))
-            t0 = time.perf_counter()
-            oracle.gemv(d, x)
-            dt = time.perf_counter() - t0
-            t_sample += dt
-            w_sample += R * i
-            t_step += dt * (o / R)
-            del d
-    t_step *= c["L"] / 3.0
+    t_sample, w_sample, blocks = 0.0, 0, 0
+    done = {}    # (layer, matrix) -> [seconds, rows]
+    for blk in range(frac):
+        for li in (0, 39, 79):
+            for k, (name, (o, i)) in enumerate(shapes.items()):
+                R = max(64, o // frac)
+                rows = min(R, o - blk * R)
+                if rows <= 0:
+                    continue
+                w = weight_f32(rows, i, 5000 + 10 * li + k + 1000 * blk).numpy()
+                g1, g2 = random_f16_scales(rows, 1, 0.010, 0.022), random_f16_scales(rows, 2, 0.008, 0.018)
+                h1, h2 = random_f16_scales(i, 3, 0.010, 0.022), random_f16_scales(i, 4, 0.008, 0.018)
+                d = oracle.derive(w, mode="given", g1=g1, h1=h1, g2=g2, h2=h2)
+                d.r = None
+                del w
+                x = bf16_values(act_bf16(1, i, 7 + k))
+                t0 = time.perf_counter()
+                oracle.gemv(d, x)
+                dt = time.perf_counter() - t0
+                t_sample += dt
+                w_sample += rows * i
+                s = done.setdefault((li, name), [0.0, 0])
+                s[0] += dt
+                s[1] += rows
+                del d
+        blocks += 1
+        if t_sample >= budget_s:
+            break
+    t_step = sum(s[0] * shapes[name][0] / s[1] for (li, name), s in done.items()) * c["L"] / 3.0
     plane_bytes = sum(rabit.planes_bytes(o, i) for o, i in shapes.values()) * c["L"]
     return {
         "value": round(plane_bytes / t_step / 1e9, 5),
         "unit": "GB/s",
         "cores": len(os.sched_getaffinity(0)),
         "kind": "oracle",
-        "sample": (f"layers 0, 39, 79 of the Llama-2-70B stack, first 1/{frac} of the output rows of each of "
+        "sample": (f"layers 0, 39, 79 of the Llama-2-70B stack, first {blocks}/{frac} of the output rows of each of "
                    f"q, k, v, o, gate, up, down ({w_sample / 1e6:.0f} M weights, {t_sample:.1f} s): oracle "
                    "float64 W_eff reconstruction + product with x at batch 1; extrapolated x rows/sample "
                    "per matrix and x 80/3 over the layers; GB/s of packed-plane bytes per step"),
