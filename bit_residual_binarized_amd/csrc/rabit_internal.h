@@ -249,8 +249,9 @@ __host__ __device__ __forceinline__ const float* part_data(const double* part) {
 
 // Σ_r part[b][r][i] over the S slices of a GEMV's partials (row
 // stride `stride`), added in ascending r, with the loads of C ranges in flight
-// together (clamped index, masked). The decode consumers use C = 8: a wider
-// chunk makes these small kernels slower to start than the round trips it saves.
+// together (clamped index, masked). sum_ranges, which the attention and
+// SiLU consumers use, takes C = 8; the residual consumer takes C = 32 beyond
+// 8 slices (measured: 64 in flight was slower than either).
 template <int C>
 __device__ __forceinline__ double sum_ranges_by(const float* __restrict__ pp, int S, int stride) {
   double v = 0.0;
