@@ -53,8 +53,11 @@ def batch(out, inp, m, seed):
     return x, dy, bf16_values(x), bf16_values(dy)
 
 
+# Shapes whose out and in are multiples of 8 take the dW kernel's ring loader
+# (ragged tiles: 384 = 1.5 x 256 columns, 200 / 264 / 1104 off the tile
+# grid; token counts off the 32-token step), the others its staged loader.
 SHAPES = [(256, 384, 100), (200, 333, 37), (130, 520, 1), (384, 256, 513), (64, 128, 32),
-          (1, 1, 3), (1000, 1100, 300)]
+          (1, 1, 3), (1000, 1100, 300), (200, 264, 45), (1000, 1104, 300)]
 
 
 @pytest.mark.parametrize("n_paths", [2, 3])
@@ -98,6 +101,38 @@ def test_grad_weight(gpu_lib, shape, n_paths):
         eg = oracle.normwise_rel_err(dg[p], rg)
         eh = oracle.normwise_rel_err(dh[p], rh)
         assert eg <= TOL_SCALE and eh <= TOL_SCALE, (p, eg, eh)
+
+
+@pytest.mark.parametrize("n_paths", [2, 3])
+def test_grad_weight_loaders_agree(gpu_lib, n_paths):
+    """The ring loader (in a multiple of 8) and the staged loader give the
+    same bits: a 200 x 264 layer against the same layer with a 265th input
+    column whose X column is zero (so its dW column is zero and adds nothing
+    to dg); dW, dg and dh of the first 264 columns compared bit for bit."""
+    out, inp, m = 200, 264, 77
+    say("grad_weight loaders", n_paths)
+    w = weight_f32(out, inp + 1, 4250).numpy()
+    g = [random_f16_scales(out, 4251), random_f16_scales(out, 4252, 0.002, 0.01),
+         random_f16_scales(out, 4253, 0.001, 0.004)][:n_paths]
+    h = [random_f16_scales(inp + 1, 4254), random_f16_scales(inp + 1, 4255, 0.002, 0.01),
+         random_f16_scales(inp + 1, 4256, 0.001, 0.004)][:n_paths]
+    layers = []
+    for n in (inp, inp + 1):
+        layer = gpu_lib.PackedLayer.empty(out, n, n_paths=n_paths)
+        layer.g.copy_(torch.from_numpy(np.stack(g)).view(torch.int16))
+        layer.h.copy_(torch.from_numpy(np.ascontiguousarray(np.stack(h)[:, :n])).view(torch.int16))
+        gpu_lib.pack(torch.from_numpy(np.ascontiguousarray(w[:, :n])).cuda(), layer, gpu_lib.RABIT_SCALES_GIVEN)
+        layers.append(layer)
+    x = act_bf16(m, inp, 4257)
+    dy = grad_bf16(m, out, 4258).cuda()
+    x1 = torch.zeros(m, inp + 1, dtype=torch.bfloat16)
+    x1[:, :inp] = x
+    ra = gpu_lib.grad_weight(layers[0], x.cuda(), dy)
+    rb = gpu_lib.grad_weight(layers[1], x1.cuda(), dy)
+    torch.cuda.synchronize()
+    assert torch.equal(ra[0], rb[0][:, :inp])
+    assert torch.equal(ra[1], rb[1])
+    assert torch.equal(ra[2], rb[2][:, :inp])
 
 
 def test_grad_weight_accumulate(gpu_lib):
