@@ -508,6 +508,8 @@ __global__ __launch_bounds__(256) void k_gemv(Args A) {
           (v8i){(int)0x99999999u, (int)0x99999999u, (int)0x99999999u, (int)0x99999999u, 0, 0, 0, 0},
           (v4f){0.f, 0.f, 0.f, 0.f}, 2, 4, 0, ascale, 0, 127);
 
+  // masks of slice 3, set once outside the rounds
+  const uint32_t m3s = 0x88888888u, o3v = 0x11111111u;
   // one round: row group 4 m rb + 4 k + w from the weights in wt
   auto round = [&](const uint4 (&wt)[4 * P], const uint16_t (&gt)[4 * P], int k) {
     const int rg = 4 * m * rb + 4 * k + w;
@@ -525,8 +527,7 @@ __global__ __launch_bounds__(256) void k_gemv(Args A) {
         constexpr int T = decltype(tc)::value;
         // T0: w & 0x1..1 (0.5), T1: w & 0x2..2 (1.0), T2: w & 0x4..4 (2.0, the
         // operand scale halved), T3: (w & 0x8..8) | 0x1..1 (+0.5 or -0.5)
-        constexpr uint32_t mT = T == 0 ? 0x11111111u : T == 1 ? 0x22222222u : T == 2 ? 0x44444444u : 0x88888888u;
-        constexpr uint32_t oT = T == 3 ? 0x11111111u : 0u;
+        constexpr uint32_t mT = T == 0 ? 0x11111111u : T == 1 ? 0x22222222u : 0x44444444u;
         const int sc = T == 2 ? ascale - 1 : ascale;
         v8i a[NBP];
 #pragma unroll
@@ -534,8 +535,20 @@ __global__ __launch_bounds__(256) void k_gemv(Args A) {
 #pragma unroll
         for (int tau = 0; tau < 4; ++tau) {
           const uint4 wv = wt[tau * P + p];
-          const v8i bv = (v8i){(int)((wv.x & mT) | oT), (int)((wv.y & mT) | oT),
-                               (int)((wv.z & mT) | oT), (int)((wv.w & mT) | oT), 0, 0, 0, 0};
+          v8i bv;
+          if constexpr (T == 3) {
+            // (w & 0x8..8) | 0x1..1 as one bitfield insert (the compiler emits an
+            // AND and an OR, each with a literal); the mask in a scalar register,
+            // the inserted constant in a vector one (one scalar operand per
+            // instruction on this target)
+            uint32_t r[4];
+            const uint32_t wd[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+            for (int d = 0; d < 4; ++d) asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r[d]) : "s"(m3s), "v"(wd[d]), "v"(o3v));
+            bv = (v8i){(int)r[0], (int)r[1], (int)r[2], (int)r[3], 0, 0, 0, 0};
+          } else {
+            bv = (v8i){(int)(wv.x & mT), (int)(wv.y & mT), (int)(wv.z & mT), (int)(wv.w & mT), 0, 0, 0, 0};
+          }
 #pragma unroll
           for (int q = 0; q < NBP; ++q)
             acc[q][tau] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
