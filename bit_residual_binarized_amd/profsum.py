@@ -1,0 +1,157 @@
+"""Summaries of rocprofv3 output (CSV) for the decode GEMV's launch shapes.
+
+usage:
+  python -m bit_residual_binarized_amd.profsum stats TRACE_DIR
+      per (kernel, grid size): dispatch count and the median, mean and
+      minimum of rocprof's per-dispatch durations (us), from the kernel trace
+      of `rocprofv3 --kernel-trace --output-format csv`.
+  python -m bit_residual_binarized_amd.profsum traffic FETCH_DIR WRITE_DIR
+      HBM bytes per k_gemv launch of the Llama-2-70B batch-1 step's four
+      launch shapes, from one `--pmc FETCH_SIZE` and one `--pmc WRITE_SIZE`
+      pass over `bench.py` (counter_collection CSV). Each counter (KiB per
+      dispatch) is divided by the factor the same counter reads on the plain
+      256 MiB device copy that bench.py runs in the same process (the
+      runtime's copy kernel), so that the result is bytes.
+
+Both print `key: value` lines (the traffic form is what bench.py reads back
+from the committed summary).
+"""
+from __future__ import annotations
+
+import csv
+import glob
+import hashlib
+import os
+import re
+import statistics
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GEMV_SRC = os.path.join(ROOT, "bit_residual_binarized_amd", "csrc", "gemv.hip")
+COPY_BYTES = 256 << 20  # the calibration copy in bench.py
+CAL_KERNEL = "__amd_rocclr_copyBuffer"
+
+# Llama-2-70B batch-1 launch shapes of the linear-only timing: (kernel
+# template arguments, grid threads) -> label. The plan gives [q,k,v] and o one
+# row group per wave (no weight ring), [gate,up] seven and down four (ring).
+SHAPES_70B_B1 = {
+    ("k_gemv<1, false, false, 2, 0>", 640 * 256): "qkv",
+    ("k_gemv<1, false, false, 2, 0>", 512 * 256): "o",
+    ("k_gemv<1, true, false, 2, 0>", 512 * 256): "gate+up",
+    ("k_gemv<1, true, false, 2, 0>", 448 * 256): "down",
+}
+
+
+def gemv_sha() -> str:
+    with open(GEMV_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def _rows(d: str, suffix: str) -> list[dict]:
+    files = sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True))
+    if not files:
+        raise SystemExit(f"no *{suffix} under {d}")
+    rows = []
+    for fn in files:
+        with open(fn, newline="") as f:
+            rows.extend(csv.DictReader(f))
+    return rows
+
+
+def _short(name: str) -> str:
+    # "void rabit::(anonymous namespace)::k_gemv<1, true, false, 2, 0>(rabit::...)" -> "k_gemv<1, true, false, 2, 0>"
+    m = re.search(r"(\w+)(<[^()]*>)?\(", name)
+    if not m:
+        return name.strip()
+    return m.group(1) + (m.group(2) or "")
+
+
+def _grid(r: dict) -> int:
+    for k in ("Grid_Size", "Grid_Size_X", "grid_size"):
+        if k in r and r[k]:
+            return int(float(r[k]))
+    return 0
+
+
+def stats(trace_dir: str) -> None:
+    rows = _rows(trace_dir, "kernel_trace.csv")
+    groups: dict[tuple[str, int], list] = {}
+    for r in rows:
+        key = (_short(r["Kernel_Name"]), _grid(r))
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        g = groups.setdefault(key, [[], r.get("VGPR_Count", ""), r.get("Accum_VGPR_Count", ""),
+                                    r.get("Group_Segment_Size", r.get("LDS_Block_Size", ""))])
+        g[0].append(dur)
+    print(f"gemv_source_sha256: {gemv_sha()}")
+    print(f"{'calls':>6} {'grid_threads':>13} {'median_us':>10} {'mean_us':>9} {'min_us':>8} "
+          f"{'vgpr':>5} {'agpr':>4} {'lds':>6}  kernel  (launch)")
+    for (k, grid), (d, vg, ag, lds) in sorted(groups.items(), key=lambda kv: -sum(kv[1][0])):
+        lab = SHAPES_70B_B1.get((k, grid), "")
+        print(f"{len(d):6d} {grid:13d} {statistics.median(d):10.2f} {statistics.fmean(d):9.2f} "
+              f"{min(d):8.2f} {vg:>5} {ag:>4} {lds:>6}  {k}" + (f"  [{lab}] b1" if lab else ""))
+    per = {}
+    for (k, grid), (d, *_rest) in groups.items():
+        lab = SHAPES_70B_B1.get((k, grid))
+        if lab:
+            per[lab] = statistics.median(d)
+    if len(per) == 4:
+        print("k_gemv_b1_median_us: " + ", ".join(f"{lab} {per[lab]:.2f}" for lab in ("qkv", "o", "gate+up", "down")))
+        print(f"k_gemv_b1_mean_of_shapes_us: {statistics.fmean(per.values()):.2f}")
+
+
+def _counter(d: str, counter: str) -> tuple[dict, float]:
+    rows = [r for r in _rows(d, "counter_collection.csv") if r["Counter_Name"] == counter]
+    cal = [float(r["Counter_Value"]) for r in rows if CAL_KERNEL in r["Kernel_Name"]]
+    if not cal:
+        raise SystemExit(f"{counter}: no {CAL_KERNEL} dispatch in {d}")
+    # the calibration copy is the largest copy dispatch of the run
+    factor = max(cal) / (COPY_BYTES / 1024)
+    per: dict[str, list] = {}
+    for r in rows:
+        lab = SHAPES_70B_B1.get((_short(r["Kernel_Name"]), _grid(r)))
+        if lab:
+            per.setdefault(lab, []).append(float(r["Counter_Value"]) / factor)
+    return per, factor
+
+
+def traffic(fetch_dir: str, write_dir: str) -> None:
+    sys.path.insert(0, ROOT)
+    import bench  # algorithmic bytes of each launch shape, as bench.py counts them
+
+    c = bench.L70
+    H, F, KV = c["H"], c["F"], c["KV"]
+    alg = {"qkv": bench.launch_alg_bytes([H, KV, KV], H), "o": bench.gemv_alg_bytes(H, H),
+           "gate+up": bench.launch_alg_bytes([F, F], H), "down": bench.gemv_alg_bytes(H, F)}
+    fetch, ff = _counter(fetch_dir, "FETCH_SIZE")
+    write, wf = _counter(write_dir, "WRITE_SIZE")
+    print(f"gemv_source_sha256: {gemv_sha()}")
+    print(f"calibration_kernel: {CAL_KERNEL}")
+    print(f"fetch_factor: {ff:.4f}")
+    print(f"write_factor: {wf:.4f}")
+    tot_t = tot_a = 0.0
+    for lab in ("qkv", "o", "gate+up", "down"):
+        if lab not in fetch or lab not in write:
+            raise SystemExit(f"launch shape {lab} missing from the counter runs")
+        fk = statistics.fmean(fetch[lab])
+        wk = statistics.fmean(write[lab])
+        t = (fk + wk) * 1024
+        tot_t += t
+        tot_a += alg[lab]
+        print(f"{lab}_launches: {len(fetch[lab])}")
+        print(f"{lab}_fetch_kib: {fk:.1f}")
+        print(f"{lab}_write_kib: {wk:.1f}")
+        print(f"{lab}_traffic_bytes: {t:.0f}")
+        print(f"{lab}_algorithmic_bytes: {alg[lab]}")
+        print(f"{lab}_fetch_over_algorithmic: {fk * 1024 / alg[lab]:.4f}")
+    print(f"traffic_bytes_per_launch: {tot_t / 4:.0f}")
+    print(f"algorithmic_bytes_per_launch: {tot_a / 4:.0f}")
+    print(f"traffic_over_algorithmic: {tot_t / tot_a:.4f}")
+
+
+if __name__ == "__main__":
+    if len(sys.argv) == 3 and sys.argv[1] == "stats":
+        stats(sys.argv[2])
+    elif len(sys.argv) == 4 and sys.argv[1] == "traffic":
+        traffic(sys.argv[2], sys.argv[3])
+    else:
+        raise SystemExit(__doc__)
