@@ -12,9 +12,15 @@ usage:
       dispatch) is divided by the factor the same counter reads on the plain
       256 MiB device copy that bench.py runs in the same process (the
       runtime's copy kernel), so that the result is bytes.
+  python -m bit_residual_binarized_amd.profsum counters PMC_DIR
+      per launch shape of the 70B batch-1 step (the four plain-input launches
+      and the two that form their inputs), instruction counts per wave
+      (device sums / SQ_WAVES) and SQ_WAIT_ANY / SQ_WAVE_CYCLES, from one
+      `--pmc SQ_WAVES SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_INSTS_VALU
+      SQ_INSTS_MFMA SQ_INSTS_SALU SQ_INSTS_LDS SQ_WAIT_ANY` pass.
 
-Both print `key: value` lines (the traffic form is what bench.py reads back
-from the committed summary).
+The output starts with `key: value` lines (the traffic form is what bench.py
+reads back from the committed summary).
 """
 from __future__ import annotations
 
@@ -40,6 +46,16 @@ SHAPES_70B_B1 = {
     ("k_gemv<1, true, false, 2, 0>", 512 * 256): "gate+up",
     ("k_gemv<1, true, false, 2, 0>", 448 * 256): "down",
 }
+
+
+# the launches of the decode step that form their inputs from the previous
+# launch's partials (attention output for o, SiLU(gate) * up for down)
+SHAPES_70B_B1_FORMED = {
+    ("k_gemv<1, false, false, 2, 1>", 512 * 256): "o, attention input formed",
+    ("k_gemv<1, true, false, 2, 2>", 448 * 256): "down, SiLU input formed",
+}
+LABELS = {"qkv": "[q,k,v] 10240x8192", "o": "o 8192x8192", "gate+up": "[gate,up] 57344x8192",
+          "down": "down 8192x28672"}
 
 
 def gemv_sha() -> str:
@@ -148,9 +164,39 @@ def traffic(fetch_dir: str, write_dir: str) -> None:
     print(f"traffic_over_algorithmic: {tot_t / tot_a:.4f}")
 
 
+def counters(pmc_dir: str) -> None:
+    rows = _rows(pmc_dir, "counter_collection.csv")
+    shapes = {**{k: LABELS[v] for k, v in SHAPES_70B_B1.items()}, **SHAPES_70B_B1_FORMED}
+    # per dispatch: counter -> value (a dispatch is one Dispatch_Id)
+    disp: dict[tuple, dict] = {}
+    for r in rows:
+        key = (_short(r["Kernel_Name"]), _grid(r))
+        if key not in shapes:
+            continue
+        d = disp.setdefault((key, r.get("Dispatch_Id", r.get("Correlation_Id"))), {})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    print(f"gemv_source_sha256: {gemv_sha()}")
+    order = list(shapes)
+    for key in order:
+        ds = [v for (k, _), v in disp.items() if k == key]
+        if not ds:
+            continue
+        tot = {c: sum(d.get(c, 0.0) for d in ds) for c in ds[0]}
+        waves = tot["SQ_WAVES"] / len(ds)
+        per = {c: tot[c] / tot["SQ_WAVES"] for c in tot}
+        kern, grid = key
+        ring, xm = kern.split(", ")[1], kern.split(", ")[4].rstrip(">")
+        print(f"\n{shapes[key]} (ring {ring}, XM {xm}, grid {grid}), launches {len(ds)}")
+        print(f"  waves {waves:.0f}; per wave: VALU {per['SQ_INSTS_VALU']:.0f} (matrix {per['SQ_INSTS_MFMA']:.0f}), "
+              f"SALU {per['SQ_INSTS_SALU']:.0f}, LDS {per['SQ_INSTS_LDS']:.0f}")
+        print(f"  wait_fraction = SQ_WAIT_ANY / SQ_WAVE_CYCLES: {tot['SQ_WAIT_ANY'] / tot['SQ_WAVE_CYCLES']:.3f}")
+
+
 if __name__ == "__main__":
     if len(sys.argv) == 3 and sys.argv[1] == "stats":
         stats(sys.argv[2])
+    elif len(sys.argv) == 3 and sys.argv[1] == "counters":
+        counters(sys.argv[2])
     elif len(sys.argv) == 4 and sys.argv[1] == "traffic":
         traffic(sys.argv[2], sys.argv[3])
     else:
