@@ -18,6 +18,11 @@ usage:
       (device sums / SQ_WAVES) and SQ_WAIT_ANY / SQ_WAVE_CYCLES, from one
       `--pmc SQ_WAVES SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_INSTS_VALU
       SQ_INSTS_MFMA SQ_INSTS_SALU SQ_INSTS_LDS SQ_WAIT_ANY` pass.
+  python -m bit_residual_binarized_amd.profsum derive FETCH_DIR WRITE_DIR
+      HBM bytes per launch of the derive/pack kernels (k_derive_tile passes,
+      k_finalize) per matrix shape, copy-calibrated as for the GEMV, against
+      the passes' algorithmic bytes (W read once per pass, 4 B per weight;
+      the sign pass also writes the planes, 0.25 B per weight).
 
 The output starts with `key: value` lines (the traffic form is what bench.py
 reads back from the committed summary).
@@ -87,6 +92,11 @@ def _grid(r: dict) -> int:
         if k in r and r[k]:
             return int(float(r[k]))
     return 0
+
+
+# weights per matrix of the Llama-2-70B layer -> the matrices of that size
+MATS_70B = {1024 * 8192: "k, v (1024x8192)", 8192 * 8192: "q, o (8192x8192)",
+            28672 * 8192: "gate, up, down (28672x8192, 8192x28672)"}
 
 
 def stats(trace_dir: str) -> None:
@@ -164,6 +174,47 @@ def traffic(fetch_dir: str, write_dir: str) -> None:
     print(f"traffic_over_algorithmic: {tot_t / tot_a:.4f}")
 
 
+def _calibrated(d: str, counter: str) -> tuple[list, float]:
+    rows = [r for r in _rows(d, "counter_collection.csv") if r["Counter_Name"] == counter]
+    cal = [float(r["Counter_Value"]) for r in rows if CAL_KERNEL in r["Kernel_Name"]]
+    if not cal:
+        raise SystemExit(f"{counter}: no {CAL_KERNEL} dispatch in {d}")
+    return rows, max(cal) / (COPY_BYTES / 1024)
+
+
+def derive(fetch_dir: str, write_dir: str) -> None:
+    # k_derive_tile: a 256-thread workgroup per 64-row x 256-column tile, so
+    # that its grid (the total thread count rocprof records) is out in / 64
+    # and gives the matrix's weights. k_finalize (one launch per path) follows
+    # each pass and is attributed to the matrix of the pass before it in
+    # dispatch order.
+    per: dict[tuple, dict] = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows, factor = _calibrated(d, counter)
+        print(f"{counter.lower()}_factor: {factor:.4f}")
+        key_of_last = None
+        for r in sorted(rows, key=lambda r: int(r.get("Dispatch_Id") or r.get("Correlation_Id") or 0)):
+            k = _short(r["Kernel_Name"])
+            if k.startswith("k_derive_tile"):
+                key_of_last = 64 * _grid(r)
+                key = (k, key_of_last)
+            elif k == "k_finalize" and key_of_last:
+                key = (k, key_of_last)
+            else:
+                continue
+            per.setdefault(key, {}).setdefault(counter, []).append(float(r["Counter_Value"]) * 1024 / factor)
+    print(f"{'kernel':>26} {'weights':>10} {'launches':>8} {'read_MB':>9} {'write_MB':>9} "
+          f"{'alg_MB':>8} {'read/alg':>8}  matrices")
+    for (k, w), v in sorted(per.items(), key=lambda kv: (kv[0][1], kv[0][0])):
+        rd = statistics.fmean(v.get("FETCH_SIZE", [0.0]))
+        wr = statistics.fmean(v.get("WRITE_SIZE", [0.0]))
+        alg = 4 * w if k.startswith("k_derive_tile") else 0
+        alg_w = w // 4 if k.startswith("k_derive_tile<1") or k.startswith("k_derive_tile<2") else 0
+        ratio = f"{rd / alg:8.3f}" if alg else f"{'-':>8}"
+        print(f"{k:>26} {w:10d} {len(v.get('FETCH_SIZE', [])):8d} {rd / 1e6:9.2f} "
+              f"{wr / 1e6:9.2f} {(alg + alg_w) / 1e6:8.2f} {ratio}  {MATS_70B.get(w, '')}")
+
+
 def counters(pmc_dir: str) -> None:
     rows = _rows(pmc_dir, "counter_collection.csv")
     shapes = {**{k: LABELS[v] for k, v in SHAPES_70B_B1.items()}, **SHAPES_70B_B1_FORMED}
@@ -197,6 +248,8 @@ if __name__ == "__main__":
         stats(sys.argv[2])
     elif len(sys.argv) == 3 and sys.argv[1] == "counters":
         counters(sys.argv[2])
+    elif len(sys.argv) == 4 and sys.argv[1] == "derive":
+        derive(sys.argv[2], sys.argv[3])
     elif len(sys.argv) == 4 and sys.argv[1] == "traffic":
         traffic(sys.argv[2], sys.argv[3])
     else:
