@@ -867,25 +867,44 @@ __global__ __launch_bounds__(256, P == 3 && MT == 2 ? 1 : 2) void k_gemv16(Args 
     // in adjacent registers, and one 64-bit shift by 15 - 4 t4 - c brings the
     // sign bits of dword c of both steps to bits 15 and 31 of each half (no
     // bit of the low word reaches those positions of the high word)
+    // the LDS operands of step pair sp (qq = 2 (sp / 4), t4 = sp % 4) are read
+    // one step pair ahead, into the other of two register sets
+    v8h fx0[2][MT], fx1[2][MT];
+    uint4 hx0[2][P], hx1[2][P];
+    auto rd = [&](int sp) {
+      const int off0 = 16 * (4 * gl + 2 * (sp >> 2)) + 4 * (sp & 3), off1 = off0 + 16;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        fx0[sp & 1][mt] = *(const v8h*)(s_x[u] + (16 * mt + j) * kXRow + off0);
+        fx1[sp & 1][mt] = *(const v8h*)(s_x[u] + (16 * mt + j) * kXRow + off1);
+      }
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        hx0[sp & 1][p] = *(const uint4*)(s_h[u][p] + off0);
+        hx1[sp & 1][p] = *(const uint4*)(s_h[u][p] + off1);
+      }
+    };
+    rd(0);
 #pragma unroll
     for (int qq = 0; qq < 4; qq += 2)
 #pragma unroll
       for (int t4 = 0; t4 < 4; ++t4) {
-        // one step pair at a time, so that the scheduler does not hoist every
-        // step's LDS reads
+        // one step pair at a time (the scheduler would otherwise hoist every
+        // step's LDS reads), with the next pair's reads issued first
         __builtin_amdgcn_sched_barrier(0);
+        const int sp = 2 * qq + t4;
+        if (sp + 1 < 8) rd(sp + 1);
         const int sh = 15 - 4 * t4;
-        const int off0 = 16 * (4 * gl + qq) + 4 * t4, off1 = off0 + 16;
         v8h fa0[MT], fa1[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          fa0[mt] = *(const v8h*)(s_x[u] + (16 * mt + j) * kXRow + off0);
-          fa1[mt] = *(const v8h*)(s_x[u] + (16 * mt + j) * kXRow + off1);
+          fa0[mt] = fx0[sp & 1][mt];
+          fa1[mt] = fx1[sp & 1][mt];
         }
 #pragma unroll
         for (int p = 0; p < P; ++p) {
-          const uint4 h0 = *(const uint4*)(s_h[u][p] + off0);
-          const uint4 h1 = *(const uint4*)(s_h[u][p] + off1);
+          const uint4 h0 = hx0[sp & 1][p];
+          const uint4 h1 = hx1[sp & 1][p];
           if constexpr (MT == 2) {
             // all four slices' operands first, then the low step's matrix
             // ops, then the high step's: the two ops on one accumulator are
