@@ -13,7 +13,10 @@ power iteration in float32, so scales are compared normwise. Tolerances:
     with the exact SVID to about 1e-9; 3 passes leave a 1e-2 difference after
     20 sweeps): the objective ||W − Σ W_hat_i|| within 1e-5 relative; the
     scales and bits within 1e-3 and 1e-4 with two paths, 5e-2 and 5e-3 with
-    three (see test_twenty_sweeps for why).
+    three (see test_twenty_sweeps for why);
+  * 20 sweeps on a planted weight whose sign decisions all have a margin
+    (test_twenty_sweeps_planted_paths): bits exact, scales <= 1e-4 with
+    three paths as with two.
 """
 import numpy as np
 import pytest
@@ -103,6 +106,40 @@ def test_twenty_sweeps(gpu_lib, P):
         assert oracle.normwise_rel_err(g[p], gr) <= tol
         assert oracle.normwise_rel_err(h[p], hr) <= tol
         assert (bits[p] != s).mean() <= btol
+
+
+def planted_paths(out, inp, P, ratio, seed):
+    """W = sum_p outer(g_p, h_p) * (+-1)_p, g and h in [1, 1.5], path p scaled
+    by ratio^-p (float32): a weight whose SVID sign decisions all have a
+    margin, so that 20 sweeps do not drift with rounding."""
+    rng = np.random.default_rng(seed)
+    sg = [rng.integers(0, 2, (out, inp)).astype(bool) for _ in range(P)]
+    a = [rng.uniform(1.0, 1.5, out) * ratio ** -p for p in range(P)]
+    b = [rng.uniform(1.0, 1.5, inp) for _ in range(P)]
+    w = sum(np.outer(a[p], b[p]) * np.where(sg[p], -1.0, 1.0) for p in range(P))
+    return w.astype(np.float32), sg, a, b
+
+
+@pytest.mark.parametrize("P", [2, 3])
+def test_twenty_sweeps_planted_paths(gpu_lib, P):
+    """20 sweeps end to end on a planted weight (paths 4x apart): in float64,
+    1e-6 relative noise on it moves no sign and the 20-sweep scales by at most
+    3e-6, so here the GPU is held to the oracle tightly with three paths too:
+    every bit equal (and equal to the planted signs), scales within 1e-4
+    normwise, and each path's g h^T within 1e-4 of the planted one."""
+    out, inp = 256, 384
+    say("svid 20 sweeps planted", P)
+    w, sg, a, b = planted_paths(out, inp, P, 4.0, 5200 + P)
+    g, h, planes = gpu_svid(gpu_lib, w, P, 20, 5)
+    ref = oracle.residual_svid(w.astype(np.float64), n_paths=P, sweeps=20)
+    bits = bits_of(gpu_lib, planes, out, inp, P)
+    for p, (s, gr, hr) in enumerate(ref):
+        assert np.array_equal(s, sg[p]), p
+        assert np.array_equal(bits[p], s), p
+        assert oracle.normwise_rel_err(g[p], gr) <= 1e-4, p
+        assert oracle.normwise_rel_err(h[p], hr) <= 1e-4, p
+        o = np.outer(a[p], b[p])
+        assert np.linalg.norm(np.outer(g[p], h[p]) - o) <= 1e-4 * np.linalg.norm(o), p
 
 
 @pytest.mark.parametrize("P", [2, 3])

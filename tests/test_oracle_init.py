@@ -105,3 +105,28 @@ def test_leading_triple_matches_full_svd():
     assert np.array_equal(s, s2)
     np.testing.assert_allclose(g2, g, rtol=1e-9, atol=1e-12)
     np.testing.assert_allclose(h2, h, rtol=1e-9, atol=1e-12)
+
+
+def _planted(out, inp, n_paths, ratio, seed):
+    """W = sum_p outer(g_p, h_p) * (+-1)_p with g, h in [1, 1.5] and path p
+    scaled by ratio^-p: every sign decision of the SVID has a margin."""
+    rng = np.random.default_rng(seed)
+    sg = [rng.integers(0, 2, (out, inp)).astype(bool) for _ in range(n_paths)]
+    a = [rng.uniform(1.0, 1.5, out) * ratio ** -p for p in range(n_paths)]
+    b = [rng.uniform(1.0, 1.5, inp) for _ in range(n_paths)]
+    w = sum(_what(sg[p], a[p], b[p]) for p in range(n_paths))
+    return w, sg, a, b
+
+
+@pytest.mark.parametrize("n_paths", [2, 3])
+def test_twenty_sweeps_recover_planted_paths(n_paths):
+    # a weight that is exactly a sum of well-separated sign x rank-1 paths is
+    # recovered path by path: the signs exactly, each rank-1 magnitude to
+    # within the power-free SVD's rounding
+    w, sg, a, b = _planted(96, 160, n_paths, 4.0, 31 + n_paths)
+    paths = residual_svid(w, n_paths=n_paths, sweeps=20)
+    for p, (s, g, h) in enumerate(paths):
+        assert np.array_equal(s, sg[p]), p
+        o = np.outer(a[p], b[p])
+        assert np.linalg.norm(np.outer(g, h) - o) <= 1e-6 * np.linalg.norm(o), p
+    assert svid_objective(w, paths) <= 1e-9 * np.linalg.norm(w)
